@@ -1,0 +1,212 @@
+"""Float64 CPU oracle for the fused LoRA / QLoRA linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+product path (the HIP library and its Python binding) never imports it, and this
+module imports nothing from the product package: the two share no code.
+
+What it computes, and where the pages define it
+-----------------------------------------------
+Sources are the web pages on Unsloth.  They are cited by page title and section:
+
+* LoRA layer: tutorial ch. 5 "加速原理：Triton kernel 与 fused LoRA", §5.3, the
+  LoRA equation ``y = W x + (alpha/r) B A x`` with ``A`` (r x d), ``B`` (d x r);
+  the same equation appears in tutorial ch. 1 "项目背景与定位", §1.2, as
+  ``Delta W = (alpha/r) B A``.
+* Term order: §5.3's listing of the unfused PEFT forward (base layer, lora_A,
+  lora_B, multiply by alpha/r, add).  The oracle follows that order.
+* Backward: §5.3's paragraph on the fused backward (gradients for X, A, B; W only
+  "if trained", and here W is frozen) and the hand-derived-backward section of
+  the wisestudy.cn Unsloth essay.  The gradients below are derived by hand from
+  the loss convention ``L = <dY, Y>_F``.
+* 4-bit weights: "探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3
+  (4-bit weights read compactly, unpacked in registers by a scaling coefficient,
+  restored to FP16/BF16 before the matrix units).  The concrete format (symmetric
+  int4 in -7..7, two per byte, groups of 64 along K, fp16 scale = absmax/7) is
+  this repository's workload definition; the pages fix none of its details.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  row-major tokens, W is (N x K) = (out x in), A is (R x K), B is (N x R);
+  scale = alpha / r passed as a number; no dropout; dW is not computed;
+  XA = X A^T is the unscaled fp32 panel saved for backward; gradients overwrite;
+  int4: low nibble holds the even k, 4-bit two's complement, ties to even,
+  a group whose fp16 scale is 0 stores q = 0, dequantised weight =
+  bf16_rne(q * s) (the product is exact in fp32).
+
+Precision: every matrix product is a float64 NumPy matmul on the exact values of
+the rounded inputs; nothing inside is rounded.  Integer decisions (the int4
+codes) are taken on exact values (see ``quantize_int4``).
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle.py`` (brute force, closed forms, finite differences,
+invariants, library witnesses, hand-worked fixtures under ``tests/golden/``).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+QMAX = 7
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 value of bf16 bit patterns (uint16): the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); returns uint16 bits.
+
+    IEEE-754 rounding written on the bit pattern: add 0x7FFF plus the lowest kept
+    bit, then drop the low 16 bits.  Inputs here are finite (no NaN handling needed).
+    """
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def fp16_rne(x: np.ndarray) -> np.ndarray:
+    """Correctly rounded float64 -> IEEE binary16 (NumPy's cast rounds to nearest even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# int4 groupwise format (page "探微索隐 ...", §二.3; format details are readings)
+# ---------------------------------------------------------------------------
+
+
+def quantize_int4(w: np.ndarray, group: int = GROUP):
+    """Symmetric groupwise int4 quantisation of an fp32 weight ``w`` (N x K).
+
+    Per row n and group g of ``group`` consecutive k:
+      a = max |w|                       (exact)
+      s = fp16_rne(a / 7)               (float64 quotient, one rounding to fp16)
+      q = clip(rint(w / s), -7, 7)      (ties to even) ; q = 0 for the group if s == 0
+
+    The code decision is exact: the float64 quotient w/s of an fp32 w and an fp16 s
+    never lands on a half-integer unless the exact quotient is one, so ``rint``
+    sees the exact tie or the exact side of it.
+
+    Returns (q int8 N x K, s float16 N x K/group).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    if k % group:
+        raise ValueError("K must be a multiple of the group size")
+    wg = w.astype(np.float64).reshape(n, k // group, group)
+    a = np.abs(wg).max(axis=2)
+    if np.any(a / QMAX > 65504.0):
+        raise ValueError("group absmax too large for an fp16 scale")
+    s16 = fp16_rne(a / QMAX)
+    s = s16.astype(np.float64)
+    safe = np.where(s == 0.0, 1.0, s)
+    q = np.rint(wg / safe[:, :, None])
+    q = np.clip(q, -QMAX, QMAX)
+    q = np.where((s == 0.0)[:, :, None], 0.0, q)
+    return q.reshape(n, k).astype(np.int8), s16
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Two 4-bit two's-complement codes per byte; the low nibble holds the even k."""
+    q = np.asarray(q, dtype=np.int8)
+    n, k = q.shape
+    if k % 2:
+        raise ValueError("K must be even")
+    lo = q[:, 0::2].astype(np.int16) & 0xF
+    hi = q[:, 1::2].astype(np.int16) & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_int4``: sign-extend each nibble (0x8..0xF -> -8..-1)."""
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int16)
+    lo = p & 0xF
+    hi = (p >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    n, kb = p.shape
+    q = np.empty((n, 2 * kb), dtype=np.int8)
+    q[:, 0::2] = lo
+    q[:, 1::2] = hi
+    return q
+
+
+def dequant_int4_bits(packed: np.ndarray, scales: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Dequantised weight as bf16 bits: bf16_rne(float32(q) * float32(s)).
+
+    The product of a 4-bit integer and an fp16 scale has at most 3 + 11 significant
+    bits, so it is exact in fp32; the only rounding is the one to bf16.
+    """
+    q = unpack_int4(packed).astype(np.float64)
+    n, k = q.shape
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    s = np.repeat(s, group, axis=1)
+    prod = (q * s).astype(np.float32)  # exact
+    return f32_to_bf16_rne(prod)
+
+
+def dequant_int4(packed: np.ndarray, scales: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Dequantised weight as float64 values (the exact bf16 values)."""
+    return bf16_bits_to_f64(dequant_int4_bits(packed, scales, group))
+
+
+# ---------------------------------------------------------------------------
+# The LoRA layer (tutorial ch. 5 §5.3 equation; tutorial ch. 1 §1.2 equation)
+# ---------------------------------------------------------------------------
+
+
+def _f64(*xs):
+    return [np.asarray(x, dtype=np.float64) for x in xs]
+
+
+def lora_forward(X, W, A, B, scale):
+    """Y = X W^T + scale * (X A^T) B^T, in the order of §5.3's unfused PEFT listing.
+
+    X: M x K, W: N x K, A: R x K, B: N x R.  Returns (Y: M x N, XA: M x R), float64.
+    """
+    X, W, A, B = _f64(X, W, A, B)
+    main = X @ W.T                 # base layer
+    xa = X @ A.T                   # lora_A
+    lora = xa @ B.T                # lora_B
+    lora = lora * float(scale)     # multiply by alpha / r
+    return main + lora, xa
+
+
+def lora_backward(dY, X, W, A, B, scale, XA=None):
+    """Hand-derived gradients of L = <dY, Y>_F with W frozen.
+
+    G  = dY B                     (M x R)
+    dX = dY W + scale * G A       (M x K)
+    dA = scale * G^T X            (R x K)
+    dB = scale * dY^T (X A^T)     (N x R)
+    """
+    dY, X, W, A, B = _f64(dY, X, W, A, B)
+    s = float(scale)
+    xa = X @ A.T if XA is None else np.asarray(XA, dtype=np.float64)
+    G = dY @ B
+    dX = dY @ W + s * (G @ A)
+    dA = s * (G.T @ X)
+    dB = s * (dY.T @ xa)
+    return dX, dA, dB
+
+
+def lora_forward_rows(X, W, A, B, scale, rows):
+    """Rows ``rows`` of (Y, XA), computed one row set at a time (for full-size sampling)."""
+    rows = np.asarray(rows)
+    Xr, W, A, B = _f64(np.asarray(X)[rows], W, A, B)
+    main = Xr @ W.T
+    xa = Xr @ A.T
+    return main + (xa @ B.T) * float(scale), xa
+
+
+def lora_backward_dx_rows(dY, W, A, B, scale, rows):
+    """Rows ``rows`` of dX = dY W + scale * (dY B) A."""
+    rows = np.asarray(rows)
+    dYr, W, A, B = _f64(np.asarray(dY)[rows], W, A, B)
+    return dYr @ W + float(scale) * ((dYr @ B) @ A)

@@ -1,0 +1,360 @@
+"""CPU pins of the float64 oracle (no GPU).
+
+Each test checks the oracle against something other than itself: hand-worked
+fixtures under tests/golden/, exact rational brute force, finite differences,
+Euler-homogeneity invariants, special cases that reduce to a library routine, and
+library witnesses (torch float64 autograd, torch's bf16 conversion, the struct
+module's IEEE half conversion).  A dropped term, a wrong sign, a transposed
+operand or a wrong rounding rule in ``oracle/`` fails at least one of them.
+"""
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_fixture(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = vals
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def test_bf16_rne_hand_cases():
+    with open(os.path.join(GOLDEN, "bf16_rne_cases.txt")) as f:
+        rows = [l.split()[:2] for l in f if l.strip() and not l.startswith("#")]
+    src = np.array([int(a, 16) for a, _ in rows], dtype=np.uint32).view(np.float32)
+    want = np.array([int(b, 16) for _, b in rows], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16_rne(src), want)
+
+
+def test_bf16_rne_matches_torch_conversion():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(1 << 20).astype(np.float32)
+    # force many exact ties and near-ties
+    u = x.view(np.uint32).copy()
+    u[: 1 << 16] = (u[: 1 << 16] & 0xFFFF0000) | 0x8000
+    u[1 << 16: 1 << 17] = (u[1 << 16: 1 << 17] & 0xFFFF0000) | 0x7FFF
+    x = u.view(np.float32)
+    torch_bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16_rne(x), torch_bits)
+
+
+def test_bf16_bits_to_f64_roundtrip():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite only
+    vals = oracle.bf16_bits_to_f64(bits)
+    witness = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(vals, witness)
+
+
+def test_fp16_rne_against_struct_half():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(20000) * 0.01, rng.standard_normal(2000) * 1e-6,
+                        # exact fp16 ties: midpoints between neighbouring halves
+                        (np.arange(1025, 1100, dtype=np.float64) + 0.5) * 2.0 ** -10])
+    got = oracle.fp16_rne(x)
+    want = np.array([np.frombuffer(struct.pack("<e", v), dtype=np.float16)[0] for v in x])
+    np.testing.assert_array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# LoRA forward
+# ---------------------------------------------------------------------------
+
+def _fixture_lora():
+    f = _read_fixture("lora_worked_example.txt")
+    M, K, N, R = (int(f[k][0]) for k in ("M", "K", "N", "R"))
+    alpha = float(f["alpha"][0])
+
+    def mat(key, r, c):
+        return np.array([float(v) for v in f[key]]).reshape(r, c)
+
+    return dict(M=M, K=K, N=N, R=R, s=alpha / R, X=mat("X", M, K), W=mat("W", N, K),
+                A=mat("A", R, K), B=mat("B", N, R), dY=mat("dY", M, N), XA=mat("XA", M, R),
+                Y=mat("Y", M, N), dX=mat("dX", M, K), dA=mat("dA", R, K), dB=mat("dB", N, R))
+
+
+def test_forward_hand_worked_example():
+    f = _fixture_lora()
+    Y, XA = oracle.lora_forward(f["X"], f["W"], f["A"], f["B"], f["s"])
+    np.testing.assert_array_equal(Y, f["Y"])
+    np.testing.assert_array_equal(XA, f["XA"])
+
+
+def test_backward_hand_worked_example():
+    f = _fixture_lora()
+    dX, dA, dB = oracle.lora_backward(f["dY"], f["X"], f["W"], f["A"], f["B"], f["s"])
+    np.testing.assert_array_equal(dX, f["dX"])
+    np.testing.assert_array_equal(dA, f["dA"])
+    np.testing.assert_array_equal(dB, f["dB"])
+
+
+def _frac_matrix(a):
+    return [[Fraction(float(v)) for v in row] for row in np.asarray(a)]
+
+
+@pytest.mark.parametrize("M,K,N,R,zero_w", [(3, 5, 4, 2, False), (4, 8, 6, 3, False),
+                                            (2, 7, 3, 1, True), (5, 4, 7, 4, False)])
+def test_forward_against_materialised_delta_w(M, K, N, R, zero_w):
+    """Brute force: Y = X (W + s B A)^T with Delta W built explicitly, in exact rationals."""
+    rng = np.random.default_rng(10 + M * 100 + K)
+    X = rng.standard_normal((M, K)).astype(np.float32).astype(np.float64)
+    W = np.zeros((N, K)) if zero_w else rng.standard_normal((N, K)).astype(np.float32).astype(np.float64)
+    A = rng.uniform(-1, 1, (R, K)).astype(np.float32).astype(np.float64)
+    B = rng.standard_normal((N, R)).astype(np.float32).astype(np.float64)
+    s = Fraction(3, 2)
+    Xf, Wf, Af, Bf = map(_frac_matrix, (X, W, A, B))
+    dW = [[sum(Bf[n][i] * Af[i][k] for i in range(R)) * s for k in range(K)] for n in range(N)]
+    Weff = [[Wf[n][k] + dW[n][k] for k in range(K)] for n in range(N)]
+    exact = [[sum(Xf[m][k] * Weff[n][k] for k in range(K)) for n in range(N)] for m in range(M)]
+    Y, XA = oracle.lora_forward(X, W, A, B, float(s))
+    ex = np.array([[float(v) for v in row] for row in exact])
+    assert np.max(np.abs(Y - ex)) <= 1e-12 * max(1.0, np.max(np.abs(ex)))
+    xa_exact = np.array([[float(sum(Xf[m][k] * Af[i][k] for k in range(K))) for i in range(R)]
+                         for m in range(M)])
+    assert np.max(np.abs(XA - xa_exact)) <= 1e-12 * max(1.0, np.max(np.abs(xa_exact)))
+
+
+def test_forward_zero_adapter_is_plain_matmul_bitwise():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((17, 64))
+    W = rng.standard_normal((48, 64))
+    A = rng.standard_normal((8, 64))
+    Y, _ = oracle.lora_forward(X, W, A, np.zeros((48, 8)), 2.0)
+    np.testing.assert_array_equal(Y, np.matmul(X, W.T))
+    Y0, _ = oracle.lora_forward(X, W, A, rng.standard_normal((48, 8)), 0.0)
+    np.testing.assert_array_equal(Y0, np.matmul(X, W.T))
+
+
+def test_forward_rows_matches_full():
+    rng = np.random.default_rng(4)
+    X, W = rng.standard_normal((40, 32)), rng.standard_normal((24, 32))
+    A, B = rng.standard_normal((4, 32)), rng.standard_normal((24, 4))
+    Y, XA = oracle.lora_forward(X, W, A, B, 2.0)
+    rows = [0, 7, 39, 13]
+    Yr, XAr = oracle.lora_forward_rows(X, W, A, B, 2.0, rows)
+    np.testing.assert_allclose(Yr, Y[rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(XAr, XA[rows], rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# LoRA backward
+# ---------------------------------------------------------------------------
+
+def _loss(dY, X, W, A, B, s):
+    Y, _ = oracle.lora_forward(X, W, A, B, s)
+    return float(np.sum(dY * Y))
+
+
+@pytest.mark.parametrize("M,K,N,R", [(3, 5, 4, 2), (6, 4, 7, 3)])
+def test_backward_central_differences(M, K, N, R):
+    """L = <dY, Y> is linear in X, in A and in B separately, so a central difference
+    with a unit step has no truncation error: it equals the gradient up to rounding."""
+    rng = np.random.default_rng(20 + M)
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((N, K))
+    A, B = rng.standard_normal((R, K)), rng.standard_normal((N, R))
+    dY, s = rng.standard_normal((M, N)), 1.75
+    dX, dA, dB = oracle.lora_backward(dY, X, W, A, B, s)
+
+    def fd(which, shape):
+        g = np.zeros(shape)
+        for idx in np.ndindex(*shape):
+            args = {"X": X, "A": A, "B": B}
+            plus = {k: v.copy() for k, v in args.items()}
+            minus = {k: v.copy() for k, v in args.items()}
+            plus[which][idx] += 1.0
+            minus[which][idx] -= 1.0
+            g[idx] = (_loss(dY, plus["X"], W, plus["A"], plus["B"], s)
+                      - _loss(dY, minus["X"], W, minus["A"], minus["B"], s)) / 2.0
+        return g
+
+    for name, got in (("X", dX), ("A", dA), ("B", dB)):
+        want = fd(name, got.shape)
+        np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-9)
+
+
+def test_backward_against_torch_autograd_float64():
+    rng = np.random.default_rng(5)
+    M, K, N, R, s = 33, 40, 24, 6, 2.0
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((N, K)) / np.sqrt(K)
+    A, B = rng.uniform(-0.2, 0.2, (R, K)), rng.standard_normal((N, R)) * 0.14
+    dY = rng.standard_normal((M, N))
+    tX, tA, tB = (torch.tensor(v, dtype=torch.float64, requires_grad=True) for v in (X, A, B))
+    tW = torch.tensor(W, dtype=torch.float64)
+    Y = tX @ tW.T + (tX @ tA.T @ tB.T) * s
+    Y.backward(torch.tensor(dY, dtype=torch.float64))
+    dX, dA, dB = oracle.lora_backward(dY, X, W, A, B, s)
+    np.testing.assert_allclose(dX, tX.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dA, tA.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dB, tB.grad.numpy(), rtol=1e-12, atol=1e-12)
+    Yo, _ = oracle.lora_forward(X, W, A, B, s)
+    np.testing.assert_allclose(Yo, Y.detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_homogeneity_invariants():
+    """Euler: <dX, X> = <dY, Y>; <dA, A> = <dB, B> = s <dY, XA B^T> (the LoRA part of L)."""
+    rng = np.random.default_rng(6)
+    M, K, N, R, s = 96, 80, 72, 8, 2.0
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((N, K)) / np.sqrt(K)
+    A, B = rng.uniform(-0.1, 0.1, (R, K)), rng.standard_normal((N, R)) * 0.14
+    dY = rng.standard_normal((M, N))
+    Y, XA = oracle.lora_forward(X, W, A, B, s)
+    dX, dA, dB = oracle.lora_backward(dY, X, W, A, B, s)
+    L = np.sum(dY * Y)
+    Lr = s * np.sum(dY * np.matmul(np.matmul(X, A.T), B.T))
+    assert abs(np.sum(dX * X) - L) <= 1e-10 * max(1.0, abs(L))
+    assert abs(np.sum(dA * A) - Lr) <= 1e-10 * max(1.0, abs(Lr))
+    assert abs(np.sum(dB * B) - Lr) <= 1e-10 * max(1.0, abs(Lr))
+
+
+def test_backward_zero_adapter_cases():
+    rng = np.random.default_rng(7)
+    M, K, N, R = 12, 16, 8, 4
+    X, W, dY = rng.standard_normal((M, K)), rng.standard_normal((N, K)), rng.standard_normal((M, N))
+    A, B = rng.standard_normal((R, K)), rng.standard_normal((N, R))
+    dX, dA, dB = oracle.lora_backward(dY, X, W, A, np.zeros((N, R)), 2.0)
+    assert not dA.any()
+    np.testing.assert_array_equal(dX, np.matmul(dY, W))
+    dX, dA, dB = oracle.lora_backward(dY, X, W, np.zeros((R, K)), B, 2.0)
+    assert not dB.any()
+
+
+def test_backward_dx_rows_matches_full():
+    rng = np.random.default_rng(8)
+    M, K, N, R = 30, 24, 20, 4
+    X, W, dY = rng.standard_normal((M, K)), rng.standard_normal((N, K)), rng.standard_normal((M, N))
+    A, B = rng.standard_normal((R, K)), rng.standard_normal((N, R))
+    dX, _, _ = oracle.lora_backward(dY, X, W, A, B, 2.0)
+    rows = [29, 0, 11]
+    np.testing.assert_allclose(oracle.lora_backward_dx_rows(dY, W, A, B, 2.0, rows), dX[rows],
+                               rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# int4 format
+# ---------------------------------------------------------------------------
+
+def test_int4_hand_worked_group():
+    f = _read_fixture("int4_format_example.txt")
+    w = np.zeros((1, 64), dtype=np.float32)
+    vals = [float(v) for v in f["values"]]
+    w[0, : len(vals)] = vals
+    q, s = oracle.quantize_int4(w)
+    assert s.view(np.uint16)[0, 0] == int(f["scale_bits"][0], 16)
+    codes = [int(v) for v in f["codes"]]
+    np.testing.assert_array_equal(q[0, : len(codes)], codes)
+    assert not q[0, len(codes):].any()
+    packed = oracle.pack_int4(q)
+    want = [int(b, 16) for b in f["bytes"]]
+    np.testing.assert_array_equal(packed[0, : len(want)], want)
+    assert not packed[0, len(want):].any()
+    bits = oracle.dequant_int4_bits(packed, s)
+    assert bits[0, 0] == int(f["dequant_k0_bf16"][0], 16)
+
+
+def test_int4_pack_unpack_exhaustive():
+    lo, hi = np.meshgrid(np.arange(-8, 8), np.arange(-8, 8), indexing="ij")
+    q = np.stack([lo.ravel(), hi.ravel()], axis=1).astype(np.int8).reshape(1, -1)
+    p = oracle.pack_int4(q)
+    assert sorted(p.ravel().tolist()) == list(range(256))
+    np.testing.assert_array_equal(oracle.unpack_int4(p), q)
+
+
+def test_int4_quantiser_properties():
+    rng = np.random.default_rng(9)
+    N, K = 64, 1024
+    w = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    q, s = oracle.quantize_int4(w)
+    assert q.dtype == np.int8 and np.abs(q).max() <= 7
+    wg = w.astype(np.float64).reshape(N, K // 64, 64)
+    qg = q.reshape(N, K // 64, 64)
+    sd = s.astype(np.float64)
+    a = np.abs(wg).max(axis=2)
+    # scale = fp16(absmax / 7), cross-checked with the struct module's IEEE half rounding
+    want = np.array([[np.frombuffer(struct.pack("<e", v / 7.0), dtype=np.float16)[0] for v in row]
+                     for row in a])
+    np.testing.assert_array_equal(s.view(np.uint16), want.view(np.uint16))
+    # the absmax element of every group maps to +-7
+    arg = np.abs(wg).argmax(axis=2)
+    top = np.take_along_axis(qg, arg[:, :, None], axis=2)[:, :, 0]
+    np.testing.assert_array_equal(np.abs(top), 7)
+    # nearest code: |w - q s| <= s / 2 (no clamping occurs below absmax * 7.5/7)
+    err = np.abs(wg - qg * sd[:, :, None])
+    assert np.all(err <= sd[:, :, None] / 2 * (1 + 1e-12))
+
+
+def test_int4_exact_ties_go_to_even():
+    s16 = np.float16(0.1)
+    s = float(s16)
+    ks = np.array([0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5, -0.5, -1.5, -6.5])
+    w = np.zeros((1, 64), dtype=np.float32)
+    w[0, 0] = 7 * s  # pins the scale to s exactly (7 s / 7 = s)
+    w[0, 1: 1 + len(ks)] = ks * s  # exact in fp32 (<= 15 significant bits)
+    assert np.all(w[0, 1: 1 + len(ks)].astype(np.float64) == ks * s)
+    q, sc = oracle.quantize_int4(w)
+    assert float(sc[0, 0]) == s
+    np.testing.assert_array_equal(q[0, 1: 1 + len(ks)], [0, 2, 2, 4, 4, 6, 6, 0, -2, -6])
+
+
+def test_int4_zero_and_underflow_groups():
+    w = np.zeros((2, 128), dtype=np.float32)
+    w[1, 64] = 1e-9  # absmax / 7 underflows to fp16 zero
+    w[1, 65] = -5e-10
+    q, s = oracle.quantize_int4(w)
+    assert not s.astype(np.float64).any()
+    assert not q.any()
+    np.testing.assert_array_equal(oracle.dequant_int4_bits(oracle.pack_int4(q), s), 0)
+
+
+def test_int4_dequant_enumeration_against_torch():
+    """All 16 nibbles x sample scales: bf16(q s) via torch's float -> bf16 rounding."""
+    rng = np.random.default_rng(11)
+    scales = np.concatenate([rng.uniform(1e-4, 0.05, 60), [2.0 ** -24, 6.1e-5, 1.0, 65504.0 / 7]])
+    s16 = scales.astype(np.float16)
+    nib = np.arange(16, dtype=np.uint8)
+    packed = np.repeat((nib | (nib << 4))[None, :], len(s16), axis=0)  # K = 32 per row
+    packed = np.concatenate([packed, packed], axis=1)  # K = 64: one group per row
+    bits = oracle.dequant_int4_bits(packed, s16[:, None])
+    q = np.where(nib >= 8, nib.astype(np.int64) - 16, nib.astype(np.int64))
+    exact = q[None, :] * s16.astype(np.float64)[:, None]  # exact products
+    want = torch.tensor(exact).to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits[:, 0:32:2], want)
+    np.testing.assert_array_equal(bits[:, 1:32:2], want)
+
+
+def test_qlora_forward_uses_dequantised_weight():
+    """QLoRA = the LoRA formula with W := dequant(quant(W)); brute force on a tiny case."""
+    rng = np.random.default_rng(12)
+    M, K, N, R = 3, 64, 5, 2
+    w = (rng.standard_normal((N, K)) / 8).astype(np.float32)
+    q, s = oracle.quantize_int4(w)
+    Wt = oracle.dequant_int4(oracle.pack_int4(q), s)
+    # dequantised values are exactly representable in bf16 and close to q * s
+    np.testing.assert_allclose(Wt, q * s.astype(np.float64).repeat(64, axis=1), rtol=2 ** -8, atol=0)
+    X = rng.standard_normal((M, K))
+    A, B = rng.standard_normal((R, K)), rng.standard_normal((N, R))
+    Y, _ = oracle.lora_forward(X, Wt, A, B, 2.0)
+    Xf, Wf, Af, Bf = map(_frac_matrix, (X, Wt, A, B))
+    for m in range(M):
+        for n in range(N):
+            ex = sum(Xf[m][k] * (Wf[n][k] + 2 * sum(Bf[n][i] * Af[i][k] for i in range(R)))
+                     for k in range(K))
+            assert abs(Y[m, n] - float(ex)) <= 1e-12 * max(1.0, abs(float(ex)))
