@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LoRA layer on one MI355X.
+
+One step = lora_fwd + lora_bwd (every kernel of the bf16 path: the fused forward with its
+rank-R panel and low-rank epilogue, the fused input gradient with its panel, the split-K
+adapter-gradient partials and their fixed-order reduction) on the LoRA attention projection
+M = 8192 tokens (4 x 2048), K = N = 4096, r = 16, alpha = 32, bf16 with fp32 accumulation,
+synthetic seeded inputs already resident in HBM.
+
+Prints one JSON line.  `value` is algorithmic TFLOP/s (4MNK + 6Mr(K+N) per step) over the
+timed steps.  `roofline` reports the dominant kernel (the fused forward, one launch per
+lora_fwd call) timed live with HIP events on its stream.  `cpu_baseline` times the float64
+oracle on a bounded sample of the same workload.  `secondary` holds the QLoRA fwd+bwd rate
+on the int4 FFN projection and the decode matrix-vector bandwidth.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk (AMD MI355X spec)
+PEAK_HBM_GBS = 8000.0       # HBM3E, AMD MI355X spec
+METRIC = "fused LoRA fwd+bwd TFLOP/s (% bf16 MFMA peak), M=8192 K=N=4096 r=16"
+
+
+def lora_flops(M, N, K, R):
+    return 4.0 * M * N * K + 6.0 * M * R * (K + N)
+
+
+def fwd_flops(M, N, K, R):
+    return 2.0 * M * N * K + 2.0 * M * R * (K + N)
+
+
+def dev_bits(a, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def event_time_ms(fn, reps, stream):
+    """Average milliseconds of fn() over reps calls, HIP events recorded on `stream`."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(inp, sample_rows):
+    """The float64 oracle, as it stands, on the first `sample_rows` tokens of the workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    x = oracle.bf16_bits_to_f64(inp.X[:sample_rows])
+    dy = oracle.bf16_bits_to_f64(inp.dY[:sample_rows])
+    w, a, b = (oracle.bf16_bits_to_f64(getattr(inp, n)) for n in ("W", "A", "B"))
+    t0 = time.perf_counter()
+    Y, XA = oracle.lora_forward(x, w, a, b, inp.scale)
+    oracle.lora_backward(dy, x, w, a, b, inp.scale, XA=XA)
+    dt = time.perf_counter() - t0
+    fl = lora_flops(sample_rows, inp.N, inp.K, inp.R)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 fwd+bwd on the first {sample_rows} of {inp.M} tokens "
+                      f"({fl:.3e} FLOP in {dt:.2f} s)"}
+
+
+def bench_qlora_ffn(lora, torch, dev, reps):
+    from qlora_fine_tuning_amd.workloads import workload_inputs
+
+    inp = workload_inputs("qlora_ffn")
+    M, N, K, R = inp.M, inp.N, inp.K, inp.R
+    Wq, Ws = lora.qlora_quantize(torch.from_numpy(inp.W).to(dev))
+    X, A, B, dY = (dev_bits(getattr(inp, n), dev) for n in ("X", "A", "B", "dY"))
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    XA = torch.empty(M, R, dtype=torch.float32, device=dev)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(R, K, dtype=torch.float32, device=dev)
+    dB = torch.empty(N, R, dtype=torch.float32, device=dev)
+    ws = torch.empty(lora.qlora_bwd_workspace_bytes(M, N, K, R), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale, Y=Y, XA=XA)
+        lora.qlora_bwd(dY, X, Wq, Ws, A, B, XA, inp.scale, dX=dX, dA=dA, dB=dB, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ms = event_time_ms(step, reps, stream)
+    fl = lora_flops(M, N, K, R)
+    return {"workload": "qlora_ffn", "M": M, "N": N, "K": K, "r": R, "ms_per_step": round(ms, 4),
+            "TFLOP/s": round(fl / ms / 1e9, 2), "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_decode(lora, torch, dev, reps, copies=6):
+    """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL)."""
+    from qlora_fine_tuning_amd.workloads import workload_inputs
+
+    out = []
+    for name in ("decode_up", "decode_down"):
+        inp = workload_inputs(name, M=8)
+        N, K, R = inp.N, inp.K, inp.R
+        Wq0, Ws0 = lora.qlora_quantize(torch.from_numpy(inp.W).to(dev))
+        Wqs = [Wq0] + [Wq0.clone() for _ in range(copies - 1)]
+        Wss = [Ws0] + [Ws0.clone() for _ in range(copies - 1)]
+        A, B = dev_bits(inp.A, dev), dev_bits(inp.B, dev)
+        Xall = dev_bits(inp.X, dev)
+        stream = torch.cuda.current_stream()
+        for M in (1, 4, 8):
+            X = Xall[:M].contiguous()
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(lora.qlora_fwd_workspace_bytes(M, N, K, R), 256), dtype=torch.uint8, device=dev)
+            state = {"i": 0}
+
+            def call():
+                i = state["i"]
+                state["i"] = (i + 1) % copies
+                lora.qlora_fwd(X, Wqs[i], Wss[i], A, B, inp.scale, Y=Y, save_xa=False, ws=ws)
+
+            for _ in range(copies):
+                call()
+            torch.cuda.synchronize()
+            ms = event_time_ms(call, reps * copies, stream)
+            nbytes = N * K // 2 + N * (K // 64) * 2 + R * K * 2 + N * R * 2 + M * K * 2 + M * N * 2
+            out.append({"workload": name, "M": M, "N": N, "K": K, "us_per_call": round(ms * 1e3, 3),
+                        "GB/s": round(nbytes / ms / 1e6, 1),
+                        "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)})
+        del Wqs, Wss
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the QLoRA and decode lines")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="tokens in the oracle's timed sample")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer's data-parallel sharding (token slices per GPU, "
+              "one all-reduce of dA and dB per layer) is not part of this build. Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from qlora_fine_tuning_amd import lora
+    from qlora_fine_tuning_amd.workloads import workload_inputs
+
+    if not os.path.exists(lora.LIB_PATH):
+        from qlora_fine_tuning_amd import build
+
+        build.build()
+    lora.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inp = workload_inputs("attn_proj")
+    M, N, K, R = inp.M, inp.N, inp.K, inp.R
+    X, W, A, B, dY = (dev_bits(getattr(inp, n), dev) for n in ("X", "W", "A", "B", "dY"))
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    XA = torch.empty(M, R, dtype=torch.float32, device=dev)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(R, K, dtype=torch.float32, device=dev)
+    dB = torch.empty(N, R, dtype=torch.float32, device=dev)
+    ws = torch.empty(lora.lora_bwd_workspace_bytes(lora.LORA_BF16, M, N, K, R), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        lora.lora_fwd(X, W, A, B, inp.scale, Y=Y, XA=XA, stream=stream)
+
+    def bwd():
+        lora.lora_bwd(dY, X, W, A, B, XA, inp.scale, dX=dX, dA=dA, dB=dB, ws=ws, stream=stream)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    fl = lora_flops(M, N, K, R)
+    value = fl / ms / 1e9
+
+    # dominant kernel: the fused forward (one kernel per lora_fwd call), timed live
+    fwd_ms = event_time_ms(fwd, max(args.steps, 10), stream)
+    bwd_ms = event_time_ms(bwd, max(args.steps, 10), stream)
+    ach = fwd_flops(M, N, K, R) / fwd_ms / 1e9
+    roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "fwd_mfma_kernel<16,false>", "kernel_ms": round(fwd_ms, 4),
+                "bwd_ms": round(bwd_ms, 4)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) / N(0,1/K) / U(+-1/sqrt K) / N(0,0.02 variance) inputs)",
+        "config": {"workload": "attn_proj: LoRA attention projection, M=8192 (4x2048) K=N=4096 r=16 alpha=32",
+                   "global_batch": 4, "seq_len": 2048, "parallelism": "single GPU"},
+        "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+    }
+    if not args.no_secondary:
+        result["secondary"] = {"qlora": bench_qlora_ffn(lora, torch, dev, 5),
+                               "decode": bench_decode(lora, torch, dev, 20)}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_rows, M))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,143 @@
+/*
+ * lora.h - C ABI of the MI355X (gfx950) fused LoRA / QLoRA linear layer.
+ *
+ * The layer (tutorial ch. 5 "加速原理：Triton kernel 与 fused LoRA", §5.3, LoRA equation;
+ * tutorial ch. 1 "项目背景与定位", §1.2, Delta W = (alpha/r) B A), written for row-major
+ * batches of tokens:
+ *
+ *     XA = X A^T                       (M x R, the rank-R panel, saved for backward)
+ *     Y  = X W^T + scale * XA B^T      (M x N)
+ *
+ * and its backward with W frozen (§5.3, the paragraph on the fused backward; gradients
+ * derived by hand for the loss convention dL/dY = dY):
+ *
+ *     G  = dY B                        (M x R)
+ *     dX = dY W + scale * G A          (M x K)
+ *     dA = scale * G^T X               (R x K)
+ *     dB = scale * dY^T XA             (N x R)
+ *
+ * QLoRA ("探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3): W is held as
+ * symmetric int4 codes in -7..7, two per byte (even k in the low nibble, 4-bit two's
+ * complement), in groups of 64 consecutive k that share one fp16 scale (absmax / 7).  The
+ * kernels read the packed bytes and unpack them in registers:
+ *     W~[n][k] = bf16_rne( q[n][k] * scale16[n][k/64] )
+ * and use W~ in the formulas above.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Shapes: X M x K, W N x K (out x in), A R x K, B N x R, Y and dY M x N, dX M x K,
+ *    XA and G M x R, dA R x K, dB N x R.  All tensors are dense row-major with no strides.
+ *  - Sizes: M >= 0 (M == 0 is a valid empty batch); N and K positive multiples of 64;
+ *    R a multiple of 8 in [8, 64]; every tensor below 2^31 elements.
+ *  - Pointers are device pointers owned by the caller, 16-byte aligned, and outputs must
+ *    not alias inputs.  The library allocates and frees nothing and keeps no state
+ *    between calls; scratch memory comes from the caller's workspace.
+ *  - `stream` is a hipStream_t (NULL for the null stream).  Work is enqueued on it and
+ *    the call returns without synchronising; faults during execution surface at the
+ *    caller's next synchronisation.
+ *  - Arguments are validated before any HIP call; an invalid call returns an error code
+ *    and leaves every output untouched.  A failed launch returns LORA_ERR_HIP.
+ *  - `scale` is alpha / r, computed by the caller.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Results are deterministic: reductions run in a fixed order, without atomics, so
+ *    two identical calls give bitwise identical outputs.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_ERR_NULL = 1,      /* a required pointer is NULL */
+  LORA_ERR_SHAPE = 2,     /* M < 0, N or K not a positive multiple of 64, or a tensor too large */
+  LORA_ERR_RANK = 3,      /* R not a multiple of 8 in [8, 64] */
+  LORA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  LORA_ERR_DTYPE = 5,     /* unknown element type */
+  LORA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the matching *_workspace_bytes() */
+  LORA_ERR_GROUP = 7,     /* int4 group size other than 64 */
+  LORA_ERR_VALUE = 8,     /* scale not finite */
+  LORA_ERR_HIP = 9        /* a HIP launch failed; lora_last_hip_error() names it */
+} lora_status;
+
+/* Element type of X, W, A, B, Y, dY and dX.  dA, dB, XA and G are always fp32. */
+typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/* Forward: Y = X W^T + scale (X A^T) B^T  (tutorial ch. 5, §5.3: one kernel per output tile
+ * that adds the low-rank term in its epilogue, so no intermediate reaches HBM).
+ *   X  [M][K], W [N][K], A [R][K], B [N][R]  of type `dt`     (inputs)
+ *   Y  [M][N] of type `dt`                                     (output)
+ *   XA [M][R] fp32, unscaled X A^T, or NULL to skip saving it   (output) */
+lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                     const void* X, const void* W, const void* A, const void* B,
+                     void* Y, float* XA, void* stream);
+
+/* Bytes of device workspace lora_bwd needs for these sizes (holds G and the per-token-tile
+ * partial sums of dA and dB). */
+size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R);
+
+/* Backward with W frozen (tutorial ch. 5, §5.3, fused backward; hand-derived gradients):
+ *   dX = dY W + scale (dY B) A,  dA = scale (dY B)^T X,  dB = scale dY^T XA.
+ *   dY [M][N], X [M][K], W [N][K], A [R][K], B [N][R] of type `dt`   (inputs)
+ *   XA [M][R] fp32 as saved by lora_fwd                             (input)
+ *   dX [M][K] of type `dt`; dA [R][K] fp32; dB [N][R] fp32           (outputs)
+ *   ws: device workspace of at least lora_bwd_workspace_bytes() bytes. */
+lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                     const void* dY, const void* X, const void* W, const void* A, const void* B,
+                     const float* XA, void* dX, float* dA, float* dB,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* int4 quantise + pack of an fp32 weight ("探微索隐 ...", §二.3 names the 4-bit store and its
+ * scaling coefficient; the exact format is given at the top of this header).
+ *   W  [N][K] fp32                        (input)
+ *   Wq [N][K/2] bytes, Ws [N][K/group] fp16 (outputs)
+ * group must be 64.  Codes are decided exactly (ties to even on the exact quotient). */
+lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W,
+                           uint8_t* Wq, void* Ws, void* stream);
+
+/* The dequantised weight W~ [N][K] as bf16 (the unpack routine the QLoRA kernels use). */
+lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq, const void* Ws,
+                          void* W_bf16, void* stream);
+
+/* Bytes of device workspace qlora_fwd needs (the small-M path keeps partial sums of
+ * X A^T there; 0 when none is needed). */
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
+
+/* QLoRA forward: Y = X W~^T + scale (X A^T) B^T with W~ unpacked in registers.  For M <= 8
+ * it runs as an HBM-bandwidth-bound matrix-vector kernel (per generated token every weight
+ * byte is streamed once: "探微索隐 ...", §一, the memory wall of decoding).
+ *   X [M][K], A [R][K], B [N][R] bf16; Wq [N][K/2]; Ws [N][K/64] fp16   (inputs)
+ *   Y [M][N] bf16; XA [M][R] fp32 or NULL                               (outputs)
+ *   ws: at least qlora_fwd_workspace_bytes() bytes (may be NULL when that is 0). */
+lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                      const void* X, const uint8_t* Wq, const void* Ws,
+                      const void* A, const void* B, void* Y, float* XA,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace qlora_bwd needs. */
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
+
+/* QLoRA backward: as lora_bwd with W := W~ unpacked in registers.  All of dY, X, A, B and
+ * dX are bf16; dA, dB fp32. */
+lora_status qlora_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                      const void* dY, const void* X, const uint8_t* Wq, const void* Ws,
+                      const void* A, const void* B, const float* XA,
+                      void* dX, float* dA, float* dB,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* lora_status_str(lora_status s);
+
+/* Name of the HIP error behind the last LORA_ERR_HIP on the calling thread (static storage). */
+const char* lora_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

@@ -1,0 +1,136 @@
+// Device helpers shared by the gfx950 kernels of the LoRA / QLoRA layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Tiles and launch shape of the MFMA kernels: 256 threads = 4 waves of 64 lanes, one
+// 256 x 256 output tile per workgroup, contraction staged through LDS 64 at a time.
+constexpr int kThreads = 256;
+constexpr int kTile = 256;
+constexpr int kStep = 64;
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l holds, for both operands,
+// row (l & 15) of its 16-row operand and the 8 contraction indices 8*(l >> 4) .. +7;
+// it receives D rows 4*(l >> 4) .. +3 of column (l & 15).
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 v as hi + lo with both parts bf16 (|v - hi - lo| <= 2^-16 |v|): lets an fp32 panel
+// enter a bf16 MFMA without losing the accuracy of the fp32 accumulator.
+__device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
+  const uint32_t h = pack_bf16(v, 0.f) & 0xffffu;
+  hi = __uint_as_float(h << 16);
+  lo = v - hi;  // exact
+}
+
+// LDS operand tiles are rows of 64 bf16 (eight 16-byte chunks).  Chunk c of row r sits at
+// chunk slot c ^ swz(r): 8 consecutive rows read at one chunk column, and 8 rows spaced 8
+// apart written at one chunk column, both land in 8 distinct slots (no bank conflicts for
+// 16-byte accesses, which the LDS serves 8 lanes at a time).
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return (r << 6) + ((c ^ swz(r)) << 3); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 zero4() { return (u32x4){0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ f32x4 fzero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
+
+// Transpose an 8x8 block of bf16 held as 8 rows of 8 (row i in in[i]) into 8 columns
+// (column j in out[j]), using byte permutes.
+__device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {      // source dword e holds columns 2e (low) and 2e+1 (high)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {    // destination dword d holds rows 2d (low) and 2d+1 (high)
+      const uint32_t lo_src = in[2 * d][e], hi_src = in[2 * d + 1][e];
+      out[2 * e][d] = __builtin_amdgcn_perm(hi_src, lo_src, 0x05040100u);
+      out[2 * e + 1][d] = __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);
+    }
+  }
+}
+
+// ---- int4 unpack ------------------------------------------------------------------------
+// A packed dword holds 8 codes, code i (k offset i) in bits 4i .. 4i+3 as 4-bit two's
+// complement.  XOR with 0x8 per nibble turns code q into the unsigned u = q + 8, so
+//   q * s = fma(u, s, -8 s)
+// exactly (the exact product has at most 14 significant bits).  The even codes sit in the
+// low nibble of each byte, the odd codes (times 16) in the high nibble, so each value costs
+// one byte-to-float conversion and one fma, and every two values one bf16 pack.
+struct I4Scale {
+  float s, s_16, m8s;  // s, s / 16, -8 s  (all exact)
+};
+__device__ __forceinline__ I4Scale i4scale(float s) { return {s, s * 0.0625f, -8.f * s}; }
+
+__device__ __forceinline__ float ubyte(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xffu); }
+
+// The 8 codes of one packed dword -> 8 bf16 values bf16_rne(q * s), in k order, as 4 pairs.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, const I4Scale& sc) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0f0f0f0fu, hi = x & 0xf0f0f0f0u;
+  u32x4 o;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    o[b] = pack_bf16(fmaf(ubyte(lo, b), sc.s, sc.m8s), fmaf(ubyte(hi, b), sc.s_16, sc.m8s));
+  return o;
+}
+
+// Offset-binary form of a packed dword for single-code access with dq1().
+struct I4Word {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ I4Word i4word(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  return {x & 0x0f0f0f0fu, x & 0xf0f0f0f0u};
+}
+// q * s of code e (0..7) of a word prepared by i4word() (exact fp32; e must be a constant).
+__device__ __forceinline__ float dq1(const I4Word& w, int e, const I4Scale& sc) {
+  return (e & 1) ? fmaf(ubyte(w.hi, e >> 1), sc.s_16, sc.m8s) : fmaf(ubyte(w.lo, e >> 1), sc.s, sc.m8s);
+}
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Workgroup id -> logical tile id such that each of the 8 XCDs (which receive workgroups
+// round-robin by id) owns one contiguous range of logical tiles; a bijection for any total.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int q = total >> 3, rem = total & 7;
+  const int x = bid & 7, local = bid >> 3;
+  return x * q + min(x, rem) + local;
+}
+
+// Logical tile id -> (row tile, column tile), walking `group` row tiles at a time so that
+// workgroups running together share operand panels in L2.
+__device__ __forceinline__ void grouped_tile(int t, int tiles_r, int tiles_c, int group,
+                                             int& tr, int& tc) {
+  const int per = group * tiles_c;
+  const int g = t / per;
+  const int first = g * group;
+  const int gs = min(group, tiles_r - first);
+  const int r = t - g * per;
+  tr = first + r % gs;
+  tc = r / gs;
+}
+
+}  // namespace lora

@@ -1,0 +1,72 @@
+// Host-side launchers of the gfx950 kernels (argument structs shared by the C ABI layer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+// Rows of tokens reduced by one split of the token-dimension (split-K) dA / dB sums.
+constexpr int64_t kSplitRows = 256;
+
+struct FwdArgs {
+  const void* X;
+  const void* W;   // bf16 [N][K], fp32 [N][K], or packed int4 [N][K/2]
+  const void* Ws;  // fp16 scales [N][K/64] (int4 only)
+  const void* A;
+  const void* B;
+  void* Y;
+  float* XA;       // may be null
+  int64_t M, N, K;
+  int R;
+  float scale;
+};
+
+struct DxArgs {
+  const void* dY;
+  const void* W;
+  const void* Ws;
+  const void* A;
+  const void* B;
+  void* dX;
+  float* G;        // [M][R] fp32: dY B, written for the dA reduction
+  int64_t M, N, K;
+  int R;
+  float scale;
+};
+
+struct DadbArgs {
+  const void* X;    // [M][K]
+  const void* dY;   // [M][N]
+  const float* G;   // [M][R]
+  const float* XA;  // [M][R]
+  float* partA;     // [splits][R][K]
+  float* partB;     // [splits][R][N]
+  float* dA;        // [R][K]
+  float* dB;        // [N][R]
+  int64_t M, N, K;
+  int R;
+  float scale;
+  int splits;
+};
+
+// bf16 / int4 MFMA paths
+hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
+hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s);
+hipError_t launch_dadb_partials_bf16(const DadbArgs& a, hipStream_t s);
+// fp32 paths
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_dx_f32(const DxArgs& a, hipStream_t s);
+hipError_t launch_dadb_partials_f32(const DadbArgs& a, hipStream_t s);
+// fixed-order reduction of the partials into dA and dB (any element type)
+hipError_t launch_dadb_reduce(const DadbArgs& a, hipStream_t s);
+// int4 utilities and the small-M matrix-vector path
+hipError_t launch_quantize_int4(int64_t N, int64_t K, const float* W, uint8_t* Wq, uint16_t* Ws,
+                                hipStream_t s);
+hipError_t launch_dequant_int4(int64_t N, int64_t K, const uint8_t* Wq, const uint16_t* Ws,
+                               uint16_t* Wout, hipStream_t s);
+// decode path: `part` holds gemv_workspace_floats() floats of split partial sums
+hipError_t launch_gemv_int4(const FwdArgs& a, float* part, hipStream_t s);
+size_t gemv_workspace_floats(int64_t N, int64_t K, int R);
+
+}  // namespace lora

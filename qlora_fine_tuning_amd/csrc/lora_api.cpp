@@ -1,0 +1,218 @@
+// C ABI of the fused LoRA / QLoRA layer: argument validation (before any HIP call), workspace
+// layout, and dispatch to the gfx950 kernels.  Declarations and conventions: include/lora.h.
+#include "lora.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+using namespace lora;
+
+thread_local const char* g_last_hip_error = "hipSuccess";
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lora_status check_dims(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0) return LORA_ERR_SHAPE;
+  if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems) return LORA_ERR_SHAPE;
+  if (M * K >= kMaxElems || M * N >= kMaxElems || N * K >= kMaxElems) return LORA_ERR_SHAPE;
+  if (R < 8 || R > 64 || R % 8 != 0) return LORA_ERR_RANK;
+  return LORA_OK;
+}
+
+// every pointer non-null and 16-byte aligned
+template <typename... P>
+lora_status check_ptrs(P... ps) {
+  const void* arr[] = {static_cast<const void*>(ps)...};
+  for (const void* p : arr)
+    if (p == nullptr) return LORA_ERR_NULL;
+  for (const void* p : arr)
+    if (!aligned16(p)) return LORA_ERR_ALIGN;
+  return LORA_OK;
+}
+
+lora_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return LORA_OK;
+  g_last_hip_error = hipGetErrorName(e);
+  return LORA_ERR_HIP;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int64_t splits_for(int64_t M) { return (M + kSplitRows - 1) / kSplitRows; }
+
+// Backward workspace: G [M][R] fp32 | partA [splits][R][K] fp32 | partB [splits][R][N] fp32.
+struct BwdLayout {
+  size_t g, pa, pb, total;
+};
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R) {
+  const int64_t s = splits_for(M);
+  BwdLayout l;
+  l.g = 0;
+  l.pa = align256((size_t)M * R * sizeof(float));
+  l.pb = l.pa + align256((size_t)s * R * K * sizeof(float));
+  l.total = l.pb + align256((size_t)s * R * N * sizeof(float));
+  return l;
+}
+
+bool use_gemv(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K % 256 == 0; }
+
+lora_status bwd_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R,
+                       float scale, const void* dY, const void* X, const void* W, const void* Ws,
+                       const void* A, const void* B, const float* XA, void* dX, float* dA,
+                       float* dB, void* ws, size_t ws_bytes, void* stream) {
+  const BwdLayout lay = bwd_layout(M, N, K, R);
+  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* G = reinterpret_cast<float*>(base + lay.g);
+  DadbArgs d{X, dY, G, XA, reinterpret_cast<float*>(base + lay.pa), reinterpret_cast<float*>(base + lay.pb),
+             dA, dB, M, N, K, R, scale, (int)splits_for(M)};
+  if (M > 0) {
+    DxArgs a{dY, W, Ws, A, B, dX, G, M, N, K, R, scale};
+    hipError_t e = (dt == LORA_F32) ? launch_dx_f32(a, s) : launch_dx_mfma(a, int4, s);
+    if (e != hipSuccess) return from_hip(e);
+    e = (dt == LORA_F32) ? launch_dadb_partials_f32(d, s) : launch_dadb_partials_bf16(d, s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return from_hip(launch_dadb_reduce(d, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_status_str(lora_status st) {
+  switch (st) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
+    case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: M < 0, N or K not a positive multiple of 64, or a tensor too large";
+    case LORA_ERR_RANK: return "LORA_ERR_RANK: R must be a multiple of 8 in [8, 64]";
+    case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE: unknown element type";
+    case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace missing or too small";
+    case LORA_ERR_GROUP: return "LORA_ERR_GROUP: int4 group size must be 64";
+    case LORA_ERR_VALUE: return "LORA_ERR_VALUE: scale must be finite";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown lora_status";
+}
+
+const char* lora_last_hip_error(void) { return g_last_hip_error; }
+
+lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                     const void* X, const void* W, const void* A, const void* B, void* Y, float* XA,
+                     void* stream) {
+  if (dt != LORA_F32 && dt != LORA_BF16) return LORA_ERR_DTYPE;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(W, A, B);
+  if (st != LORA_OK) return st;
+  if (M == 0) return LORA_OK;  // empty batch: X, Y and XA may be NULL
+  st = check_ptrs(X, Y);
+  if (st != LORA_OK) return st;
+  if (XA != nullptr && !aligned16(XA)) return LORA_ERR_ALIGN;
+  FwdArgs a{X, W, nullptr, A, B, Y, XA, M, N, K, R, scale};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(dt == LORA_F32 ? launch_fwd_f32(a, s) : launch_fwd_mfma(a, false, s));
+}
+
+size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (dt != LORA_F32 && dt != LORA_BF16) return 0;
+  if (check_dims(M, N, K, R) != LORA_OK) return 0;
+  return bwd_layout(M, N, K, R).total;
+}
+
+lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                     const void* dY, const void* X, const void* W, const void* A, const void* B,
+                     const float* XA, void* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (dt != LORA_F32 && dt != LORA_BF16) return LORA_ERR_DTYPE;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(W, A, B, dA, dB);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(dY, X, XA, dX)) != LORA_OK) return st;
+  return bwd_common(false, dt, M, N, K, R, scale, dY, X, W, nullptr, A, B, XA, dX, dA, dB, ws,
+                    ws_bytes, stream);
+}
+
+lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W, uint8_t* Wq,
+                           void* Ws, void* stream) {
+  if (group != 64) return LORA_ERR_GROUP;
+  if (N <= 0 || K <= 0 || K % 64 != 0 || N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems)
+    return LORA_ERR_SHAPE;
+  lora_status st = check_ptrs(W, Wq, Ws);
+  if (st != LORA_OK) return st;
+  return from_hip(launch_quantize_int4(N, K, W, Wq, static_cast<uint16_t*>(Ws),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq, const void* Ws,
+                          void* W_bf16, void* stream) {
+  if (group != 64) return LORA_ERR_GROUP;
+  if (N <= 0 || K <= 0 || K % 64 != 0 || N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems)
+    return LORA_ERR_SHAPE;
+  lora_status st = check_ptrs(Wq, Ws, W_bf16);
+  if (st != LORA_OK) return st;
+  return from_hip(launch_dequant_int4(N, K, Wq, static_cast<const uint16_t*>(Ws),
+                                      static_cast<uint16_t*>(W_bf16), static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (check_dims(M, N, K, R) != LORA_OK) return 0;
+  if (!use_gemv(M, K)) return 0;
+  return align256(gemv_workspace_floats(N, K, R) * sizeof(float));
+}
+
+lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                      const void* X, const uint8_t* Wq, const void* Ws, const void* A, const void* B,
+                      void* Y, float* XA, void* ws, size_t ws_bytes, void* stream) {
+  if (group != 64) return LORA_ERR_GROUP;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(Wq, Ws, A, B);
+  if (st != LORA_OK) return st;
+  if (M == 0) return LORA_OK;  // empty batch: X, Y and XA may be NULL
+  st = check_ptrs(X, Y);
+  if (st != LORA_OK) return st;
+  if (XA != nullptr && !aligned16(XA)) return LORA_ERR_ALIGN;
+  const size_t need = qlora_fwd_workspace_bytes(M, N, K, R);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return LORA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
+  FwdArgs a{X, Wq, Ws, A, B, Y, XA, M, N, K, R, scale};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_gemv(M, K)) return from_hip(launch_gemv_int4(a, static_cast<float*>(ws), s));
+  return from_hip(launch_fwd_mfma(a, true, s));
+}
+
+size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (check_dims(M, N, K, R) != LORA_OK) return 0;
+  return bwd_layout(M, N, K, R).total;
+}
+
+lora_status qlora_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                      const void* dY, const void* X, const uint8_t* Wq, const void* Ws, const void* A,
+                      const void* B, const float* XA, void* dX, float* dA, float* dB, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (group != 64) return LORA_ERR_GROUP;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(Wq, Ws, A, B, dA, dB);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(dY, X, XA, dX)) != LORA_OK) return st;
+  return bwd_common(true, LORA_BF16, M, N, K, R, scale, dY, X, Wq, Ws, A, B, XA, dX, dA, dB, ws,
+                    ws_bytes, stream);
+}
+
+}  // extern "C"

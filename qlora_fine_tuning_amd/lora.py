@@ -1,0 +1,237 @@
+"""Python binding of the C ABI in include/lora.h (ctypes; argument marshalling only).
+
+Every entry point keeps the C name.  Tensors are torch CUDA tensors used as device memory;
+outputs and workspaces that the caller does not pass are allocated here with torch.  All
+arithmetic runs in the gfx950 HIP library: if it is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblora_mi355x.so")
+
+LORA_F32, LORA_BF16 = 0, 1
+GROUP = 64
+STATUS = {
+    0: "LORA_OK", 1: "LORA_ERR_NULL", 2: "LORA_ERR_SHAPE", 3: "LORA_ERR_RANK", 4: "LORA_ERR_ALIGN",
+    5: "LORA_ERR_DTYPE", 6: "LORA_ERR_WORKSPACE", 7: "LORA_ERR_GROUP", 8: "LORA_ERR_VALUE",
+    9: "LORA_ERR_HIP",
+}
+
+# C signatures: name -> (restype, argtypes)
+_i64, _i32, _f32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = {
+    "lora_fwd": (_i32, [_i32, _i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p]),
+    "lora_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i32]),
+    "lora_bwd": (_i32, [_i32, _i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "qlora_quantize": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p]),
+    "qlora_dequant": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p]),
+    "qlora_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "qlora_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "qlora_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "qlora_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "lora_status_str": (ctypes.c_char_p, [_i32]),
+    "lora_last_hip_error": (ctypes.c_char_p, []),
+}
+
+_LIB = None
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _LIB
+        msg = lib.lora_status_str(status).decode() if lib is not None else STATUS.get(status, str(status))
+        if status == 9 and lib is not None:
+            msg += f" ({lib.lora_last_hip_error().decode()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def load(path: Optional[str] = None):
+    """Load the HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m qlora_fine_tuning_amd.build` "
+                           "(the layer has no other implementation)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise LoraError(fn, st)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LORA_F32
+    if t.dtype == torch.bfloat16:
+        return LORA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _want(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def lora_fwd(X, W, A, B, scale: float, *, Y=None, XA=None, save_xa: bool = True,
+             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Y = X W^T + scale (X A^T) B^T; returns (Y, XA) with XA = X A^T in fp32 (or None)."""
+    lib = load()
+    dt = _dtype_code(X)
+    for t, n in ((X, "X"), (W, "W"), (A, "A"), (B, "B")):
+        _want(t, n, X.dtype)
+    M, K = X.shape
+    N, R = W.shape[0], A.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    if XA is None and save_xa:
+        XA = torch.empty((M, R), dtype=torch.float32, device=X.device)
+    st = lib.lora_fwd(dt, M, N, K, R, float(scale), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(Y),
+                      _ptr(XA), _stream(stream))
+    _check("lora_fwd", st)
+    return Y, XA
+
+
+def lora_bwd_workspace_bytes(dt: int, M: int, N: int, K: int, R: int) -> int:
+    return int(load().lora_bwd_workspace_bytes(dt, M, N, K, R))
+
+
+def lora_bwd(dY, X, W, A, B, XA, scale: float, *, dX=None, dA=None, dB=None, ws=None,
+             stream=None):
+    """Returns (dX, dA, dB): dX in X's dtype, dA (R x K) and dB (N x R) in fp32."""
+    lib = load()
+    dt = _dtype_code(X)
+    M, K = X.shape
+    N, R = W.shape[0], A.shape[0]
+    dev = X.device
+    if dX is None:
+        dX = torch.empty((M, K), dtype=X.dtype, device=dev)
+    if dA is None:
+        dA = torch.empty((R, K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((N, R), dtype=torch.float32, device=dev)
+    need = lib.lora_bwd_workspace_bytes(dt, M, N, K, R)
+    if ws is None:
+        ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    st = lib.lora_bwd(dt, M, N, K, R, float(scale), _ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B),
+                      _ptr(XA), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws.numel() * ws.element_size(),
+                      _stream(stream))
+    _check("lora_bwd", st)
+    return dX, dA, dB
+
+
+def qlora_quantize(W32, *, stream=None):
+    """fp32 W (N x K) -> (Wq uint8 N x K/2, Ws fp16 N x K/64)."""
+    lib = load()
+    _want(W32, "W", torch.float32)
+    N, K = W32.shape
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W32.device)
+    Ws = torch.empty((N, max(K // GROUP, 1)), dtype=torch.float16, device=W32.device)
+    st = lib.qlora_quantize(N, K, GROUP, _ptr(W32), _ptr(Wq), _ptr(Ws), _stream(stream))
+    _check("qlora_quantize", st)
+    return Wq, Ws
+
+
+def qlora_dequant(Wq, Ws, *, out=None, stream=None):
+    """Dequantised weight bf16_rne(q * s) as a bf16 N x K tensor."""
+    lib = load()
+    N, K = Wq.shape[0], Wq.shape[1] * 2
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=Wq.device)
+    st = lib.qlora_dequant(N, K, GROUP, _ptr(Wq), _ptr(Ws), _ptr(out), _stream(stream))
+    _check("qlora_dequant", st)
+    return out
+
+
+def qlora_fwd_workspace_bytes(M: int, N: int, K: int, R: int) -> int:
+    return int(load().qlora_fwd_workspace_bytes(M, N, K, R))
+
+
+def qlora_fwd(X, Wq, Ws, A, B, scale: float, *, Y=None, XA=None, save_xa: bool = True, ws=None,
+              stream=None):
+    lib = load()
+    M, K = X.shape
+    N, R = Wq.shape[0], A.shape[0]
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if XA is None and save_xa:
+        XA = torch.empty((M, R), dtype=torch.float32, device=dev)
+    need = lib.qlora_fwd_workspace_bytes(M, N, K, R)
+    if ws is None and need:
+        ws = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib.qlora_fwd(M, N, K, R, float(scale), GROUP, _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A), _ptr(B),
+                       _ptr(Y), _ptr(XA), _ptr(ws), wsb, _stream(stream))
+    _check("qlora_fwd", st)
+    return Y, XA
+
+
+def qlora_bwd_workspace_bytes(M: int, N: int, K: int, R: int) -> int:
+    return int(load().qlora_bwd_workspace_bytes(M, N, K, R))
+
+
+def qlora_bwd(dY, X, Wq, Ws, A, B, XA, scale: float, *, dX=None, dA=None, dB=None, ws=None,
+              stream=None):
+    lib = load()
+    M, K = X.shape
+    N, R = Wq.shape[0], A.shape[0]
+    dev = X.device
+    if dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty((R, K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((N, R), dtype=torch.float32, device=dev)
+    need = lib.qlora_bwd_workspace_bytes(M, N, K, R)
+    if ws is None:
+        ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    st = lib.qlora_bwd(M, N, K, R, float(scale), GROUP, _ptr(dY), _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A),
+                       _ptr(B), _ptr(XA), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                       ws.numel() * ws.element_size(), _stream(stream))
+    _check("qlora_bwd", st)
+    return dX, dA, dB
+
+
+class LoRALinearFunction(torch.autograd.Function):
+    """Autograd wrapper: the forward saves X A^T (fp32) for the backward."""
+
+    @staticmethod
+    def forward(ctx, X, W, A, B, scale):
+        Y, XA = lora_fwd(X, W, A, B, scale)
+        ctx.save_for_backward(X, W, A, B, XA)
+        ctx.scale = scale
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, W, A, B, XA = ctx.saved_tensors
+        dX, dA, dB = lora_bwd(dY.contiguous(), X, W, A, B, XA, ctx.scale)
+        return dX, None, dA.to(A.dtype), dB.to(B.dtype), None

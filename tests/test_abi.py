@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point that
+include/lora.h declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from qlora_fine_tuning_amd import lora
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lora.LIB_PATH):
+        from qlora_fine_tuning_amd import build
+
+        build.build()
+    return lora.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keywords = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in keywords and (n.startswith("lora_") or n.startswith("qlora_"))})
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("lora_fwd", "lora_bwd", "lora_bwd_workspace_bytes", "qlora_fwd", "qlora_bwd",
+              "qlora_quantize", "qlora_dequant", "qlora_fwd_workspace_bytes",
+              "qlora_bwd_workspace_bytes", "lora_status_str", "lora_last_hip_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in lora.h but not exported"
+    assert set(declared_functions()) == set(lora.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    for code, name in lora.STATUS.items():
+        assert lib.lora_status_str(code).decode().startswith(name)
+
+
+# Fake, 16-byte aligned, never dereferenced: validation fails before any HIP call.
+P = ctypes.c_void_p(0x10000)
+MIS = ctypes.c_void_p(0x10008)
+NUL = None
+
+
+def fwd(lib, dt=1, M=64, N=256, K=256, R=16, scale=2.0, X=P, W=P, A=P, B=P, Y=P, XA=P):
+    return lib.lora_fwd(dt, M, N, K, R, scale, X, W, A, B, Y, XA, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), 5),
+    (dict(N=100), 2), (dict(K=96), 2), (dict(M=-1), 2), (dict(N=0), 2),
+    (dict(R=12), 3), (dict(R=0), 3), (dict(R=72), 3),
+    (dict(scale=float("nan")), 8), (dict(scale=float("inf")), 8),
+    (dict(X=NUL), 1), (dict(W=NUL), 1), (dict(A=NUL), 1), (dict(B=NUL), 1), (dict(Y=NUL), 1),
+    (dict(X=MIS), 4), (dict(W=MIS), 4), (dict(XA=MIS), 4),
+])
+def test_lora_fwd_validation(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_lora_fwd_empty_batch_is_ok_without_token_buffers(lib):
+    # M == 0: nothing to compute, X / Y / XA may be NULL, and no HIP call is made
+    assert fwd(lib, M=0, X=NUL, Y=NUL, XA=NUL) == 0
+
+
+def bwd(lib, dt=1, M=64, N=256, K=256, R=16, scale=2.0, ws=P, ws_bytes=None, **ptrs):
+    p = dict(dY=P, X=P, W=P, A=P, B=P, XA=P, dX=P, dA=P, dB=P)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.lora_bwd_workspace_bytes(dt, M, N, K, R)
+    return lib.lora_bwd(dt, M, N, K, R, scale, p["dY"], p["X"], p["W"], p["A"], p["B"], p["XA"],
+                        p["dX"], p["dA"], p["dB"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), 5), (dict(K=32), 2), (dict(R=4), 3),
+    (dict(dY=NUL), 1), (dict(XA=NUL), 1), (dict(dA=NUL), 1), (dict(dB=NUL), 1),
+    (dict(dX=MIS), 4),
+    (dict(ws=NUL), 6), (dict(ws_bytes=16), 6), (dict(ws=MIS), 4),
+])
+def test_lora_bwd_validation(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_workspace_sizes(lib):
+    # G (M x R fp32) + split partials of dA and dB, one split per 256 tokens
+    M, N, K, R = 8192, 4096, 4096, 16
+    need = lib.lora_bwd_workspace_bytes(1, M, N, K, R)
+    splits = M // 256
+    assert need >= 4 * (M * R + splits * R * (K + N))
+    assert need < 4 * (M * R + splits * R * (K + N)) + 3 * 256
+    assert lib.lora_bwd_workspace_bytes(1, M, N, K, 12) == 0  # invalid rank
+    assert lib.qlora_bwd_workspace_bytes(M, N, K, R) == need
+    # the decode path keeps split partial sums; the large-M path needs none
+    assert lib.qlora_fwd_workspace_bytes(4, 27648, 5120, 16) > 0
+    assert lib.qlora_fwd_workspace_bytes(4096, 27648, 5120, 16) == 0
+
+
+def test_qlora_validation(lib):
+    assert lib.qlora_quantize(64, 128, 32, P, P, P, None) == 7
+    assert lib.qlora_quantize(64, 100, 64, P, P, P, None) == 2
+    assert lib.qlora_quantize(64, 128, 64, NUL, P, P, None) == 1
+    assert lib.qlora_dequant(64, 128, 64, P, MIS, P, None) == 4
+    assert lib.qlora_fwd(4, 256, 256, 16, 2.0, 64, P, P, P, P, P, P, P, NUL, 0, None) == 6
+    assert lib.qlora_fwd(4, 256, 256, 16, 2.0, 63, P, P, P, P, P, P, P, P, 1 << 20, None) == 7
+    assert lib.qlora_bwd(64, 256, 256, 16, 2.0, 64, P, P, P, P, P, P, P, P, P, P, P, 0, None) == 6
+
+
+def test_binding_refuses_to_run_without_the_library(tmp_path):
+    # the product path has no fallback: a missing library is an error, never a silent CPU path
+    saved = lora._LIB
+    try:
+        lora._LIB = None
+        with pytest.raises(RuntimeError):
+            lora.load(str(tmp_path / "missing.so"))
+    finally:
+        lora._LIB = saved
