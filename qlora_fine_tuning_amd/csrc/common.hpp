@@ -44,11 +44,36 @@ __device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
 }
 
 // LDS operand tiles are rows of 64 bf16 (eight 16-byte chunks).  Chunk c of row r sits at
-// chunk slot c ^ swz(r): 8 consecutive rows read at one chunk column, and 8 rows spaced 8
-// apart written at one chunk column, both land in 8 distinct slots (no bank conflicts for
-// 16-byte accesses, which the LDS serves 8 lanes at a time).
+// chunk slot c ^ swz(r).
+//  * swz: 8 consecutive rows read at one chunk column, and 8 rows spaced 8 apart written at
+//    one chunk column (the in-register transposes), both land in 8 distinct slots.
+//  * swzf ("fixed"): 16 consecutive rows read at one chunk column hit 16 distinct
+//    (row parity, slot) pairs, i.e. distinct banks over 256 bytes, and the slot depends only
+//    on bits 0..3 of the row, so fragment rows 16 apart differ by a constant address and
+//    every fragment read of a wave shares one address register.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return (r << 6) + ((c ^ swz(r)) << 3); }
+__device__ __forceinline__ int swzf(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lds_offf(int r, int c) { return (r << 6) + ((c ^ swzf(r)) << 3); }
+
+// ---- buffer loads ----------------------------------------------------------------------
+// A buffer resource covers `bytes` bytes from `base`; loads whose offset falls outside read
+// zero.  buffer_load ... lds (16 bytes per lane) writes a wave's 64 x 16 bytes to LDS at
+// consecutive addresses starting at the given LDS pointer, with no VGPRs in between.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#define LORA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LORA_LDS(lds), 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+// s_waitcnt vmcnt(0): this wave's outstanding vector-memory loads (LDS DMA included) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

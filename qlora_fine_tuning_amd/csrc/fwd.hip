@@ -5,7 +5,8 @@
 // tutorial ch. 5 "加速原理：Triton kernel 与 fused LoRA", §5.3: one program per output tile
 // accumulates the base product and the low-rank product and stores Y once, so no
 // intermediate reaches HBM.  Here one workgroup owns a 256 x 256 tile of Y:
-//  * the K loop stages X, W and A tiles (64 wide) through double-buffered LDS;
+//  * the K loop stages X, W and A tiles (64 wide) through two LDS buffers.  X, A and bf16 W
+//    go HBM -> LDS with buffer_load ... lds (no registers on the way), issued one step ahead;
 //  * each wave accumulates a 128 x 128 block of Y^T on 16x16x32 bf16 MFMA (the W tile is
 //    the row operand, so each lane ends up holding 4 consecutive outputs of one Y row);
 //  * the same LDS X fragments feed the rank-R panel X A^T (each of the two waves that
@@ -28,10 +29,12 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 const uint16_t* __restrict__ Bm, uint16_t* __restrict__ Y,
                 float* __restrict__ XA, int M, int N, int K, int R, float scale) {
   constexpr int TT = kTile * kStep;  // elements of one 256 x 64 operand tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TT + 2 * RP * kStep];
-  uint16_t* const sX = smem;           // [2][256 rows m][64 k]
-  uint16_t* const sW = smem + 2 * TT;  // [2][256 rows n][64 k]
-  uint16_t* const sA = smem + 4 * TT;  // [2][RP rows][64 k]
+  constexpr int AROWS = RP < 32 ? 32 : RP;  // adapter rows in LDS: each wave copies 8k of them
+  constexpr int AT = AROWS * kStep;
+  // Separate arrays per buffer: the compiler can then see that loads into one buffer never
+  // alias reads of the other and keeps the copy engine and the MFMA loop overlapped.
+  __shared__ __attribute__((aligned(1024))) uint16_t sX0[TT], sX1[TT], sW0[TT], sW1[TT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[AT], sA1[AT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -43,75 +46,64 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 8, tm, tn);
   const int m0 = tm * kTile, n0 = tn * kTile;
   const int nk = K / kStep;
+  const uint32_t rowb = (uint32_t)K * 2;  // bytes per row of X, W (bf16) and A
 
-  constexpr int AQ = (RP * 8 + kThreads - 1) / kThreads;  // 16-byte chunks of the A tile per thread
-  u32x4 rx[8], rw[8], ra[AQ];
-  float rs[2] = {0.f, 0.f};
+  const rsrc_t rX = make_rsrc(X + (size_t)m0 * K, (uint32_t)min(M - m0, kTile) * rowb);
+  const rsrc_t rA = make_rsrc(A, (uint32_t)R * rowb);
+  rsrc_t rW;
+  if constexpr (!INT4) rW = make_rsrc(static_cast<const uint16_t*>(Wp) + (size_t)n0 * K,
+                                      (uint32_t)min(N - n0, kTile) * rowb);
 
-  auto gload = [&](int kt) {
-    const int k0 = kt * kStep;
+  // Lane offsets of the 16-byte LDS-DMA chunks: instruction i of wave w fills rows
+  // (4i + w) * 8 .. +7 of a 256-row tile; lane l goes to physical chunk l & 7 of row
+  // (l >> 3) there, which holds logical chunk (l & 7) ^ swz(row).
+  // With swzf the slot does not depend on i, so one lane offset serves all 8 instructions.
+  const uint32_t tile_voff = [&]() {
+    const int r = wave * 8 + (lane >> 3);
+    return (uint32_t)r * rowb + (uint32_t)((lane & 7) ^ swzf(r)) * 16u;
+  }();
+  auto dma_tile = [&](const rsrc_t& rs, uint16_t* dst, int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = i * kThreads + tid, r = c >> 3, ch = c & 7;
-      rx[i] = (m0 + r < M) ? ld16(X + (size_t)(m0 + r) * K + k0 + ch * 8) : zero4();
-    }
-    if constexpr (!INT4) {
-      const uint16_t* W = static_cast<const uint16_t*>(Wp);
+    for (int i = 0; i < 8; ++i)
+      dma16(rs, dst + (4 * i + wave) * 512, tile_voff, (uint32_t)k0 * 2u + (uint32_t)i * 32u * rowb);
+  };
+  auto dma_a = [&](uint16_t* dst, int k0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = i * kThreads + tid, r = c >> 3, ch = c & 7;
-        rw[i] = (n0 + r < N) ? ld16(W + (size_t)(n0 + r) * K + k0 + ch * 8) : zero4();
-      }
-    } else {
-      // one row per thread pair: thread (tid & 1) takes 32 of the row's 64 codes
-      const uint8_t* Wq = static_cast<const uint8_t*>(Wp);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int n = n0 + q * 128 + (tid >> 1);
-        if (n < N) {
-          rw[q] = ld16(Wq + (size_t)n * (K / 2) + k0 / 2 + (tid & 1) * 16);
-          rs[q] = half_bits_to_f32(Wscale[(size_t)n * (K / 64) + k0 / 64]);
-        } else {
-          rw[q] = zero4();
-          rs[q] = 0.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < AQ; ++q) {
-      const int c = q * kThreads + tid, r = c >> 3, ch = c & 7;
-      ra[q] = (c < RP * 8 && r < R) ? ld16(A + (size_t)r * K + k0 + ch * 8) : zero4();
+    for (int q0 = 0; q0 < AROWS / 8; q0 += 4) {  // rows q*8 .. q*8+7; rows >= R read as zero
+      const int q = q0 + wave;
+      const int r = q * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swzf(r);
+      dma16(rA, dst + q * 512, (uint32_t)r * rowb + (uint32_t)c * 16u, (uint32_t)k0 * 2u);
     }
   };
 
-  auto sstore = [&](int buf) {
-    uint16_t* x = sX + buf * TT;
-    uint16_t* w = sW + buf * TT;
+  // int4 W: one row per thread pair, thread (tid & 1) takes 32 of the row's 64 codes
+  u32x4 rq[2];
+  float rs[2];
+  rsrc_t rWq, rWs;
+  if constexpr (INT4) {
+    const int nrows = min(N - n0, kTile);
+    rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + (size_t)n0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2));
+    rWs = make_rsrc(Wscale + (size_t)n0 * (K / 64), (uint32_t)nrows * (uint32_t)(K / 64) * 2u);
+  }
+  auto load_w4 = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = i * kThreads + tid, r = c >> 3, ch = c & 7;
-      st16(x + lds_off(r, ch), rx[i]);
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t r = (uint32_t)(q * 128 + (tid >> 1));
+      rq[q] = bload16(rWq, r * (uint32_t)(K / 2) + (uint32_t)(tid & 1) * 16u, (uint32_t)k0 / 2u);
+      const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b16(rWs, (int)(r * (uint32_t)(K / 64) * 2u),
+                                                               (int)((uint32_t)k0 / 32u), 0);
+      rs[q] = half_bits_to_f32((uint16_t)sb);
     }
-    if constexpr (!INT4) {
+  };
+  auto store_w4 = [&](uint16_t* w) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = i * kThreads + tid, r = c >> 3, ch = c & 7;
-        st16(w + lds_off(r, ch), rw[i]);
-      }
-    } else {
+    for (int q = 0; q < 2; ++q) {
+      const int r = q * 128 + (tid >> 1);
+      const I4Scale sc = i4scale(rs[q]);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int r = q * 128 + (tid >> 1);
-        const I4Scale sc = i4scale(rs[q]);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)  // packed dword d = codes k = 8d .. 8d+7 of this half
-          st16(w + lds_off(r, (tid & 1) * 4 + d), dequant8(rw[q][d], sc));
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < AQ; ++q) {
-      const int c = q * kThreads + tid;
-      if (c < RP * 8) st16(sA + buf * RP * kStep + lds_off(c >> 3, c & 7), ra[q]);
+      for (int d = 0; d < 4; ++d)  // packed dword d = codes k = 8d .. 8d+7 of this half
+        st16(w + lds_offf(r, (tid & 1) * 4 + d), dequant8(rq[q][d], sc));
     }
   };
 
@@ -126,54 +118,110 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
 #pragma unroll
     for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* x = sX + cur * TT;
-    const uint16_t* w = sW + cur * TT;
-    const uint16_t* a = sA + cur * RP * kStep;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ch = kk * 4 + g4;
-      u32x4 fa[8], fb[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = ld16(w + lds_off(wn * 128 + i * 16 + l16, ch));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = ld16(x + lds_off(wm * 128 + j * 16 + l16, ch));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
-#pragma unroll
-      for (int c = 0; c < RP / 16; ++c) {
-        const u32x4 pa = ld16(a + lds_off(c * 16 + l16, ch));
-        if (wn == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pacc[c][j] = mfma16(pa, fb[j], pacc[c][j]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pacc[c][j] = mfma16(pa, fb[4 + j], pacc[c][j]);
-        }
-      }
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+  // adapter rows R .. AROWS-1 stay zero in both buffers
+  for (int e = R * kStep + tid * 8; e < AT; e += kThreads * 8) {
+    st16(sA0 + e, zero4());
+    st16(sA1 + e, zero4());
   }
 
+  // MFMA operands of one 32-wide half step: 8 W fragments (rows of Y^T), 8 X fragments
+  // (columns of Y^T), RP/16 adapter fragments.
+  struct Frag {
+    u32x4 w[8], x[8], a[RP / 16];
+  };
+  // Reads the fragments of half step `kk` into `nx` while running the MFMAs of `cu`.  The
+  // reads are spread between the MFMA rows so that LDS latency hides behind matrix work.
+  auto phase = [&](const Frag& cu, Frag& nx, const uint16_t* x, const uint16_t* w,
+                   const uint16_t* a, int kk) {
+    const int ch = kk * 4 + g4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      nx.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
+      nx.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(cu.w[i], cu.x[j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < RP / 16; ++c) nx.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 xp = wn ? cu.x[4 + j] : cu.x[j];  // this wave's half of the panel rows
+#pragma unroll
+      for (int c = 0; c < RP / 16; ++c) pacc[c][j] = mfma16(cu.a[c], xp, pacc[c][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto read_frags = [&](Frag& f, const uint16_t* x, const uint16_t* w, const uint16_t* a, int kk) {
+    const int ch = kk * 4 + g4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
+      f.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
+    }
+#pragma unroll
+    for (int c = 0; c < RP / 16; ++c) f.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
+  };
+  auto wait_all = [&]() {
+    wait_vmem();
+    __syncthreads();
+  };
+  // Copies of step kn (clamped to the last step: a repeated copy of the last step into the
+  // idle buffer is harmless and keeps the loop free of branches).
+  auto prefetch = [&](int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an) {
+    const int k1 = min(kn, nk - 1) * kStep;
+    dma_tile(rX, xn, k1);
+    if constexpr (!INT4) dma_tile(rW, wnx, k1);
+    else load_w4(k1);
+    dma_a(an, k1);
+  };
+
+  // Pipeline (buffers b = kt & 1): on entry to step kt the kk = 0 fragments of step kt are in
+  // registers and the copies of step kt+1 are in flight into buffer 1-b.
+  //   read kk = 1 fragments of step kt  ||  MFMAs of kk = 0
+  //   wait for the step kt+1 copies; barrier (everyone is done reading buffer b)
+  //   start the copies of step kt+2 into buffer b
+  //   read kk = 0 fragments of step kt+1  ||  MFMAs of kk = 1
+  Frag f0, f1;
+  prefetch(0, sX0, sW0, sA0);
+  if constexpr (INT4) store_w4(sW0);
+  wait_all();
+  read_frags(f0, sX0, sW0, sA0, 0);
+  prefetch(1, sX1, sW1, sA1);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool odd = kt & 1;
+    uint16_t* const xc = odd ? sX1 : sX0;
+    uint16_t* const wc = odd ? sW1 : sW0;
+    uint16_t* const ac = odd ? sA1 : sA0;
+    uint16_t* const xo = odd ? sX0 : sX1;
+    uint16_t* const wo = odd ? sW0 : sW1;
+    uint16_t* const ao = odd ? sA0 : sA1;
+    phase(f0, f1, xc, wc, ac, 1);
+    if constexpr (INT4) store_w4(wo);  // the unpacked W of step kt+1
+    wait_all();
+    prefetch(kt + 2, xc, wc, ac);
+    phase(f1, f0, xo, wo, ao, 0);
+  }
+  wait_vmem();
+  __syncthreads();
+
   // ---- epilogue: XA panel -> LDS (and HBM once per row tile), then the rank-R update ----
+  // panel rows are spread over the four freed tile buffers, 64 rows each
   constexpr int XS = RP + 4;  // fp32 row stride of the panel in LDS
-  float* const sXA = reinterpret_cast<float*>(smem);
+  static_assert(64 * XS * 4 <= TT * 2, "panel slice must fit a tile buffer");
+  auto xa_rows = [&](int q) -> float* {
+    return reinterpret_cast<float*>(q == 0 ? sX0 : (q == 1 ? sX1 : (q == 2 ? sW0 : sW1)));
+  };
 #pragma unroll
   for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ml = wm * 128 + (wn * 4 + j) * 16 + l16;
       const int rk = c * 16 + g4 * 4;
-      *reinterpret_cast<f32x4*>(sXA + ml * XS + rk) = pacc[c][j];
+      *reinterpret_cast<f32x4*>(xa_rows(ml >> 6) + (ml & 63) * XS + rk) = pacc[c][j];
       if (XA != nullptr && tn == 0 && m0 + ml < M && rk < R)
         *reinterpret_cast<f32x4*>(XA + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
     }
@@ -190,7 +238,8 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float* src = sXA + (wm * 128 + j * 16 + l16) * XS + rk;
+      const int ml = wm * 128 + j * 16 + l16;
+      const float* src = xa_rows(ml >> 6) + (ml & 63) * XS + rk;
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
       const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
