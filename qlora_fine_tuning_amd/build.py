@@ -37,6 +37,14 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The MFMA kernels keep their main accumulators in AGPRs through
+# inline asm; the builtin MFMAs of their small rank-R panels are put in VGPRs so that the two
+# never compete for the AGPR file.
+EXTRA_FLAGS = {
+    "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -68,7 +76,8 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIP_FLAGS, "-x", "hip", "-c", src, "-o", obj]
+        extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+        cmd = [hipcc, *HIP_FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
         _run(cmd, verbose)
         return obj
 

@@ -27,6 +27,29 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// acc += a * b with the accumulator tied in place to AGPRs.  Written as inline asm because
+// the compiler otherwise rotates loop-carried accumulators through temporary registers
+// (hundreds of v_accvgpr_mov per K step).  The compiler does not see the MFMA's hazards, so:
+//  * a and b must be results of LDS or memory loads (s_waitcnt-protected), never fresh VALU
+//    results;
+//  * mfma_acc_ready() must separate the accumulators' initialisation from the first use,
+//    and mfma_drain() the last use from any other instruction that reads them.
+__device__ __forceinline__ void mfma16_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void mfma_acc_ready(f32x4 (&acc)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+  asm volatile("s_nop 7");
+}
+template <int N>
+__device__ __forceinline__ void mfma_drain(f32x4 (&acc)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7");  // > the longest MFMA write-to-read latency
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+}
+
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);

@@ -107,12 +107,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[64];  // acc[i * 8 + j]: Y^T rows (W) block i, columns (X) block j
   f32x4 pacc[RP / 16][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = fzero4();
+  for (int i = 0; i < 64; ++i) acc[i] = fzero4();
+  mfma_acc_ready(acc);
 #pragma unroll
   for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
@@ -140,7 +139,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       nx.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(cu.w[i], cu.x[j], acc[i][j]);
+      for (int j = 0; j < 8; ++j) mfma16_acc(acc[i * 8 + j], cu.w[i], cu.x[j]);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -207,6 +206,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   }
   wait_vmem();
   __syncthreads();
+  mfma_drain(acc);
 
   // ---- epilogue: XA panel -> LDS (and HBM once per row tile), then the rank-R update ----
   // panel rows are spread over the four freed tile buffers, 64 rows each
@@ -252,7 +252,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
         fx[e] = (g4 < 2) ? pack_bf16(h0, h1) : pack_bf16(lo0, lo1);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][j] = mfma16(fbm[i], fx, acc[i][j]);
+      for (int i = 0; i < 8; ++i) acc[i * 8 + j] = mfma16(fbm[i], fx, acc[i * 8 + j]);
     }
   }
 
@@ -264,7 +264,8 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     for (int j = 0; j < 8; ++j) {
       const int m = m0 + wm * 128 + j * 16 + l16;
       if (m < M && n < N) {
-        const u32x2 o = {pack_bf16(acc[i][j][0], acc[i][j][1]), pack_bf16(acc[i][j][2], acc[i][j][3])};
+        const f32x4 v = acc[i * 8 + j];
+        const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
         *reinterpret_cast<u32x2*>(Y + (size_t)m * N + n) = o;
       }
     }
