@@ -42,6 +42,7 @@ HIP_FLAGS = [
 # never compete for the AGPR file.
 EXTRA_FLAGS = {
     "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "dx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

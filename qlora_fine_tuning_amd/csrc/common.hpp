@@ -99,6 +99,17 @@ __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ds_read_b64_tr_b16: each group of 16 lanes reads a 4 x 16 block of 16-bit elements, lane
+// 4i + b passing the address of elements 4b .. 4b+3 of the block's row i; lane l of the group
+// receives column l of the block (rows 0..3 in order).  Two such reads give an MFMA operand
+// whose 8 contraction indices run down a column of a row-major LDS tile.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x4 join(u32x2 a, u32x2 b) { return (u32x4){a[0], a[1], b[0], b[1]}; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x4 zero4() { return (u32x4){0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ f32x4 fzero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }

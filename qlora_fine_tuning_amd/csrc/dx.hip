@@ -6,19 +6,28 @@
 // tutorial ch. 5 "加速原理：Triton kernel 与 fused LoRA", §5.3 (the backward is fused as
 // well); the gradient is derived by hand from Y = X W^T + scale X A^T B^T.  One workgroup
 // owns a 256 (tokens) x 256 (k) tile of dX and loops over N, 64 at a time:
-//  * dY tiles go to LDS as they are (n contiguous); W tiles are read n-major from HBM and
-//    transposed 8 x 8 in registers on the way into LDS, so both MFMA operands are read
-//    with 16-byte LDS loads along the contraction index n;
-//  * the rank-R panel G = dY B is accumulated from the same LDS dY fragments;
-//  * the epilogue adds A^T (scale G)^T with a bf16 hi + lo split of scale * G, then
-//    rounds dX once.
+//  * dY tiles and W tiles go HBM -> LDS with buffer_load ... lds, both in their own row-major
+//    order (coalesced), one step ahead in two buffers;
+//  * the contraction index n runs along dY rows but down W columns: the W operand is read
+//    with ds_read_b64_tr_b16, which hands each lane 4 consecutive rows of one column, so no
+//    transposed copy of W is ever made;
+//  * each wave accumulates a 128 (k) x 128 (m) block of dX^T in AGPRs; the rank-R panel
+//    G = dY B comes from the same LDS dY fragments, with B^T read the same transposing way;
+//  * the epilogue adds A^T (scale G)^T with a bf16 hi + lo split of scale * G, then rounds
+//    dX once.
 // QLoRA: W arrives as packed int4 codes plus fp16 group scales ("探微索隐：Unsloth 如何加速
-// LLM 推理？（以 Qwen 27B 为例）", §二.3); each thread unpacks an 8 (n) x 8 (k) block of
-// codes directly into the transposed order, so no separate transpose is needed.
+// LLM 推理？（以 Qwen 27B 为例）", §二.3); threads unpack them in registers into the same
+// row-major LDS tile.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace lora {
+
+// W tile in LDS: 4 blocks of 64 columns, each 64 rows (n) x 128 bytes; 16-byte chunk c of row
+// r sits in slot c ^ wsw(r).  A transposing read covers 4 consecutive rows x 32 bytes; wsw
+// separates rows r, r+2 (bit 1) and the row groups of neighbouring 16-lane groups (bit 3),
+// so those reads hit distinct banks.
+__device__ __forceinline__ int wsw(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
 
 template <int RP, bool INT4>
 __global__ void __launch_bounds__(kThreads)
@@ -26,11 +35,12 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
                const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
                const uint16_t* __restrict__ Bm, uint16_t* __restrict__ dX,
                float* __restrict__ G, int M, int N, int K, int R, float scale) {
-  constexpr int TT = kTile * kStep;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TT + 2 * RP * kStep];
-  uint16_t* const sDY = smem;           // [2][256 rows m][64 n]
-  uint16_t* const sWT = smem + 2 * TT;  // [2][256 rows k][64 n]
-  uint16_t* const sBT = smem + 4 * TT;  // [2][RP rows][64 n]
+  constexpr int TT = kTile * kStep;  // 16384 elements: dY tile 256 x 64, W tile 64 x 256
+  constexpr int BT = kStep * RP;     // B tile: 64 rows (n) x RP ranks
+  constexpr int BQ = (BT / 8 + kThreads - 1) / kThreads;  // 16-byte chunks per thread
+  constexpr int BTA = BQ * kThreads * 8;  // every thread stores BQ chunks; the tail is padding
+  __shared__ __attribute__((aligned(1024))) uint16_t sD0[TT], sD1[TT], sW0[TT], sW1[TT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BTA], sB1[BTA];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -42,176 +52,227 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_k, 8, tm, tk);
   const int m0 = tm * kTile, k0 = tk * kTile;
   const int nsteps = N / kStep;
+  const uint32_t rowD = (uint32_t)N * 2, rowW = (uint32_t)K * 2;
 
-  // this thread's 8 x 8 block of the W tile: rows n = nb*8 .. +7, columns k = kb*8 .. +7
-  const int nb = tid >> 5, kb = tid & 31;
-  const bool kin = k0 + kb * 8 < K;
-  // this thread's slice of the B tile: row n = tid >> 2, ranks bq .. bq + RP/4 - 1
-  constexpr int BQ = RP / 4;
-  const int bn = tid >> 2, bq = (tid & 3) * BQ;
-
-  u32x4 rdy[8], rw[8];
-  uint32_t rq[8];
-  float rs[8];
-  uint16_t rb[BQ];
-
-  auto gload = [&](int st) {
-    const int n0 = st * kStep;
+  // ---- copies into LDS ----
+  const rsrc_t rD = make_rsrc(dY + (size_t)m0 * N, (uint32_t)min(M - m0, kTile) * rowD);
+  const uint32_t voffD = [&]() {
+    const int r = wave * 8 + (lane >> 3);
+    return (uint32_t)r * rowD + (uint32_t)((lane & 7) ^ swzf(r)) * 16u;
+  }();
+  auto dma_d = [&](uint16_t* dst, int n0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = i * kThreads + tid, r = c >> 3, ch = c & 7;
-      rdy[i] = (m0 + r < M) ? ld16(dY + (size_t)(m0 + r) * N + n0 + ch * 8) : zero4();
-    }
-    if constexpr (!INT4) {
-      const uint16_t* W = static_cast<const uint16_t*>(Wp);
+    for (int i = 0; i < 8; ++i) dma16(rD, dst + (4 * i + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)i * 32u * rowD);
+  };
+  // W (bf16): instruction i of wave w fills block i >> 1, rows ((i & 1) * 4 + w) * 8 .. +7
+  rsrc_t rW;
+  if constexpr (!INT4)
+    rW = make_rsrc(static_cast<const uint16_t*>(Wp) + k0, (uint32_t)((size_t)N * K - k0) * 2u);
+  const uint32_t voffW = [&]() {
+    const int r = wave * 8 + (lane >> 3);  // row within the 64-row tile, less (i & 1) * 32
+    return (uint32_t)r * rowW + (uint32_t)((lane & 7) ^ wsw(r)) * 16u;
+  }();
+  auto dma_w = [&](uint16_t* dst, int n0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        rw[j] = kin ? ld16(W + (size_t)(n0 + nb * 8 + j) * K + k0 + kb * 8) : zero4();
-    } else {
-      const uint8_t* Wq = static_cast<const uint8_t*>(Wp);
+    for (int i = 0; i < 8; ++i)
+      dma16(rW, dst + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffW,
+            (uint32_t)n0 * rowW + (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
+  };
+  // W (int4): thread t unpacks row t >> 2, columns (t & 3) * 64 .. +63 (one scale group)
+  u32x4 rq[2];
+  float rsc = 0.f;
+  rsrc_t rWq, rWs;
+  if constexpr (INT4) {
+    rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + k0 / 2, (uint32_t)((size_t)N * (K / 2) - k0 / 2));
+    rWs = make_rsrc(Wscale + k0 / 64, (uint32_t)((size_t)N * (K / 64) - k0 / 64) * 2u);
+  }
+  const int qrow = tid >> 2, qblk = tid & 3;
+  auto load_w4 = [&](int n0) {
+    const uint32_t r = (uint32_t)(n0 + qrow);
+    const uint32_t vo = r * (uint32_t)(K / 2) + (uint32_t)qblk * 32u;
+    rq[0] = bload16(rWq, vo, 0);
+    rq[1] = bload16(rWq, vo + 16u, 0);
+    rsc = half_bits_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+        rWs, (int)((r * (uint32_t)(K / 64) + (uint32_t)qblk) * 2u), 0, 0));
+  };
+  auto store_w4 = [&](uint16_t* w) {
+    const I4Scale sc = i4scale(rsc);
+    uint16_t* row = w + qblk * 4096 + qrow * 64;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const size_t n = (size_t)(n0 + nb * 8 + j);
-        if (kin) {
-          rq[j] = *reinterpret_cast<const uint32_t*>(Wq + n * (K / 2) + (k0 + kb * 8) / 2);
-          rs[j] = half_bits_to_f32(Wscale[n * (K / 64) + (k0 + kb * 8) / 64]);
-        } else {
-          rq[j] = 0u;
-          rs[j] = 0.f;
-        }
-      }
-    }
+    for (int d = 0; d < 8; ++d) st16(row + ((d ^ wsw(qrow)) << 3), dequant8(rq[d >> 2][d & 3], sc));
+  };
+  // B: 64 rows x RP ranks, through registers (ranks >= R are zero); branch-free: chunks past
+  // the tile read a valid row and land in the padding
+  u32x4 rb[BQ];
+  auto load_b = [&](int n0) {
 #pragma unroll
-    for (int h = 0; h < BQ; h += 4) {
-      const bool in = bq + h < R;
-      const u32x2 v = in ? *reinterpret_cast<const u32x2*>(Bm + (size_t)(n0 + bn) * R + bq + h)
-                         : (u32x2){0u, 0u};
-      rb[h + 0] = (uint16_t)(v[0] & 0xffffu);
-      rb[h + 1] = (uint16_t)(v[0] >> 16);
-      rb[h + 2] = (uint16_t)(v[1] & 0xffffu);
-      rb[h + 3] = (uint16_t)(v[1] >> 16);
+    for (int q = 0; q < BQ; ++q) {
+      const int c = q * kThreads + tid, row = (c / (RP / 8)) & 63, rk = (c % (RP / 8)) * 8;
+      const bool in = rk < R;
+      const u32x4 v = ld16(Bm + (size_t)(n0 + row) * R + (in ? rk : 0));
+      rb[q] = in ? v : zero4();
     }
   };
-
-  auto sstore = [&](int buf) {
-    uint16_t* dy = sDY + buf * TT;
-    uint16_t* wt = sWT + buf * TT;
-    uint16_t* bt = sBT + buf * RP * kStep;
+  auto store_b = [&](uint16_t* b) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = i * kThreads + tid, r = c >> 3, ch = c & 7;
-      st16(dy + lds_off(r, ch), rdy[i]);
-    }
-    if constexpr (!INT4) {
-      u32x4 cols[8];
-      transpose8x8(rw, cols);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st16(wt + lds_off(kb * 8 + e, nb), cols[e]);
-    } else {
-      I4Word wd[8];
-      I4Scale sc[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        wd[j] = i4word(rq[j]);
-        sc[j] = i4scale(rs[j]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {  // column k = kb*8 + e, rows n = nb*8 + 2d, +1
-        u32x4 o;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          o[d] = pack_bf16(dq1(wd[2 * d], e, sc[2 * d]), dq1(wd[2 * d + 1], e, sc[2 * d + 1]));
-        st16(wt + lds_off(kb * 8 + e, nb), o);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < BQ; ++h) bt[lds_off(bq + h, bn >> 3) + (bn & 7)] = rb[h];
+    for (int q = 0; q < BQ; ++q) st16(b + (q * kThreads + tid) * 8, rb[q]);
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[64];  // acc[i * 8 + j]: dX^T rows (k) block i, columns (m) block j
   f32x4 pacc[RP / 16][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = fzero4();
+  for (int i = 0; i < 64; ++i) acc[i] = fzero4();
 #pragma unroll
   for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
+  mfma_acc_ready(acc);
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // transposing-read addresses: lane (l16, g4) reads rows 4 (l16 >> 2) + .. of its 16-lane
+  // group, columns 4 (l16 & 3) ..; per 16-column block q of a 64-column W block the chunk is
+  // 2q + ((l16 & 3) >> 1), swizzled by wsw of a row whose bits 1 and 3 are fixed per lane.
+  const int trow = g4 * 8 + (l16 >> 2);  // + kk * 32 + h * 4
+  const int tsw = wsw(trow);
+  int woff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    woff[q] = trow * 64 + (((2 * q + ((l16 & 3) >> 1)) ^ tsw) << 3) + (l16 & 1) * 4;
+  const int boff = trow * RP + (l16 & 3) * 4;
+
+  struct Frag {
+    u32x4 w[8], d[8], b[RP / 16];
+  };
+  auto wfrag = [&](const uint16_t* w, int kk, int i) -> u32x4 {
+    const int kb = wk * 8 + i;  // 16-column block within the 256-column tile
+    const uint16_t* p = w + (kb >> 2) * 4096 + kk * 32 * 64 + woff[kb & 3];
+    return join(ld_tr(p), ld_tr(p + 4 * 64));
+  };
+  auto bfrag = [&](const uint16_t* b, int kk, int c) -> u32x4 {
+    const uint16_t* p = b + kk * 32 * RP + boff + c * 16;
+    return join(ld_tr(p), ld_tr(p + 4 * RP));
+  };
+  auto phase = [&](const Frag& cu, Frag& nx, const uint16_t* d, const uint16_t* w,
+                   const uint16_t* b, int kk) {
+    const int ch = kk * 4 + g4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      nx.w[i] = wfrag(w, kk, i);
+      nx.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mfma16_acc(acc[i * 8 + j], cu.w[i], cu.d[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < RP / 16; ++c) nx.b[c] = bfrag(b, kk, c);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 dp = wk ? cu.d[4 + j] : cu.d[j];
+#pragma unroll
+      for (int c = 0; c < RP / 16; ++c) pacc[c][j] = mfma16(cu.b[c], dp, pacc[c][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto read_frags = [&](Frag& f, const uint16_t* d, const uint16_t* w, const uint16_t* b, int kk) {
+    const int ch = kk * 4 + g4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f.w[i] = wfrag(w, kk, i);
+      f.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
+    }
+#pragma unroll
+    for (int c = 0; c < RP / 16; ++c) f.b[c] = bfrag(b, kk, c);
+  };
+  auto wait_all = [&]() {
+    wait_vmem();
+    __syncthreads();
+  };
+  auto prefetch = [&](int st, uint16_t* dn, uint16_t* wn, uint16_t* bn) {
+    const int n0 = min(st, nsteps - 1) * kStep;
+    dma_d(dn, n0);
+    if constexpr (!INT4) dma_w(wn, n0);
+    else load_w4(n0);
+    load_b(n0);
+    (void)bn;
+  };
+  auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch
+    if constexpr (INT4) store_w4(wn);
+    store_b(bn);
+  };
+
+  // Same pipeline as the forward kernel (see there), over N steps of 64.
+  Frag f0, f1;
+  prefetch(0, sD0, sW0, sB0);
+  finish(sW0, sB0);
+  wait_all();
+  read_frags(f0, sD0, sW0, sB0, 0);
+  prefetch(1, sD1, sW1, sB1);
 
   for (int st = 0; st < nsteps; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nsteps) gload(st + 1);
-    const uint16_t* dy = sDY + cur * TT;
-    const uint16_t* wt = sWT + cur * TT;
-    const uint16_t* bt = sBT + cur * RP * kStep;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ch = kk * 4 + g4;
-      u32x4 fa[8], fb[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = ld16(wt + lds_off(wk * 128 + i * 16 + l16, ch));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = ld16(dy + lds_off(wm * 128 + j * 16 + l16, ch));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
-#pragma unroll
-      for (int c = 0; c < RP / 16; ++c) {
-        const u32x4 pb = ld16(bt + lds_off(c * 16 + l16, ch));
-        if (wk == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pacc[c][j] = mfma16(pb, fb[j], pacc[c][j]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pacc[c][j] = mfma16(pb, fb[4 + j], pacc[c][j]);
-        }
-      }
-    }
-    if (st + 1 < nsteps) sstore(cur ^ 1);
-    __syncthreads();
+    const bool odd = st & 1;
+    uint16_t* const dc = odd ? sD1 : sD0;
+    uint16_t* const wc = odd ? sW1 : sW0;
+    uint16_t* const bc = odd ? sB1 : sB0;
+    uint16_t* const dn = odd ? sD0 : sD1;
+    uint16_t* const wn = odd ? sW0 : sW1;
+    uint16_t* const bn = odd ? sB0 : sB1;
+    phase(f0, f1, dc, wc, bc, 1);
+    finish(wn, bn);  // the register-staged parts of step st+1
+    wait_all();
+    prefetch(st + 2, dc, wc, bc);
+    phase(f1, f0, dn, wn, bn, 0);
   }
+  wait_vmem();
+  __syncthreads();
+  mfma_drain(acc);
 
-  // ---- epilogue: G panel -> LDS (and HBM once per row tile); A^T tile -> LDS ----
-  constexpr int GS = RP + 4;  // fp32 row stride of G in LDS
-  constexpr int AS = RP + 8;  // bf16 row stride of A^T in LDS
-  float* const sG = reinterpret_cast<float*>(smem);
-  uint16_t* const sAT = reinterpret_cast<uint16_t*>(sG + kTile * GS);
+  // ---- epilogue: G panel -> LDS (and HBM once per row tile); A tile -> LDS ----
+  // The four freed tile buffers each take 64 rows of G (fp32, stride GS) followed by RP/4
+  // rows of the A tile (bf16, stride AS; the 32-byte pad staggers the banks of the 4 rows a
+  // transposing read touches).
+  constexpr int GS = RP + 4;
+  constexpr int AS = kTile + 16;
+  constexpr int AR = RP / 4;                // A rows per buffer
+  constexpr int GBYTES = 64 * GS * 4;
+  static_assert(GBYTES + AR * AS * 2 <= TT * 2, "epilogue tiles must fit a freed buffer");
+  auto buf = [&](int q) -> char* {
+    return reinterpret_cast<char*>(q == 0 ? sD0 : (q == 1 ? sD1 : (q == 2 ? sW0 : sW1)));
+  };
+  auto grow = [&](int ml) -> float* { return reinterpret_cast<float*>(buf(ml >> 6)) + (ml & 63) * GS; };
+  auto arow_ptr = [&](int r) -> uint16_t* {
+    return reinterpret_cast<uint16_t*>(buf(r / AR) + GBYTES) + (r % AR) * AS;
+  };
 #pragma unroll
   for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ml = wm * 128 + (wk * 4 + j) * 16 + l16;
       const int rk = c * 16 + g4 * 4;
-      *reinterpret_cast<f32x4*>(sG + ml * GS + rk) = pacc[c][j];
+      *reinterpret_cast<f32x4*>(grow(ml) + rk) = pacc[c][j];
       if (tk == 0 && m0 + ml < M && rk < R)
         *reinterpret_cast<f32x4*>(G + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
     }
   for (int c = tid; c < RP * 32; c += kThreads) {
     const int rank = c >> 5, kc = c & 31;
     const u32x4 v = (rank < R && k0 + kc * 8 < K) ? ld16(A + (size_t)rank * K + k0 + kc * 8) : zero4();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sAT[(kc * 8 + 2 * e) * AS + rank] = (uint16_t)(v[e] & 0xffffu);
-      sAT[(kc * 8 + 2 * e + 1) * AS + rank] = (uint16_t)(v[e] >> 16);
-    }
+    st16(arow_ptr(rank) + kc * 8, v);
   }
   __syncthreads();
 
 #pragma unroll
   for (int c = 0; c < RP / 16; ++c) {
     const int rk = c * 16 + (g4 & 1) * 8;
+    // A^T operand: lane (l16, g4) gets A[rk .. rk+7][k] for column k = l16 of its block
+    const int arow = c * 16 + (g4 & 1) * 8 + (l16 >> 2);
+    const uint16_t* a0 = arow_ptr(arow) + (l16 & 3) * 4;
+    const uint16_t* a1 = arow_ptr(arow + 4) + (l16 & 3) * 4;
     u32x4 fat[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) fat[i] = ld16(sAT + (wk * 128 + i * 16 + l16) * AS + rk);
+    for (int i = 0; i < 8; ++i) fat[i] = join(ld_tr(a0 + wk * 128 + i * 16), ld_tr(a1 + wk * 128 + i * 16));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float* src = sG + (wm * 128 + j * 16 + l16) * GS + rk;
+      const float* src = grow(wm * 128 + j * 16 + l16) + rk;
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
       const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -224,7 +285,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
         fg[e] = (g4 < 2) ? pack_bf16(h0, h1) : pack_bf16(lo0, lo1);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][j] = mfma16(fat[i], fg, acc[i][j]);
+      for (int i = 0; i < 8; ++i) acc[i * 8 + j] = mfma16(fat[i], fg, acc[i * 8 + j]);
     }
   }
 
@@ -236,7 +297,8 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     for (int j = 0; j < 8; ++j) {
       const int m = m0 + wm * 128 + j * 16 + l16;
       if (m < M && k < K) {
-        const u32x2 o = {pack_bf16(acc[i][j][0], acc[i][j][1]), pack_bf16(acc[i][j][2], acc[i][j][3])};
+        const f32x4 v = acc[i * 8 + j];
+        const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
         *reinterpret_cast<u32x2*>(dX + (size_t)m * K + k) = o;
       }
     }
