@@ -60,8 +60,8 @@ def event_time_ms(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
-def cpu_baseline(inp, sample_rows):
-    """The float64 oracle, as it stands, on the first `sample_rows` tokens of the workload."""
+def cpu_baseline(inp, min_seconds):
+    """The float64 oracle, as it stands, on the whole workload, repeated for >= min_seconds."""
     import oracle
 
     try:
@@ -70,16 +70,18 @@ def cpu_baseline(inp, sample_rows):
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    x = oracle.bf16_bits_to_f64(inp.X[:sample_rows])
-    dy = oracle.bf16_bits_to_f64(inp.dY[:sample_rows])
-    w, a, b = (oracle.bf16_bits_to_f64(getattr(inp, n)) for n in ("W", "A", "B"))
-    t0 = time.perf_counter()
-    Y, XA = oracle.lora_forward(x, w, a, b, inp.scale)
-    oracle.lora_backward(dy, x, w, a, b, inp.scale, XA=XA)
-    dt = time.perf_counter() - t0
-    fl = lora_flops(sample_rows, inp.N, inp.K, inp.R)
+    x, dy, w, a, b = (oracle.bf16_bits_to_f64(getattr(inp, n)) for n in ("X", "dY", "W", "A", "B"))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        Y, XA = oracle.lora_forward(x, w, a, b, inp.scale)
+        oracle.lora_backward(dy, x, w, a, b, inp.scale, XA=XA)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 200:
+            break
+    fl = lora_flops(inp.M, inp.N, inp.K, inp.R) * reps
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 fwd+bwd on the first {sample_rows} of {inp.M} tokens "
+            "sample": f"float64 fwd+bwd of the whole workload ({inp.M} tokens), {reps} repetitions "
                       f"({fl:.3e} FLOP in {dt:.2f} s)"}
 
 
@@ -154,7 +156,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the QLoRA and decode lines")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle baseline (whole workload, repeated)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -236,8 +241,14 @@ def main(argv=None):
     if not args.no_secondary:
         result["secondary"] = {"qlora": bench_qlora_ffn(lora, torch, dev, 5),
                                "decode": bench_decode(lora, torch, dev, 20)}
+    if args.calib_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_rows, M))
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

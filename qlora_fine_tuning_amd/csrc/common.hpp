@@ -68,15 +68,15 @@ __device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
 
 // LDS operand tiles are rows of 64 bf16 (eight 16-byte chunks).  Chunk c of row r sits at
 // chunk slot c ^ swz(r).
-//  * swz: 8 consecutive rows read at one chunk column, and 8 rows spaced 8 apart written at
-//    one chunk column (the in-register transposes), both land in 8 distinct slots.
-//  * swzf ("fixed"): 16 consecutive rows read at one chunk column hit 16 distinct
-//    (row parity, slot) pairs, i.e. distinct banks over 256 bytes, and the slot depends only
-//    on bits 0..3 of the row, so fragment rows 16 apart differ by a constant address and
-//    every fragment read of a wave shares one address register.
+//  * swzf ("fixed"): slot c ^ (r & 7).  A fragment read (16 consecutive rows at one chunk
+//    column, the four 16-lane groups at four columns) measures free of bank conflicts on
+//    gfx950, and the slot depends only on the row's low 3 bits, so fragment rows 16 apart
+//    differ by a constant address and all fragment reads of a wave share one register.
+//  * swz: slot c ^ ((r ^ (r >> 3)) & 7), for tiles written through registers where 8 rows
+//    spaced 8 apart are stored at one chunk column (the in-register transposes).
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return (r << 6) + ((c ^ swz(r)) << 3); }
-__device__ __forceinline__ int swzf(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swzf(int r) { return r & 7; }
 __device__ __forceinline__ int lds_offf(int r, int c) { return (r << 6) + ((c ^ swzf(r)) << 3); }
 
 // ---- buffer loads ----------------------------------------------------------------------
