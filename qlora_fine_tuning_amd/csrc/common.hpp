@@ -171,6 +171,37 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Store a wave's 128 x 128 block of an MFMA result as bf16 through a private 32 KB LDS
+// buffer.  acc[i * 8 + j] holds output rows j*16 + (lane & 15) and columns i*16 + 4*(lane >> 4)
+// .. +3 (the transposed-operand layout of the kernels).  Staging rows are 256 bytes with the
+// 16-byte slot of chunk c at c ^ (row & 15), so both the 8-byte writes and the 16-byte
+// reads are free of bank conflicts; each store instruction then writes four whole 256-byte
+// row segments.  Rows >= rows_valid and columns >= cols_valid (a multiple of 8) are dropped.
+__device__ __forceinline__ void store_block_bf16(const f32x4* acc, uint16_t* stage, uint16_t* out,
+                                                 size_t ld, int rows_valid, int cols_valid,
+                                                 int lane) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = 2 * i + (g4 >> 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = j * 16 + l16;
+      const f32x4 v = acc[i * 8 + j];
+      const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(stage + row * 128 + ((c ^ l16) << 3) + (g4 & 1) * 4) = o;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes have landed
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int p = 0; p < 32; ++p) {
+    const int row = p * 4 + (lane >> 4), c = lane & 15;
+    const u32x4 v = ld16(stage + row * 128 + ((c ^ (row & 15)) << 3));
+    if (row < rows_valid && c * 8 < cols_valid) st16(out + (size_t)row * ld + c * 8, v);
+  }
+}
+
 // Workgroup id -> logical tile id such that each of the 8 XCDs (which receive workgroups
 // round-robin by id) owns one contiguous range of logical tiles; a bijection for any total.
 __device__ __forceinline__ int xcd_remap(int bid, int total) {

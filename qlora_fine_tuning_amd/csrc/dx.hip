@@ -209,20 +209,21 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   read_frags(f0, sD0, sW0, sB0, 0);
   prefetch(1, sD1, sW1, sB1);
 
-  for (int st = 0; st < nsteps; ++st) {
-    const bool odd = st & 1;
-    uint16_t* const dc = odd ? sD1 : sD0;
-    uint16_t* const wc = odd ? sW1 : sW0;
-    uint16_t* const bc = odd ? sB1 : sB0;
-    uint16_t* const dn = odd ? sD0 : sD1;
-    uint16_t* const wn = odd ? sW0 : sW1;
-    uint16_t* const bn = odd ? sB0 : sB1;
+  // one N step on fixed buffers (c = this step's, o = the other; see the forward kernel)
+  auto step = [&](int st, uint16_t* dc, uint16_t* wc, uint16_t* bc, uint16_t* dn, uint16_t* wn,
+                  uint16_t* bn) {
     phase(f0, f1, dc, wc, bc, 1);
     finish(wn, bn);  // the register-staged parts of step st+1
     wait_all();
     prefetch(st + 2, dc, wc, bc);
     phase(f1, f0, dn, wn, bn, 0);
+  };
+  int st = 0;
+  for (; st + 2 <= nsteps; st += 2) {
+    step(st, sD0, sW0, sB0, sD1, sW1, sB1);
+    step(st + 1, sD1, sW1, sB1, sD0, sW0, sB0);
   }
+  if (st < nsteps) step(st, sD0, sW0, sB0, sD1, sW1, sB1);
   wait_vmem();
   __syncthreads();
   mfma_drain(acc);
@@ -289,20 +290,11 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     }
   }
 
-  // ---- store dX (one rounding): lane holds dX[m][k .. k+3] ----
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = k0 + wk * 128 + i * 16 + g4 * 4;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + wm * 128 + j * 16 + l16;
-      if (m < M && k < K) {
-        const f32x4 v = acc[i * 8 + j];
-        const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(dX + (size_t)m * K + k) = o;
-      }
-    }
-  }
+  // ---- store dX (one rounding), staged through this wave's freed tile buffer ----
+  __syncthreads();  // every wave is done with G and A in LDS
+  uint16_t* const stage = wave == 0 ? sD0 : (wave == 1 ? sD1 : (wave == 2 ? sW0 : sW1));
+  const int mw = m0 + wm * 128, kw = k0 + wk * 128;
+  store_block_bf16(acc, stage, dX + (size_t)mw * K + kw, (size_t)K, M - mw, K - kw, lane);
 }
 
 template <int RP, bool INT4>

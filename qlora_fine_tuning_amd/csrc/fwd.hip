@@ -190,20 +190,22 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   read_frags(f0, sX0, sW0, sA0, 0);
   prefetch(1, sX1, sW1, sA1);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool odd = kt & 1;
-    uint16_t* const xc = odd ? sX1 : sX0;
-    uint16_t* const wc = odd ? sW1 : sW0;
-    uint16_t* const ac = odd ? sA1 : sA0;
-    uint16_t* const xo = odd ? sX0 : sX1;
-    uint16_t* const wo = odd ? sW0 : sW1;
-    uint16_t* const ao = odd ? sA0 : sA1;
+  // One K step on fixed buffers (c = this step's, o = the other): the buffer identities are
+  // compile-time, so the compiler can see that the copies into c never alias the reads of o.
+  auto step = [&](int kt, uint16_t* xc, uint16_t* wc, uint16_t* ac, uint16_t* xo, uint16_t* wo,
+                  uint16_t* ao) {
     phase(f0, f1, xc, wc, ac, 1);
     if constexpr (INT4) store_w4(wo);  // the unpacked W of step kt+1
     wait_all();
     prefetch(kt + 2, xc, wc, ac);
     phase(f1, f0, xo, wo, ao, 0);
+  };
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    step(kt, sX0, sW0, sA0, sX1, sW1, sA1);
+    step(kt + 1, sX1, sW1, sA1, sX0, sW0, sA0);
   }
+  if (kt < nk) step(kt, sX0, sW0, sA0, sX1, sW1, sA1);
   wait_vmem();
   __syncthreads();
   mfma_drain(acc);
@@ -256,20 +258,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     }
   }
 
-  // ---- store Y (bf16, one rounding): lane holds Y[m][n .. n+3] ----
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int n = n0 + wn * 128 + i * 16 + g4 * 4;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + wm * 128 + j * 16 + l16;
-      if (m < M && n < N) {
-        const f32x4 v = acc[i * 8 + j];
-        const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(Y + (size_t)m * N + n) = o;
-      }
-    }
-  }
+  // ---- store Y (bf16, one rounding), staged through this wave's freed tile buffer ----
+  __syncthreads();  // every wave is done with the panel rows in LDS
+  uint16_t* const stage = wave == 0 ? sX0 : (wave == 1 ? sX1 : (wave == 2 ? sW0 : sW1));
+  const int mw = m0 + wm * 128, nw = n0 + wn * 128;
+  store_block_bf16(acc, stage, Y + (size_t)mw * N + nw, (size_t)N, M - mw, N - nw, lane);
 }
 
 template <int RP, bool INT4>
