@@ -28,7 +28,7 @@
  *  - Shapes: X M x K, W N x K (out x in), A R x K, B N x R, Y and dY M x N, dX M x K,
  *    XA and G M x R, dA R x K, dB N x R.  All tensors are dense row-major with no strides.
  *  - Sizes: M >= 0 (M == 0 is a valid empty batch); N and K positive multiples of 64;
- *    R a multiple of 8 in [8, 64]; every tensor below 2^31 elements.
+ *    N and K at most 2^20; R a multiple of 8 in [8, 64]; every tensor below 2^31 elements.
  *  - Pointers are device pointers owned by the caller, 16-byte aligned, and outputs must
  *    not alias inputs.  The library allocates and frees nothing and keeps no state
  *    between calls; scratch memory comes from the caller's workspace.
@@ -92,6 +92,21 @@ lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
                      const float* XA, void* dX, float* dA, float* dB,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* The backward in two halves (lora_bwd = lora_bwd_dx then lora_bwd_dadb on the same workspace):
+ * the input gradient, which the previous layer waits for, and the adapter gradients, which can
+ * be deferred (e.g. overlapped with the previous layer's input gradient).
+ *   lora_bwd_dx:   dX = dY W + scale (dY B) A; also writes G = dY B (fp32 M x R) into `ws`.
+ *   lora_bwd_dadb: dA = scale G^T X, dB = scale dY^T XA, reading G from `ws` as left there by
+ *                  lora_bwd_dx (or qlora_bwd_dx) with the same sizes.
+ * Same argument meanings and workspace size as lora_bwd.  lora_bwd_dadb takes dt = LORA_BF16 for
+ * the QLoRA path (its activations are bf16). */
+lora_status lora_bwd_dx(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                        const void* dY, const void* W, const void* A, const void* B, void* dX,
+                        void* ws, size_t ws_bytes, void* stream);
+lora_status lora_bwd_dadb(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                          const void* dY, const void* X, const float* XA, float* dA, float* dB,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* int4 quantise + pack of an fp32 weight ("探微索隐 ...", §二.3 names the 4-bit store and its
  * scaling coefficient; the exact format is given at the top of this header).
  *   W  [N][K] fp32                        (input)
@@ -129,6 +144,11 @@ lora_status qlora_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
                       const void* A, const void* B, const float* XA,
                       void* dX, float* dA, float* dB,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* qlora_bwd's input-gradient half (W := W~ unpacked in registers); pair with lora_bwd_dadb. */
+lora_status qlora_bwd_dx(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                         const void* dY, const uint8_t* Wq, const void* Ws, const void* A,
+                         const void* B, void* dX, void* ws, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* lora_status_str(lora_status s);

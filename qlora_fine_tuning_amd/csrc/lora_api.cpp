@@ -14,12 +14,14 @@ using namespace lora;
 thread_local const char* g_last_hip_error = "hipSuccess";
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
+// Longest row (N or K): the kernels address a 256-row tile with 32-bit byte offsets.
+constexpr int64_t kMaxRow = (int64_t)1 << 20;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 lora_status check_dims(int64_t M, int64_t N, int64_t K, int32_t R) {
   if (M < 0 || N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0) return LORA_ERR_SHAPE;
-  if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems) return LORA_ERR_SHAPE;
+  if (M >= kMaxElems || N > kMaxRow || K > kMaxRow) return LORA_ERR_SHAPE;
   if (M * K >= kMaxElems || M * N >= kMaxElems || N * K >= kMaxElems) return LORA_ERR_SHAPE;
   if (R < 8 || R > 64 || R % 8 != 0) return LORA_ERR_RANK;
   return LORA_OK;
@@ -62,23 +64,33 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R) {
 
 bool use_gemv(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K % 256 == 0; }
 
-lora_status bwd_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R,
-                       float scale, const void* dY, const void* X, const void* W, const void* Ws,
-                       const void* A, const void* B, const float* XA, void* dX, float* dA,
-                       float* dB, void* ws, size_t ws_bytes, void* stream) {
+// The two halves of the backward; sizes and pointers validated by the callers.
+lora_status bwd_dx_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R,
+                          float scale, const void* dY, const void* W, const void* Ws, const void* A,
+                          const void* B, void* dX, void* ws, size_t ws_bytes, void* stream) {
+  const BwdLayout lay = bwd_layout(M, N, K, R);
+  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  if (M == 0) return LORA_OK;
+  float* G = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.g);
+  DxArgs a{dY, W, Ws, A, B, dX, G, M, N, K, R, scale};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip((dt == LORA_F32) ? launch_dx_f32(a, s) : launch_dx_mfma(a, int4, s));
+}
+
+lora_status bwd_dadb_common(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                            const void* dY, const void* X, const float* XA, float* dA, float* dB,
+                            void* ws, size_t ws_bytes, void* stream) {
   const BwdLayout lay = bwd_layout(M, N, K, R);
   if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return LORA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  float* G = reinterpret_cast<float*>(base + lay.g);
-  DadbArgs d{X, dY, G, XA, reinterpret_cast<float*>(base + lay.pa), reinterpret_cast<float*>(base + lay.pb),
+  DadbArgs d{X, dY, reinterpret_cast<const float*>(base + lay.g), XA,
+             reinterpret_cast<float*>(base + lay.pa), reinterpret_cast<float*>(base + lay.pb),
              dA, dB, M, N, K, R, scale, (int)splits_for(M)};
   if (M > 0) {
-    DxArgs a{dY, W, Ws, A, B, dX, G, M, N, K, R, scale};
-    hipError_t e = (dt == LORA_F32) ? launch_dx_f32(a, s) : launch_dx_mfma(a, int4, s);
-    if (e != hipSuccess) return from_hip(e);
-    e = (dt == LORA_F32) ? launch_dadb_partials_f32(d, s) : launch_dadb_partials_bf16(d, s);
+    const hipError_t e = (dt == LORA_F32) ? launch_dadb_partials_f32(d, s) : launch_dadb_partials_bf16(d, s);
     if (e != hipSuccess) return from_hip(e);
   }
   return from_hip(launch_dadb_reduce(d, s));
@@ -141,8 +153,35 @@ lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
   st = check_ptrs(W, A, B, dA, dB);
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, X, XA, dX)) != LORA_OK) return st;
-  return bwd_common(false, dt, M, N, K, R, scale, dY, X, W, nullptr, A, B, XA, dX, dA, dB, ws,
-                    ws_bytes, stream);
+  st = bwd_dx_common(false, dt, M, N, K, R, scale, dY, W, nullptr, A, B, dX, ws, ws_bytes, stream);
+  if (st != LORA_OK) return st;
+  return bwd_dadb_common(dt, M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
+}
+
+lora_status lora_bwd_dx(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                        const void* dY, const void* W, const void* A, const void* B, void* dX,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (dt != LORA_F32 && dt != LORA_BF16) return LORA_ERR_DTYPE;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(W, A, B);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(dY, dX)) != LORA_OK) return st;
+  return bwd_dx_common(false, dt, M, N, K, R, scale, dY, W, nullptr, A, B, dX, ws, ws_bytes, stream);
+}
+
+lora_status lora_bwd_dadb(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                          const void* dY, const void* X, const float* XA, float* dA, float* dB,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (dt != LORA_F32 && dt != LORA_BF16) return LORA_ERR_DTYPE;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(dA, dB);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(dY, X, XA)) != LORA_OK) return st;
+  return bwd_dadb_common(dt, M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
 }
 
 lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W, uint8_t* Wq,
@@ -211,8 +250,22 @@ lora_status qlora_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
   st = check_ptrs(Wq, Ws, A, B, dA, dB);
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, X, XA, dX)) != LORA_OK) return st;
-  return bwd_common(true, LORA_BF16, M, N, K, R, scale, dY, X, Wq, Ws, A, B, XA, dX, dA, dB, ws,
-                    ws_bytes, stream);
+  st = bwd_dx_common(true, LORA_BF16, M, N, K, R, scale, dY, Wq, Ws, A, B, dX, ws, ws_bytes, stream);
+  if (st != LORA_OK) return st;
+  return bwd_dadb_common(LORA_BF16, M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
+}
+
+lora_status qlora_bwd_dx(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                         const void* dY, const uint8_t* Wq, const void* Ws, const void* A,
+                         const void* B, void* dX, void* ws, size_t ws_bytes, void* stream) {
+  if (group != 64) return LORA_ERR_GROUP;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(Wq, Ws, A, B);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(dY, dX)) != LORA_OK) return st;
+  return bwd_dx_common(true, LORA_BF16, M, N, K, R, scale, dY, Wq, Ws, A, B, dX, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -29,6 +29,9 @@ SIGNATURES = {
     "lora_fwd": (_i32, [_i32, _i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p]),
     "lora_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i32]),
     "lora_bwd": (_i32, [_i32, _i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "lora_bwd_dx": (_i32, [_i32, _i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "lora_bwd_dadb": (_i32, [_i32, _i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "qlora_bwd_dx": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "qlora_quantize": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p]),
     "qlora_dequant": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p]),
     "qlora_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
@@ -145,6 +148,58 @@ def lora_bwd(dY, X, W, A, B, XA, scale: float, *, dX=None, dA=None, dB=None, ws=
                       _stream(stream))
     _check("lora_bwd", st)
     return dX, dA, dB
+
+
+def _ws_for(lib, dt, M, N, K, R, ws, dev):
+    need = lib.lora_bwd_workspace_bytes(dt, M, N, K, R)
+    if ws is None:
+        ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    return ws, ws.numel() * ws.element_size()
+
+
+def lora_bwd_dx(dY, W, A, B, scale: float, *, ws, dX=None, stream=None):
+    """Input-gradient half of lora_bwd: dX, and G = dY B left in `ws` for lora_bwd_dadb."""
+    lib = load()
+    dt = _dtype_code(dY)
+    M, N = dY.shape
+    K, R = W.shape[1], A.shape[0]
+    if dX is None:
+        dX = torch.empty((M, K), dtype=dY.dtype, device=dY.device)
+    ws, wsb = _ws_for(lib, dt, M, N, K, R, ws, dY.device)
+    st = lib.lora_bwd_dx(dt, M, N, K, R, float(scale), _ptr(dY), _ptr(W), _ptr(A), _ptr(B), _ptr(dX),
+                         _ptr(ws), wsb, _stream(stream))
+    _check("lora_bwd_dx", st)
+    return dX
+
+
+def lora_bwd_dadb(dY, X, XA, scale: float, R: int, *, ws, dA=None, dB=None, stream=None):
+    """Adapter-gradient half of lora_bwd, reading G from `ws` (left by lora_bwd_dx / qlora_bwd_dx)."""
+    lib = load()
+    dt = _dtype_code(X)
+    M, K = X.shape
+    N = dY.shape[1]
+    if dA is None:
+        dA = torch.empty((R, K), dtype=torch.float32, device=X.device)
+    if dB is None:
+        dB = torch.empty((N, R), dtype=torch.float32, device=X.device)
+    ws, wsb = _ws_for(lib, dt, M, N, K, R, ws, X.device)
+    st = lib.lora_bwd_dadb(dt, M, N, K, R, float(scale), _ptr(dY), _ptr(X), _ptr(XA), _ptr(dA), _ptr(dB),
+                           _ptr(ws), wsb, _stream(stream))
+    _check("lora_bwd_dadb", st)
+    return dA, dB
+
+
+def qlora_bwd_dx(dY, Wq, Ws, A, B, scale: float, *, ws, dX=None, stream=None):
+    lib = load()
+    M, N = dY.shape
+    K, R = Wq.shape[1] * 2, A.shape[0]
+    if dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dY.device)
+    ws, wsb = _ws_for(lib, LORA_BF16, M, N, K, R, ws, dY.device)
+    st = lib.qlora_bwd_dx(M, N, K, R, float(scale), GROUP, _ptr(dY), _ptr(Wq), _ptr(Ws), _ptr(A), _ptr(B),
+                          _ptr(dX), _ptr(ws), wsb, _stream(stream))
+    _check("qlora_bwd_dx", st)
+    return dX
 
 
 def qlora_quantize(W32, *, stream=None):

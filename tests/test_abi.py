@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lora_fwd", "lora_bwd", "lora_bwd_workspace_bytes", "qlora_fwd", "qlora_bwd",
               "qlora_quantize", "qlora_dequant", "qlora_fwd_workspace_bytes",
-              "qlora_bwd_workspace_bytes", "lora_status_str", "lora_last_hip_error"):
+              "qlora_bwd_workspace_bytes", "lora_status_str", "lora_last_hip_error",
+              "lora_bwd_dx", "lora_bwd_dadb", "qlora_bwd_dx"):
         assert n in names
 
 
@@ -106,6 +107,16 @@ def test_workspace_sizes(lib):
     # the decode path keeps split partial sums; the large-M path needs none
     assert lib.qlora_fwd_workspace_bytes(4, 27648, 5120, 16) > 0
     assert lib.qlora_fwd_workspace_bytes(4096, 27648, 5120, 16) == 0
+
+
+def test_split_backward_validation(lib):
+    need = lib.lora_bwd_workspace_bytes(1, 64, 256, 256, 16)
+    assert lib.lora_bwd_dx(1, 64, 256, 256, 16, 2.0, P, P, P, P, NUL, P, need, None) == 1
+    assert lib.lora_bwd_dx(1, 64, 256, 256, 16, 2.0, P, P, P, P, P, P, 8, None) == 6
+    assert lib.lora_bwd_dadb(1, 64, 256, 256, 16, 2.0, P, P, NUL, P, P, P, need, None) == 1
+    assert lib.lora_bwd_dadb(1, 64, 256, 200, 16, 2.0, P, P, P, P, P, P, need, None) == 2
+    assert lib.qlora_bwd_dx(64, 256, 256, 16, 2.0, 64, P, P, P, P, P, P, NUL, 0, None) == 6
+    assert lib.qlora_bwd_dx(64, 256, 256, 16, 2.0, 32, P, P, P, P, P, P, P, need, None) == 7
 
 
 def test_qlora_validation(lib):
