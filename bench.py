@@ -8,8 +8,10 @@ M = 8192 tokens (4 x 2048), K = N = 4096, r = 16, alpha = 32, bf16 with fp32 acc
 synthetic seeded inputs already resident in HBM.
 
 Prints one JSON line.  `value` is algorithmic TFLOP/s (4MNK + 6Mr(K+N) per step) over the
-timed steps.  `roofline` reports the dominant kernel (the fused forward, one launch per
-lora_fwd call) timed live with HIP events on its stream.  `cpu_baseline` times the float64
+timed steps.  `roofline` reports the dominant kernel, the fused input gradient (the only
+kernel of a lora_bwd_dx call), timed live with HIP events on its stream; its `traffic` is the
+per-launch HBM byte count recorded under profiles/ from rocprofv3 counters, or null when the
+kernel's sources have changed since the counters were taken.  `cpu_baseline` times the float64
 oracle on a bounded sample of the same workload.  `secondary` holds the QLoRA fwd+bwd rate
 on the int4 FFN projection and the decode matrix-vector bandwidth.
 """
@@ -38,6 +40,38 @@ def lora_flops(M, N, K, R):
 
 def fwd_flops(M, N, K, R):
     return 2.0 * M * N * K + 2.0 * M * R * (K + N)
+
+
+def dx_flops(M, N, K, R):
+    # dY W (2MNK) + the rank-R panel G = dY B (2MNR) + its epilogue G A (2MRK)
+    return 2.0 * M * N * K + 2.0 * M * R * (K + N)
+
+
+DX_SOURCES = ("qlora_fine_tuning_amd/csrc/dx.hip", "qlora_fine_tuning_amd/csrc/common.hpp")
+TRAFFIC_PROFILE = "profiles/lora_fwd_bwd_attn_proj_hbm_traffic.md"
+
+
+def source_sha(files):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel, files):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    sha = source_sha(files)
+    for line in open(path):
+        f = line.split()
+        if len(f) == 4 and f[0] == "roofline_traffic" and f[1] == kernel and f[3] == f"source_sha={sha}":
+            return float(f[2].split("=")[1])
+    return None
 
 
 def dev_bits(a, dev):
@@ -218,13 +252,20 @@ def main(argv=None):
     fl = lora_flops(M, N, K, R)
     value = fl / ms / 1e9
 
-    # dominant kernel: the fused forward (one kernel per lora_fwd call), timed live
-    fwd_ms = event_time_ms(fwd, max(args.steps, 10), stream)
-    bwd_ms = event_time_ms(bwd, max(args.steps, 10), stream)
-    ach = fwd_flops(M, N, K, R) / fwd_ms / 1e9
+    # dominant kernel: the fused input gradient (the one kernel of lora_bwd_dx), timed live
+    def bwd_dx():
+        lora.lora_bwd_dx(dY, W, A, B, inp.scale, ws=ws, dX=dX, stream=stream)
+
+    reps = max(args.steps, 10)
+    dx_ms = event_time_ms(bwd_dx, reps, stream)
+    fwd_ms = event_time_ms(fwd, reps, stream)
+    bwd_ms = event_time_ms(bwd, reps, stream)
+    ach = dx_flops(M, N, K, R) / dx_ms / 1e9
+    kernel = "dx_mfma_kernel<16,false>"
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "fwd_mfma_kernel<16,false>", "kernel_ms": round(fwd_ms, 4),
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(kernel, DX_SOURCES),
+                "traffic_unit": "HBM bytes per launch", "kernel": kernel, "kernel_ms": round(dx_ms, 4),
+                "fwd_ms": round(fwd_ms, 4), "fwd_frac": round(fwd_flops(M, N, K, R) / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
                 "bwd_ms": round(bwd_ms, 4)}
 
     result = {

@@ -141,6 +141,38 @@ def test_backward_is_bitwise_deterministic(gpu_lib):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_backward_matches_fused_call(gpu_lib, dtype):
+    # lora_bwd_dx followed by lora_bwd_dadb on one workspace is lora_bwd, bit for bit
+    _say(f"case split backward {dtype}")
+    lora = gpu_lib
+    inp = make_inputs(700, 512, 384, 16, seed=17, dtype=dtype)
+    X, W, A, B, dY = (to_dev(inp, n) for n in ("X", "W", "A", "B", "dY"))
+    _, XA = lora.lora_fwd(X, W, A, B, inp.scale)
+    dX, dA, dB = lora.lora_bwd(dY, X, W, A, B, XA, inp.scale)
+    ws = torch.full((lora.lora_bwd_workspace_bytes(lora._dtype_code(X), 700, 512, 384, 16),), 0xFF,
+                    dtype=torch.uint8, device=X.device)
+    dX2 = lora.lora_bwd_dx(dY, W, A, B, inp.scale, ws=ws)
+    dA2, dB2 = lora.lora_bwd_dadb(dY, X, XA, inp.scale, 16, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2) and torch.equal(dA, dA2) and torch.equal(dB, dB2)
+
+
+def test_split_qlora_backward_matches_fused_call(gpu_lib):
+    _say("case split qlora backward")
+    lora = gpu_lib
+    inp = make_inputs(300, 576, 512, 16, seed=19, dtype="bf16", int4=True)
+    Wq, Ws = lora.qlora_quantize(torch.from_numpy(inp.W).cuda())
+    X, A, B, dY = (to_dev(inp, n) for n in ("X", "A", "B", "dY"))
+    _, XA = lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale)
+    dX, dA, dB = lora.qlora_bwd(dY, X, Wq, Ws, A, B, XA, inp.scale)
+    ws = torch.empty(lora.qlora_bwd_workspace_bytes(300, 576, 512, 16), dtype=torch.uint8, device=X.device)
+    dX2 = lora.qlora_bwd_dx(dY, Wq, Ws, A, B, inp.scale, ws=ws)
+    dA2, dB2 = lora.lora_bwd_dadb(dY, X, XA, inp.scale, 16, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2) and torch.equal(dA, dA2) and torch.equal(dB, dB2)
+
+
 # ---------------------------------------------------------------------------
 # full workload shapes, sampled rows
 # ---------------------------------------------------------------------------
