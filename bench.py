@@ -163,7 +163,7 @@ def bench_decode(lora, torch, dev, reps, copies=6):
         for M in (1, 4, 8):
             X = Xall[:M].contiguous()
             Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(lora.qlora_fwd_workspace_bytes(M, N, K, R), 256), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(lora.qlora_fwd_workspace_bytes(M, N, K, R), 256), dtype=torch.uint8, device=dev)
             state = {"i": 0}
 
             def call():

@@ -39,8 +39,8 @@
  *    and leaves every output untouched.  A failed launch returns LORA_ERR_HIP.
  *  - `scale` is alpha / r, computed by the caller.
  *  - Outputs are overwritten, never accumulated into.
- *  - Results are deterministic: reductions run in a fixed order, without atomics, so
- *    two identical calls give bitwise identical outputs.
+ *  - Results are deterministic: every reduction adds its terms in a fixed order (no
+ *    floating-point atomics), so two identical calls give bitwise identical outputs.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H
@@ -119,13 +119,17 @@ lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W,
 lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq, const void* Ws,
                           void* W_bf16, void* stream);
 
-/* Bytes of device workspace qlora_fwd needs (the small-M path keeps partial sums of
- * X A^T there; 0 when none is needed). */
+/* Bytes of device workspace qlora_fwd needs: 0 for M > 8; for the M <= 8 (decode) path, per-
+ * tile arrival counters followed by per-split partial sums.  The counters must be zero before
+ * the first call that uses the workspace (e.g. hipMemset once after allocating it); every
+ * call leaves them zero again, so a workspace can be reused by later calls without clearing.
+ * Two calls that overlap in time must not share a workspace. */
 size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
 
 /* QLoRA forward: Y = X W~^T + scale (X A^T) B^T with W~ unpacked in registers.  For M <= 8
- * it runs as an HBM-bandwidth-bound matrix-vector kernel (per generated token every weight
- * byte is streamed once: "探微索隐 ...", §一, the memory wall of decoding).
+ * it runs as one HBM-bandwidth-bound matrix-vector kernel (per generated token every weight
+ * byte is streamed once: "探微索隐 ...", §一, the memory wall of decoding); its K splits are
+ * added in a fixed order, so results do not depend on timing.
  *   X [M][K], A [R][K], B [N][R] bf16; Wq [N][K/2]; Ws [N][K/64] fp16   (inputs)
  *   Y [M][N] bf16; XA [M][R] fp32 or NULL                               (outputs)
  *   ws: at least qlora_fwd_workspace_bytes() bytes (may be NULL when that is 0). */

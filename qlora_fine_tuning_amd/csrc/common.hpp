@@ -153,6 +153,33 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, const I4Scale& sc) {
   return o;
 }
 
+// The same 8 values with one mixed-precision fma each.  Code u (offset binary, 0..15) is put
+// in an fp16 mantissa next to the exponent of 1024, giving the exact fp16 value 1024 + u (or
+// 1024 + 16 u for a code in bits 4..7), and v_fma_mix_f32 widens it and computes
+//   (1024 + u) s - 1032 s = (u - 8) s   or   (1024 + 16 u) (s / 16) - 72 s = (u - 8) s
+// exactly (all products and addends fit fp32 exactly), so the result equals dequant8().
+struct I4Mix {
+  float s, s16, c0, c1;  // s, s / 16, -1032 s, -72 s
+};
+__device__ __forceinline__ I4Mix i4mix(float s) { return {s, s * 0.0625f, -1032.f * s, -72.f * s}; }
+__device__ __forceinline__ float f16lo(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xffffu)); }
+__device__ __forceinline__ float f16hi(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16)); }
+__device__ __forceinline__ u32x4 dequant8_mix(uint32_t w, const I4Mix& m) {
+  // (v & mask) ^ c with c = 0x6400 in each half plus the code's top bit: the fp16 bits and
+  // the XOR with 8 in one three-input bit operation
+  const uint32_t y = w >> 8;
+  const uint32_t p0 = (w & 0x000f000fu) ^ 0x64086408u;  // codes 0 (low half) and 4 (high half)
+  const uint32_t p1 = (w & 0x00f000f0u) ^ 0x64806480u;  // codes 1 and 5, times 16
+  const uint32_t p2 = (y & 0x000f000fu) ^ 0x64086408u;  // codes 2 and 6
+  const uint32_t p3 = (y & 0x00f000f0u) ^ 0x64806480u;  // codes 3 and 7, times 16
+  u32x4 o;
+  o[0] = pack_bf16(fmaf(f16lo(p0), m.s, m.c0), fmaf(f16lo(p1), m.s16, m.c1));
+  o[1] = pack_bf16(fmaf(f16lo(p2), m.s, m.c0), fmaf(f16lo(p3), m.s16, m.c1));
+  o[2] = pack_bf16(fmaf(f16hi(p0), m.s, m.c0), fmaf(f16hi(p1), m.s16, m.c1));
+  o[3] = pack_bf16(fmaf(f16hi(p2), m.s, m.c0), fmaf(f16hi(p3), m.s16, m.c1));
+  return o;
+}
+
 // Offset-binary form of a packed dword for single-code access with dq1().
 struct I4Word {
   uint32_t lo, hi;

@@ -65,8 +65,9 @@ hipError_t launch_quantize_int4(int64_t N, int64_t K, const float* W, uint8_t* W
                                 hipStream_t s);
 hipError_t launch_dequant_int4(int64_t N, int64_t K, const uint8_t* Wq, const uint16_t* Ws,
                                uint16_t* Wout, hipStream_t s);
-// decode path: `part` holds gemv_workspace_floats() floats of split partial sums
-hipError_t launch_gemv_int4(const FwdArgs& a, float* part, hipStream_t s);
-size_t gemv_workspace_floats(int64_t N, int64_t K, int R);
+// decode path (M <= 8): `ws` holds gemv_workspace_bytes() bytes whose leading per-tile
+// arrival counters are zero before the call and are left zero by it
+hipError_t launch_gemv_int4(const FwdArgs& a, void* ws, hipStream_t s);
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int R);
 
 }  // namespace lora

@@ -62,7 +62,7 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R) {
   return l;
 }
 
-bool use_gemv(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K % 256 == 0; }
+bool use_gemv(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K % 1024 == 0; }
 
 // The two halves of the backward; sizes and pointers validated by the callers.
 lora_status bwd_dx_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R,
@@ -209,7 +209,7 @@ lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq
 size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
   if (check_dims(M, N, K, R) != LORA_OK) return 0;
   if (!use_gemv(M, K)) return 0;
-  return align256(gemv_workspace_floats(N, K, R) * sizeof(float));
+  return gemv_workspace_bytes(M, N, K, R);
 }
 
 lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
@@ -230,7 +230,7 @@ lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
   if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
   FwdArgs a{X, Wq, Ws, A, B, Y, XA, M, N, K, R, scale};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (use_gemv(M, K)) return from_hip(launch_gemv_int4(a, static_cast<float*>(ws), s));
+  if (use_gemv(M, K)) return from_hip(launch_gemv_int4(a, ws, s));
   return from_hip(launch_fwd_mfma(a, true, s));
 }
 

@@ -241,7 +241,8 @@ def qlora_fwd(X, Wq, Ws, A, B, scale: float, *, Y=None, XA=None, save_xa: bool =
         XA = torch.empty((M, R), dtype=torch.float32, device=dev)
     need = lib.qlora_fwd_workspace_bytes(M, N, K, R)
     if ws is None and need:
-        ws = torch.empty(int(need), dtype=torch.uint8, device=dev)
+        # the decode path's arrival counters must start at zero (each call leaves them zero)
+        ws = torch.zeros(int(need), dtype=torch.uint8, device=dev)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib.qlora_fwd(M, N, K, R, float(scale), GROUP, _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A), _ptr(B),
                        _ptr(Y), _ptr(XA), _ptr(ws), wsb, _stream(stream))

@@ -124,8 +124,9 @@ def test_qlora_validation(lib):
     assert lib.qlora_quantize(64, 100, 64, P, P, P, None) == 2
     assert lib.qlora_quantize(64, 128, 64, NUL, P, P, None) == 1
     assert lib.qlora_dequant(64, 128, 64, P, MIS, P, None) == 4
-    assert lib.qlora_fwd(4, 256, 256, 16, 2.0, 64, P, P, P, P, P, P, P, NUL, 0, None) == 6
-    assert lib.qlora_fwd(4, 256, 256, 16, 2.0, 63, P, P, P, P, P, P, P, P, 1 << 20, None) == 7
+    # M <= 8 with K % 1024 == 0 takes the decode path, which needs a workspace
+    assert lib.qlora_fwd(4, 256, 1024, 16, 2.0, 64, P, P, P, P, P, P, P, NUL, 0, None) == 6
+    assert lib.qlora_fwd(4, 256, 1024, 16, 2.0, 63, P, P, P, P, P, P, P, P, 1 << 20, None) == 7
     assert lib.qlora_bwd(64, 256, 256, 16, 2.0, 64, P, P, P, P, P, P, P, P, P, P, P, 0, None) == 6
 
 
