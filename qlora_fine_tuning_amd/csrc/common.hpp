@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lora {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,6 +51,11 @@ __device__ __forceinline__ void mfma_drain(f32x4 (&acc)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
 }
+
+// Tag for a K-loop phase that issues no copies.
+struct NoCopy {
+  __device__ void operator()(int) const {}
+};
 
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {

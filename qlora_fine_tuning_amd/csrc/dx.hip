@@ -151,8 +151,10 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const uint16_t* p = b + kk * 32 * RP + boff + c * 16;
     return join(ld_tr(p), ld_tr(p + 4 * RP));
   };
+  // copy(q), q = 0..15: part q of the next step's copies, issued after MFMAs 1 and 5 of row i
+  // (see the forward kernel)
   auto phase = [&](const Frag& cu, Frag& nx, const uint16_t* d, const uint16_t* w,
-                   const uint16_t* b, int kk) {
+                   const uint16_t* b, int kk, auto&& copy) {
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -160,7 +162,16 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       nx.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mfma16_acc(acc[i * 8 + j], cu.w[i], cu.d[j]);
+      for (int j = 0; j < 8; ++j) {
+        mfma16_acc(acc[i * 8 + j], cu.w[i], cu.d[j]);
+        if constexpr (!std::is_same_v<std::decay_t<decltype(copy)>, NoCopy>) {
+          if (j == 1 || j == 5) {
+            __builtin_amdgcn_sched_barrier(0);
+            copy(2 * i + (j == 5));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -196,6 +207,22 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     load_b(n0);
     (void)bn;
   };
+  // the same copies in 16 parts for phase(): dY rows 8q.. (q < 8), W rows (bf16) or the int4
+  // register loads, and the B rows with the last part
+  auto prefetch_part = [&](int q, int st, uint16_t* dn, uint16_t* wn) {
+    const int n0 = min(st, nsteps - 1) * kStep;
+    if (q < 8) {
+      dma16(rD, dn + (4 * q + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)q * 32u * rowD);
+    } else if constexpr (!INT4) {
+      const int i = q - 8;
+      dma16(rW, wn + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffW,
+            (uint32_t)n0 * rowW + (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
+    } else if (q == 8) {
+      load_w4(n0);
+    }
+    if (q == 15) load_b(n0);
+  };
+  const NoCopy nocopy;
   auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch
     if constexpr (INT4) store_w4(wn);
     store_b(bn);
@@ -212,11 +239,15 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   // one N step on fixed buffers (c = this step's, o = the other; see the forward kernel)
   auto step = [&](int st, uint16_t* dc, uint16_t* wc, uint16_t* bc, uint16_t* dn, uint16_t* wn,
                   uint16_t* bn) {
-    phase(f0, f1, dc, wc, bc, 1);
+    phase(f0, f1, dc, wc, bc, 1, nocopy);
     finish(wn, bn);  // the register-staged parts of step st+1
     wait_all();
-    prefetch(st + 2, dc, wc, bc);
-    phase(f1, f0, dn, wn, bn, 0);
+    if constexpr (INT4 || RP > 32) {  // (interleaved, these two forms crash the compiler)
+      prefetch(st + 2, dc, wc, bc);
+      phase(f1, f0, dn, wn, bn, 0, nocopy);
+    } else {
+      phase(f1, f0, dn, wn, bn, 0, [&](int q) { prefetch_part(q, st + 2, dc, wc); });
+    }
   };
   int st = 0;
   for (; st + 2 <= nsteps; st += 2) {

@@ -6,7 +6,8 @@
 // accumulates the base product and the low-rank product and stores Y once, so no
 // intermediate reaches HBM.  Here one workgroup owns a 256 x 256 tile of Y:
 //  * the K loop stages X, W and A tiles (64 wide) through two LDS buffers.  X, A and bf16 W
-//    go HBM -> LDS with buffer_load ... lds (no registers on the way), issued one step ahead;
+//    go HBM -> LDS with buffer_load ... lds (no registers on the way), issued one step ahead
+//    and spread between the MFMAs of the step's second half;
 //  * each wave accumulates a 128 x 128 block of Y^T on 16x16x32 bf16 MFMA (the W tile is
 //    the row operand, so each lane ends up holding 4 consecutive outputs of one Y row);
 //  * the same LDS X fragments feed the rank-R panel X A^T (each of the two waves that
@@ -130,8 +131,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   };
   // Reads the fragments of half step `kk` into `nx` while running the MFMAs of `cu`.  The
   // reads are spread between the MFMA rows so that LDS latency hides behind matrix work.
+  // copy(d), d = 0..15, issues part d of the next step's copies after MFMAs 1 and 5 of row i
+  // (d = 2 i, 2 i + 1): spread out, the copies never hold up the wave's MFMA issue the way a
+  // burst of 17 copies right after the barrier does.
   auto phase = [&](const Frag& cu, Frag& nx, const uint16_t* x, const uint16_t* w,
-                   const uint16_t* a, int kk) {
+                   const uint16_t* a, int kk, auto&& copy) {
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -139,7 +143,16 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       nx.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mfma16_acc(acc[i * 8 + j], cu.w[i], cu.x[j]);
+      for (int j = 0; j < 8; ++j) {
+        mfma16_acc(acc[i * 8 + j], cu.w[i], cu.x[j]);
+        if constexpr (!std::is_same_v<std::decay_t<decltype(copy)>, NoCopy>) {
+          if (j == 1 || j == 5) {
+            __builtin_amdgcn_sched_barrier(0);
+            copy(2 * i + (j == 5));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -176,6 +189,20 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     else load_w4(k1);
     dma_a(an, k1);
   };
+  // The same copies in 16 parts for phase(): X rows 8d.. (d < 8), W rows (bf16) or the int4
+  // register loads, and the adapter rows with the last part.
+  auto prefetch_part = [&](int d, int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an) {
+    const int k1 = min(kn, nk - 1) * kStep;
+    if (d < 8) {
+      dma16(rX, xn + (4 * d + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)d * 32u * rowb);
+    } else if constexpr (!INT4) {
+      dma16(rW, wnx + (4 * (d - 8) + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)(d - 8) * 32u * rowb);
+    } else if (d == 8) {
+      load_w4(k1);
+    }
+    if (d == 15) dma_a(an, k1);
+  };
+  const NoCopy nocopy;
 
   // Pipeline (buffers b = kt & 1): on entry to step kt the kk = 0 fragments of step kt are in
   // registers and the copies of step kt+1 are in flight into buffer 1-b.
@@ -194,11 +221,10 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   // compile-time, so the compiler can see that the copies into c never alias the reads of o.
   auto step = [&](int kt, uint16_t* xc, uint16_t* wc, uint16_t* ac, uint16_t* xo, uint16_t* wo,
                   uint16_t* ao) {
-    phase(f0, f1, xc, wc, ac, 1);
+    phase(f0, f1, xc, wc, ac, 1, nocopy);
     if constexpr (INT4) store_w4(wo);  // the unpacked W of step kt+1
     wait_all();
-    prefetch(kt + 2, xc, wc, ac);
-    phase(f1, f0, xo, wo, ao, 0);
+    phase(f1, f0, xo, wo, ao, 0, [&](int d) { prefetch_part(d, kt + 2, xc, wc, ac); });
   };
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
