@@ -119,7 +119,7 @@ lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W,
 lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq, const void* Ws,
                           void* W_bf16, void* stream);
 
-/* Bytes of device workspace qlora_fwd needs: 0 for M > 8; for the M <= 8 (decode) path, per-
+/* Bytes of device workspace qlora_fwd needs: 0 unless M <= 8 and K % 1024 == 0; for that (decode) path, per-
  * tile arrival counters followed by per-split partial sums.  The counters must be zero before
  * the first call that uses the workspace (e.g. hipMemset once after allocating it); every
  * call leaves them zero again, so a workspace can be reused by later calls without clearing.
@@ -127,7 +127,7 @@ lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq
 size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
 
 /* QLoRA forward: Y = X W~^T + scale (X A^T) B^T with W~ unpacked in registers.  For M <= 8
- * it runs as one HBM-bandwidth-bound matrix-vector kernel (per generated token every weight
+ * and K a multiple of 1024 it runs as one HBM-bandwidth-bound matrix-vector kernel (per generated token every weight
  * byte is streamed once: "探微索隐 ...", §一, the memory wall of decoding); its K splits are
  * added in a fixed order, so results do not depend on timing.
  *   X [M][K], A [R][K], B [N][R] bf16; Wq [N][K/2]; Ws [N][K/64] fp16   (inputs)
