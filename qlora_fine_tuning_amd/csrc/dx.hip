@@ -207,10 +207,12 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     load_b(n0);
     (void)bn;
   };
-  // the same copies in 16 parts for phase(): dY rows 8q.. (q < 8), W rows (bf16) or the int4
-  // register loads, and the B rows with the last part
+  // the same copies in 16 parts for phase(): the B rows first (a register load, waited for
+  // at the next barrier, so it gets the longest time), then dY rows 8q.. (q < 8), W rows (bf16)
+  // or the int4 register loads
   auto prefetch_part = [&](int q, int st, uint16_t* dn, uint16_t* wn) {
     const int n0 = min(st, nsteps - 1) * kStep;
+    if (q == 0) load_b(n0);
     if (q < 8) {
       dma16(rD, dn + (4 * q + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)q * 32u * rowD);
     } else if constexpr (!INT4) {
@@ -220,7 +222,6 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     } else if (q == 8) {
       load_w4(n0);
     }
-    if (q == 15) load_b(n0);
   };
   const NoCopy nocopy;
   auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch
@@ -255,6 +256,17 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     step(st + 1, sD1, sW1, sB1, sD0, sW0, sB0);
   }
   if (st < nsteps) step(st, sD0, sW0, sB0, sD1, sW1, sB1);
+  // the A tile of the low-rank epilogue, loaded now so its latency overlaps the panel work
+  // (ranks up to 32; the rank-64 instances load it later, prefetching there crashes the compiler)
+  constexpr int AQ = RP <= 32 ? (RP * 32 + kThreads - 1) / kThreads : 1;
+  u32x4 av[AQ];
+  if constexpr (RP <= 32) {
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int c = q * kThreads + tid, rank = c >> 5, kc = c & 31;
+      av[q] = (c < RP * 32 && rank < R && k0 + kc * 8 < K) ? ld16(A + (size_t)rank * K + k0 + kc * 8) : zero4();
+    }
+  }
   wait_vmem();
   __syncthreads();
   mfma_drain(acc);
@@ -285,10 +297,18 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       if (tk == 0 && m0 + ml < M && rk < R)
         *reinterpret_cast<f32x4*>(G + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
     }
-  for (int c = tid; c < RP * 32; c += kThreads) {
-    const int rank = c >> 5, kc = c & 31;
-    const u32x4 v = (rank < R && k0 + kc * 8 < K) ? ld16(A + (size_t)rank * K + k0 + kc * 8) : zero4();
-    st16(arow_ptr(rank) + kc * 8, v);
+  if constexpr (RP <= 32) {
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int c = q * kThreads + tid, rank = c >> 5, kc = c & 31;
+      if (c < RP * 32) st16(arow_ptr(rank) + kc * 8, av[q]);
+    }
+  } else {
+    for (int c = tid; c < RP * 32; c += kThreads) {
+      const int rank = c >> 5, kc = c & 31;
+      const u32x4 v = (rank < R && k0 + kc * 8 < K) ? ld16(A + (size_t)rank * K + k0 + kc * 8) : zero4();
+      st16(arow_ptr(rank) + kc * 8, v);
+    }
   }
   __syncthreads();
 

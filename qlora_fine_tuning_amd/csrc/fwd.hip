@@ -189,10 +189,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     else load_w4(k1);
     dma_a(an, k1);
   };
-  // The same copies in 16 parts for phase(): X rows 8d.. (d < 8), W rows (bf16) or the int4
-  // register loads, and the adapter rows with the last part.
+  // The same copies in 16 parts for phase(): the adapter rows first, then X rows 8d.. (d < 8),
+  // W rows (bf16) or the int4 register loads.
   auto prefetch_part = [&](int d, int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an) {
     const int k1 = min(kn, nk - 1) * kStep;
+    if (d == 0) dma_a(an, k1);
     if (d < 8) {
       dma16(rX, xn + (4 * d + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)d * 32u * rowb);
     } else if constexpr (!INT4) {
@@ -200,7 +201,6 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     } else if (d == 8) {
       load_w4(k1);
     }
-    if (d == 15) dma_a(an, k1);
   };
   const NoCopy nocopy;
 
@@ -232,6 +232,23 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     step(kt + 1, sX1, sW1, sA1, sX0, sW0, sA0);
   }
   if (kt < nk) step(kt, sX0, sW0, sA0, sX1, sW1, sA1);
+  // B fragments of the low-rank epilogue, loaded now so their latency overlaps the panel work
+  // (ranks up to 32; the rank-64 instances load them later, prefetching there crashes the
+  // compiler)
+  constexpr int BPRE = RP <= 32 ? RP / 16 : 1;
+  u32x4 fbm[BPRE][8];
+  auto load_bfrag = [&](u32x4 (&f)[8], int c) {
+    const int rk = c * 16 + (g4 & 1) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + wn * 128 + i * 16 + l16;
+      f[i] = (n < N && rk < R) ? ld16(Bm + (size_t)n * R + rk) : zero4();
+    }
+  };
+  if constexpr (RP <= 32) {
+#pragma unroll
+    for (int c = 0; c < RP / 16; ++c) load_bfrag(fbm[c], c);
+  }
   wait_vmem();
   __syncthreads();
   mfma_drain(acc);
@@ -258,12 +275,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
 #pragma unroll
   for (int c = 0; c < RP / 16; ++c) {
     const int rk = c * 16 + (g4 & 1) * 8;
-    u32x4 fbm[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + i * 16 + l16;
-      fbm[i] = (n < N && rk < R) ? ld16(Bm + (size_t)n * R + rk) : zero4();
-    }
+    if constexpr (RP > 32) load_bfrag(fbm[0], c);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ml = wm * 128 + j * 16 + l16;
@@ -280,7 +292,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
         fx[e] = (g4 < 2) ? pack_bf16(h0, h1) : pack_bf16(lo0, lo1);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i * 8 + j] = mfma16(fbm[i], fx, acc[i * 8 + j]);
+      for (int i = 0; i < 8; ++i) acc[i * 8 + j] = mfma16(fbm[RP <= 32 ? c : 0][i], fx, acc[i * 8 + j]);
     }
   }
 
