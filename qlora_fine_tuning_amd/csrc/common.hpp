@@ -137,19 +137,23 @@ __device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
 
 // ---- int4 unpack ------------------------------------------------------------------------
 // A packed dword holds 8 codes, code i (k offset i) in bits 4i .. 4i+3 as 4-bit two's
-// complement.  XOR with 0x8 per nibble turns code q into the unsigned u = q + 8, so
-//   q * s = fma(u, s, -8 s)
-// exactly (the exact product has at most 14 significant bits).  The even codes sit in the
-// low nibble of each byte, the odd codes (times 16) in the high nibble, so each value costs
-// one byte-to-float conversion and one fma, and every two values one bf16 pack.
+// complement.  XOR with 0x8 per nibble turns code q into the unsigned u = q + 8.  Code u is
+// placed in an fp16 mantissa next to the exponent of 1024, giving the exact fp16 value
+// 1024 + u (or 1024 + 16 u for a code in bits 4..7 of its byte), and one v_fma_mix_f32 widens
+// it and computes
+//   (1024 + u) s - 1032 s = (u - 8) s   or   (1024 + 16 u) (s / 16) - 72 s = (u - 8) s,
+// exact: every product and addend fits fp32 exactly (s has at most 11 significant bits), so
+// the fma returns q s itself, and one RNE pack per pair gives bf16_rne(q s): dequant8_mix.
+// 17 VALU operations per 8 codes; dequant8 below (an fma on byte-to-float conversions) takes 23
+// and gives the same bits.
+// The same values through byte-to-float conversions: q * s = fma(u, s, -8 s), exact (the
+// product has at most 14 significant bits).  The even codes sit in the low nibble of each
+// byte, the odd codes (times 16) in the high nibble.  Used by the input-gradient kernel.
 struct I4Scale {
   float s, s_16, m8s;  // s, s / 16, -8 s  (all exact)
 };
 __device__ __forceinline__ I4Scale i4scale(float s) { return {s, s * 0.0625f, -8.f * s}; }
-
 __device__ __forceinline__ float ubyte(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xffu); }
-
-// The 8 codes of one packed dword -> 8 bf16 values bf16_rne(q * s), in k order, as 4 pairs.
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, const I4Scale& sc) {
   const uint32_t x = w ^ 0x88888888u;
   const uint32_t lo = x & 0x0f0f0f0fu, hi = x & 0xf0f0f0f0u;
@@ -160,17 +164,13 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, const I4Scale& sc) {
   return o;
 }
 
-// The same 8 values with one mixed-precision fma each.  Code u (offset binary, 0..15) is put
-// in an fp16 mantissa next to the exponent of 1024, giving the exact fp16 value 1024 + u (or
-// 1024 + 16 u for a code in bits 4..7), and v_fma_mix_f32 widens it and computes
-//   (1024 + u) s - 1032 s = (u - 8) s   or   (1024 + 16 u) (s / 16) - 72 s = (u - 8) s
-// exactly (all products and addends fit fp32 exactly), so the result equals dequant8().
 struct I4Mix {
   float s, s16, c0, c1;  // s, s / 16, -1032 s, -72 s
 };
 __device__ __forceinline__ I4Mix i4mix(float s) { return {s, s * 0.0625f, -1032.f * s, -72.f * s}; }
 __device__ __forceinline__ float f16lo(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xffffu)); }
 __device__ __forceinline__ float f16hi(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16)); }
+// The 8 codes of one packed dword -> 8 bf16 values bf16_rne(q * s), in k order, as 4 pairs.
 __device__ __forceinline__ u32x4 dequant8_mix(uint32_t w, const I4Mix& m) {
   // (v & mask) ^ c with c = 0x6400 in each half plus the code's top bit: the fp16 bits and
   // the XOR with 8 in one three-input bit operation
@@ -185,19 +185,6 @@ __device__ __forceinline__ u32x4 dequant8_mix(uint32_t w, const I4Mix& m) {
   o[2] = pack_bf16(fmaf(f16hi(p0), m.s, m.c0), fmaf(f16hi(p1), m.s16, m.c1));
   o[3] = pack_bf16(fmaf(f16hi(p2), m.s, m.c0), fmaf(f16hi(p3), m.s16, m.c1));
   return o;
-}
-
-// Offset-binary form of a packed dword for single-code access with dq1().
-struct I4Word {
-  uint32_t lo, hi;
-};
-__device__ __forceinline__ I4Word i4word(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  return {x & 0x0f0f0f0fu, x & 0xf0f0f0f0u};
-}
-// q * s of code e (0..7) of a word prepared by i4word() (exact fp32; e must be a constant).
-__device__ __forceinline__ float dq1(const I4Word& w, int e, const I4Scale& sc) {
-  return (e & 1) ? fmaf(ubyte(w.hi, e >> 1), sc.s_16, sc.m8s) : fmaf(ubyte(w.lo, e >> 1), sc.s, sc.m8s);
 }
 
 // fp16 bits -> fp32 (exact).

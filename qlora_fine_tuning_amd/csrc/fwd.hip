@@ -101,10 +101,10 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = q * 128 + (tid >> 1);
-      const I4Scale sc = i4scale(rs[q]);
+      const I4Mix sc = i4mix(rs[q]);
 #pragma unroll
       for (int d = 0; d < 4; ++d)  // packed dword d = codes k = 8d .. 8d+7 of this half
-        st16(w + lds_offf(r, (tid & 1) * 4 + d), dequant8(rq[q][d], sc));
+        st16(w + lds_offf(r, (tid & 1) * 4 + d), dequant8_mix(rq[q][d], sc));
     }
   };
 

@@ -66,10 +66,10 @@ dequant_int4_kernel(const uint8_t* __restrict__ Wq, const uint16_t* __restrict__
   const int cpr = K / 32;
   const int64_t row = c / cpr, kc = c - row * cpr;
   const u32x4 w = ld16(Wq + row * (K / 2) + kc * 16);
-  const I4Scale sc = i4scale(half_bits_to_f32(Ws[row * (K / 64) + kc / 2]));
+  const I4Mix sc = i4mix(half_bits_to_f32(Ws[row * (K / 64) + kc / 2]));
   uint16_t* dst = Wout + row * K + kc * 32;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) st16(dst + 8 * d, dequant8(w[d], sc));
+  for (int d = 0; d < 4; ++d) st16(dst + 8 * d, dequant8_mix(w[d], sc));
 }
 
 // ---- decode matrix-vector product, M <= 8 --------------------------------------------
