@@ -78,28 +78,36 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       dma16(rW, dst + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffW,
             (uint32_t)n0 * rowW + (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
   };
-  // W (int4): thread t unpacks row t >> 2, columns (t & 3) * 64 .. +63 (one scale group)
-  u32x4 rq[2];
-  float rsc = 0.f;
+  // W (int4): thread t unpacks row t >> 2, columns (t & 3) * 64 .. +63 (one scale group).
+  // A step's codes and raw fp16 scale stay in registers from their load to their unpacking
+  // into LDS: two sets alternating by step, loaded two steps ahead, at rank 16; one set loaded
+  // one step ahead for larger ranks (the two-set form of those instances crashes the compiler).
+  struct W4 {
+    u32x4 q[2];
+    uint32_t s;  // fp16 bits; converted when used, so the load is not waited for early
+  };
+  W4 w4a, w4b;
+  constexpr bool AHEAD = INT4 && RP == 16;
   rsrc_t rWq, rWs;
   if constexpr (INT4) {
     rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + k0 / 2, (uint32_t)((size_t)N * (K / 2) - k0 / 2));
     rWs = make_rsrc(Wscale + k0 / 64, (uint32_t)((size_t)N * (K / 64) - k0 / 64) * 2u);
   }
   const int qrow = tid >> 2, qblk = tid & 3;
-  auto load_w4 = [&](int n0) {
-    const uint32_t r = (uint32_t)(n0 + qrow);
+  auto load_w4 = [&](W4& v, int stn) {
+    const uint32_t r = (uint32_t)(min(stn, nsteps - 1) * kStep + qrow);
     const uint32_t vo = r * (uint32_t)(K / 2) + (uint32_t)qblk * 32u;
-    rq[0] = bload16(rWq, vo, 0);
-    rq[1] = bload16(rWq, vo + 16u, 0);
-    rsc = half_bits_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-        rWs, (int)((r * (uint32_t)(K / 64) + (uint32_t)qblk) * 2u), 0, 0));
+    v.q[0] = bload16(rWq, vo, 0);
+    v.q[1] = bload16(rWq, vo + 16u, 0);
+    v.s = __builtin_amdgcn_raw_buffer_load_b16(rWs, (int)((r * (uint32_t)(K / 64) + (uint32_t)qblk) * 2u), 0, 0);
   };
-  auto store_w4 = [&](uint16_t* w) {
-    const I4Scale sc = i4scale(rsc);
+  auto store_w4_part = [&](const W4& v, uint16_t* w, int d) {  // packed dword d of the 64 codes
     uint16_t* row = w + qblk * 4096 + qrow * 64;
+    st16(row + ((d ^ wsw(qrow)) << 3), dequant8(v.q[d >> 2][d & 3], i4scale(half_bits_to_f32((uint16_t)v.s))));
+  };
+  auto store_w4 = [&](const W4& v, uint16_t* w) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) st16(row + ((d ^ wsw(qrow)) << 3), dequant8(rq[d >> 2][d & 3], sc));
+    for (int d = 0; d < 8; ++d) store_w4_part(v, w, d);
   };
   // B: 64 rows x RP ranks, through registers (ranks >= R are zero); branch-free: chunks past
   // the tile read a valid row and land in the padding
@@ -195,15 +203,17 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
 #pragma unroll
     for (int c = 0; c < RP / 16; ++c) f.b[c] = bfrag(b, kk, c);
   };
+  // wait for the copies of the next step: for int4 W, the three register loads issued after
+  // them stay in flight
   auto wait_all = [&]() {
-    wait_vmem();
+    if constexpr (INT4) __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
+    else wait_vmem();
     __syncthreads();
   };
   auto prefetch = [&](int st, uint16_t* dn, uint16_t* wn, uint16_t* bn) {
     const int n0 = min(st, nsteps - 1) * kStep;
     dma_d(dn, n0);
     if constexpr (!INT4) dma_w(wn, n0);
-    else load_w4(n0);
     load_b(n0);
     (void)bn;
   };
@@ -219,43 +229,58 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       const int i = q - 8;
       dma16(rW, wn + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffW,
             (uint32_t)n0 * rowW + (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
-    } else if (q == 8) {
-      load_w4(n0);
     }
   };
   const NoCopy nocopy;
-  auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch
-    if constexpr (INT4) store_w4(wn);
+  auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch (bf16)
+    (void)wn;
     store_b(bn);
   };
+  auto finish_b = [&](uint16_t* bn) { store_b(bn); };
 
   // Same pipeline as the forward kernel (see there), over N steps of 64.
   Frag f0, f1;
   prefetch(0, sD0, sW0, sB0);
+  if constexpr (INT4) {
+    load_w4(w4a, 0);
+    if constexpr (AHEAD) load_w4(w4b, 1);
+    store_w4(w4a, sW0);
+  }
   finish(sW0, sB0);
-  wait_all();
+  wait_vmem();
+  __syncthreads();
   read_frags(f0, sD0, sW0, sB0, 0);
   prefetch(1, sD1, sW1, sB1);
+  if constexpr (INT4) load_w4(w4a, AHEAD ? 2 : 1);
 
   // one N step on fixed buffers (c = this step's, o = the other; see the forward kernel)
-  auto step = [&](int st, uint16_t* dc, uint16_t* wc, uint16_t* bc, uint16_t* dn, uint16_t* wn,
-                  uint16_t* bn) {
-    phase(f0, f1, dc, wc, bc, 1, nocopy);
-    finish(wn, bn);  // the register-staged parts of step st+1
+  // w4n: the register set holding step st+1's int4 W (stored during the first half) and then
+  // receiving the next load (issued after the copies of step st+2)
+  auto step = [&](int st, W4& w4n, uint16_t* dc, uint16_t* wc, uint16_t* bc, uint16_t* dn,
+                  uint16_t* wn, uint16_t* bn) {
+    if constexpr (INT4) {  // the unpacked W of step st+1, spread between the MFMAs
+      phase(f0, f1, dc, wc, bc, 1, [&](int d) { if (d % 2 == 0) store_w4_part(w4n, wn, d / 2); });
+      finish_b(bn);
+    } else {
+      phase(f0, f1, dc, wc, bc, 1, nocopy);
+      finish(wn, bn);  // the register-staged parts of step st+1
+    }
     wait_all();
     if constexpr (INT4 || RP > 32) {  // (interleaved, these two forms crash the compiler)
       prefetch(st + 2, dc, wc, bc);
+      if constexpr (INT4) load_w4(w4n, st + (AHEAD ? 3 : 2));  // after every copy
       phase(f1, f0, dn, wn, bn, 0, nocopy);
     } else {
       phase(f1, f0, dn, wn, bn, 0, [&](int q) { prefetch_part(q, st + 2, dc, wc); });
     }
   };
   int st = 0;
+  W4& w4odd = AHEAD ? w4b : w4a;  // the set of odd steps
   for (; st + 2 <= nsteps; st += 2) {
-    step(st, sD0, sW0, sB0, sD1, sW1, sB1);
-    step(st + 1, sD1, sW1, sB1, sD0, sW0, sB0);
+    step(st, w4odd, sD0, sW0, sB0, sD1, sW1, sB1);
+    step(st + 1, w4a, sD1, sW1, sB1, sD0, sW0, sB0);
   }
-  if (st < nsteps) step(st, sD0, sW0, sB0, sD1, sW1, sB1);
+  if (st < nsteps) step(st, w4odd, sD0, sW0, sB0, sD1, sW1, sB1);
   // the A tile of the low-rank epilogue, loaded now so its latency overlaps the panel work
   // (ranks up to 32; the rank-64 instances load it later, prefetching there crashes the compiler)
   constexpr int AQ = RP <= 32 ? (RP * 32 + kThreads - 1) / kThreads : 1;

@@ -78,34 +78,42 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     }
   };
 
-  // int4 W: one row per thread pair, thread (tid & 1) takes 32 of the row's 64 codes
-  u32x4 rq[2];
-  float rs[2];
+  // int4 W: one row per thread pair, thread (tid & 1) takes 32 of the row's 64 codes.  The
+  // codes and raw fp16 scales of a step stay in registers (two sets, alternating by step) from
+  // their load, two steps ahead, to their unpacking into LDS.
+  struct W4 {
+    u32x4 q[2];
+    uint32_t s[2];  // fp16 bits; converted when used, so the load is not waited for early
+  };
+  W4 w4a, w4b;
+  // Two sets, loaded two steps ahead, at rank 16; larger ranks use one set loaded one step
+  // ahead (the two-set form of those instances crashes the compiler).
+  constexpr bool AHEAD = INT4 && RP == 16;
   rsrc_t rWq, rWs;
   if constexpr (INT4) {
     const int nrows = min(N - n0, kTile);
     rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + (size_t)n0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2));
     rWs = make_rsrc(Wscale + (size_t)n0 * (K / 64), (uint32_t)nrows * (uint32_t)(K / 64) * 2u);
   }
-  auto load_w4 = [&](int k0) {
+  auto load_w4 = [&](W4& v, int kn) {
+    const uint32_t k0 = (uint32_t)min(kn, nk - 1) * kStep;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const uint32_t r = (uint32_t)(q * 128 + (tid >> 1));
-      rq[q] = bload16(rWq, r * (uint32_t)(K / 2) + (uint32_t)(tid & 1) * 16u, (uint32_t)k0 / 2u);
-      const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b16(rWs, (int)(r * (uint32_t)(K / 64) * 2u),
-                                                               (int)((uint32_t)k0 / 32u), 0);
-      rs[q] = half_bits_to_f32((uint16_t)sb);
+      v.q[q] = bload16(rWq, r * (uint32_t)(K / 2) + (uint32_t)(tid & 1) * 16u, k0 / 2u);
+      v.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rWs, (int)(r * (uint32_t)(K / 64) * 2u), (int)(k0 / 32u), 0);
     }
   };
-  auto store_w4 = [&](uint16_t* w) {
+  // part p = 4 q + d: packed dword d (codes k = 8d .. 8d+7 of this half) of row q * 128 + ...
+  auto store_w4_part = [&](const W4& v, uint16_t* w, int p) {
+    const int q = p >> 2, d = p & 3;
+    const int r = q * 128 + (tid >> 1);
+    st16(w + lds_offf(r, (tid & 1) * 4 + d),
+         dequant8_mix(v.q[q][d], i4mix(half_bits_to_f32((uint16_t)v.s[q]))));
+  };
+  auto store_w4 = [&](const W4& v, uint16_t* w) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = q * 128 + (tid >> 1);
-      const I4Mix sc = i4mix(rs[q]);
-#pragma unroll
-      for (int d = 0; d < 4; ++d)  // packed dword d = codes k = 8d .. 8d+7 of this half
-        st16(w + lds_offf(r, (tid & 1) * 4 + d), dequant8_mix(rq[q][d], sc));
-    }
+    for (int p = 0; p < 8; ++p) store_w4_part(v, w, p);
   };
 
   f32x4 acc[64];  // acc[i * 8 + j]: Y^T rows (W) block i, columns (X) block j
@@ -176,8 +184,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
 #pragma unroll
     for (int c = 0; c < RP / 16; ++c) f.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
   };
+  // wait for the copies of the next step: for int4 W, the four register loads issued after
+  // them (two steps ahead) stay in flight
   auto wait_all = [&]() {
-    wait_vmem();
+    if constexpr (INT4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else wait_vmem();
     __syncthreads();
   };
   // Copies of step kn (clamped to the last step: a repeated copy of the last step into the
@@ -186,7 +197,6 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     const int k1 = min(kn, nk - 1) * kStep;
     dma_tile(rX, xn, k1);
     if constexpr (!INT4) dma_tile(rW, wnx, k1);
-    else load_w4(k1);
     dma_a(an, k1);
   };
   // The same copies in 16 parts for phase(): the adapter rows first, then X rows 8d.. (d < 8),
@@ -198,8 +208,6 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       dma16(rX, xn + (4 * d + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)d * 32u * rowb);
     } else if constexpr (!INT4) {
       dma16(rW, wnx + (4 * (d - 8) + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)(d - 8) * 32u * rowb);
-    } else if (d == 8) {
-      load_w4(k1);
     }
   };
   const NoCopy nocopy;
@@ -212,26 +220,40 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   //   read kk = 0 fragments of step kt+1  ||  MFMAs of kk = 1
   Frag f0, f1;
   prefetch(0, sX0, sW0, sA0);
-  if constexpr (INT4) store_w4(sW0);
-  wait_all();
+  if constexpr (INT4) {
+    load_w4(w4a, 0);
+    if constexpr (AHEAD) load_w4(w4b, 1);
+    store_w4(w4a, sW0);
+  }
+  wait_vmem();
+  __syncthreads();
   read_frags(f0, sX0, sW0, sA0, 0);
   prefetch(1, sX1, sW1, sA1);
+  if constexpr (INT4) load_w4(w4a, AHEAD ? 2 : 1);
 
   // One K step on fixed buffers (c = this step's, o = the other): the buffer identities are
   // compile-time, so the compiler can see that the copies into c never alias the reads of o.
-  auto step = [&](int kt, uint16_t* xc, uint16_t* wc, uint16_t* ac, uint16_t* xo, uint16_t* wo,
-                  uint16_t* ao) {
-    phase(f0, f1, xc, wc, ac, 1, nocopy);
-    if constexpr (INT4) store_w4(wo);  // the unpacked W of step kt+1
+  // w4n: the register set holding step kt+1's int4 W (stored during the first half) and then
+  // receiving step kt+3's (loaded during the second half)
+  auto step = [&](int kt, W4& w4n, uint16_t* xc, uint16_t* wc, uint16_t* ac, uint16_t* xo,
+                  uint16_t* wo, uint16_t* ao) {
+    if constexpr (INT4)  // the unpacked W of step kt+1, spread between the MFMAs
+      phase(f0, f1, xc, wc, ac, 1, [&](int d) { if (d % 2 == 0) store_w4_part(w4n, wo, d / 2); });
+    else
+      phase(f0, f1, xc, wc, ac, 1, nocopy);
     wait_all();
-    phase(f1, f0, xo, wo, ao, 0, [&](int d) { prefetch_part(d, kt + 2, xc, wc, ac); });
+    phase(f1, f0, xo, wo, ao, 0, [&](int d) {
+      prefetch_part(d, kt + 2, xc, wc, ac);
+      if constexpr (INT4) { if (d == 15) load_w4(w4n, kt + (AHEAD ? 3 : 2)); }  // after every copy
+    });
   };
   int kt = 0;
+  W4& w4odd = AHEAD ? w4b : w4a;  // the set of odd steps
   for (; kt + 2 <= nk; kt += 2) {
-    step(kt, sX0, sW0, sA0, sX1, sW1, sA1);
-    step(kt + 1, sX1, sW1, sA1, sX0, sW0, sA0);
+    step(kt, w4odd, sX0, sW0, sA0, sX1, sW1, sA1);
+    step(kt + 1, w4a, sX1, sW1, sA1, sX0, sW0, sA0);
   }
-  if (kt < nk) step(kt, sX0, sW0, sA0, sX1, sW1, sA1);
+  if (kt < nk) step(kt, w4odd, sX0, sW0, sA0, sX1, sW1, sA1);
   // B fragments of the low-rank epilogue, loaded now so their latency overlaps the panel work
   // (ranks up to 32; the rank-64 instances load them later, prefetching there crashes the
   // compiler)
