@@ -15,6 +15,11 @@
 //    G = dY B comes from the same LDS dY fragments, with B^T read the same transposing way;
 //  * the epilogue adds A^T (scale G)^T with a bf16 hi + lo split of scale * G, then rounds
 //    dX once.
+// When the output has too few tiles to fill the chip for a long N loop (the QLoRA FFN input
+// gradient: 320 tiles, 432 steps), N is cut into S equal ranges and the grid holds S units per
+// tile.  Every unit stores its fp32 partial of the tile (and of its G panel) and moves the
+// tile's arrival counter; the last unit to arrive adds the S partials in split order (its own
+// from registers) and runs the epilogue, so the sum does not depend on arrival order.
 // QLoRA: W arrives as packed int4 codes plus fp16 group scales ("探微索隐：Unsloth 如何加速
 // LLM 推理？（以 Qwen 27B 为例）", §二.3); threads unpack them in registers into the same
 // row-major LDS tile.
@@ -29,12 +34,24 @@ namespace lora {
 // so those reads hit distinct banks.
 __device__ __forceinline__ int wsw(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
 
+// Split partials cross XCDs, whose L2 caches are not coherent with each other: they are
+// written and read with device-scope (sc1) accesses, and every writer waits for its stores
+// before it moves the tile's counter.
+constexpr int kCpolSc1 = 16;  // cache-policy operand of the buffer intrinsics: sc1
+__device__ __forceinline__ void st_part(rsrc_t r, uint32_t voff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, kCpolSc1);
+}
+__device__ __forceinline__ f32x4 ld_part(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCpolSc1);
+}
+
 template <int RP, bool INT4>
 __global__ void __launch_bounds__(kThreads)
 dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
                const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
                const uint16_t* __restrict__ Bm, uint16_t* __restrict__ dX,
-               float* __restrict__ G, int M, int N, int K, int R, float scale) {
+               float* __restrict__ G, int M, int N, int K, int R, float scale, int splits,
+               float* __restrict__ part, uint32_t* __restrict__ ctr) {
   constexpr int TT = kTile * kStep;  // 16384 elements: dY tile 256 x 64, W tile 64 x 256
   constexpr int BT = kStep * RP;     // B tile: 64 rows (n) x RP ranks
   constexpr int BQ = (BT / 8 + kThreads - 1) / kThreads;  // 16-byte chunks per thread
@@ -48,10 +65,17 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_k = (K + kTile - 1) / kTile;
+  const int tiles = tiles_m * tiles_k;
+  // unit -> (split, tile), split-major: units running together share operand panels in L2
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int sp = unit / tiles, tile = unit - sp * tiles;
   int tm, tk;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_k, 8, tm, tk);
+  grouped_tile(tile, tiles_m, tiles_k, 8, tm, tk);
   const int m0 = tm * kTile, k0 = tk * kTile;
-  const int nsteps = N / kStep;
+  const int ntot = N / kStep;
+  const int sbeg = sp * ntot / splits;  // this unit's N steps: [sbeg, sbeg + nsteps)
+  const int nsteps = (sp + 1) * ntot / splits - sbeg;
+  const int nbase = sbeg * kStep;
   const uint32_t rowD = (uint32_t)N * 2, rowW = (uint32_t)K * 2;
 
   // ---- copies into LDS ----
@@ -95,7 +119,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   }
   const int qrow = tid >> 2, qblk = tid & 3;
   auto load_w4 = [&](W4& v, int stn) {
-    const uint32_t r = (uint32_t)(min(stn, nsteps - 1) * kStep + qrow);
+    const uint32_t r = (uint32_t)(nbase + min(stn, nsteps - 1) * kStep + qrow);
     const uint32_t vo = r * (uint32_t)(K / 2) + (uint32_t)qblk * 32u;
     v.q[0] = bload16(rWq, vo, 0);
     v.q[1] = bload16(rWq, vo + 16u, 0);
@@ -211,7 +235,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     __syncthreads();
   };
   auto prefetch = [&](int st, uint16_t* dn, uint16_t* wn, uint16_t* bn) {
-    const int n0 = min(st, nsteps - 1) * kStep;
+    const int n0 = nbase + min(st, nsteps - 1) * kStep;
     dma_d(dn, n0);
     if constexpr (!INT4) dma_w(wn, n0);
     load_b(n0);
@@ -221,7 +245,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   // at the next barrier, so it gets the longest time), then dY rows 8q.. (q < 8), W rows (bf16)
   // or the int4 register loads
   auto prefetch_part = [&](int q, int st, uint16_t* dn, uint16_t* wn) {
-    const int n0 = min(st, nsteps - 1) * kStep;
+    const int n0 = nbase + min(st, nsteps - 1) * kStep;
     if (q == 0) load_b(n0);
     if (q < 8) {
       dma16(rD, dn + (4 * q + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)q * 32u * rowD);
@@ -295,6 +319,63 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   wait_vmem();
   __syncthreads();
   mfma_drain(acc);
+
+  // ---- split N: store this unit's partial; the last unit of the tile adds them all ----
+  // (ranks up to 32: the rank-64 instances crash the compiler with this block and run unsplit)
+  if constexpr (RP <= 32) if (splits > 1) {
+    // partial slot: [wave][acc block][lane] f32x4, then the G panel [wave][block][lane]
+    constexpr uint32_t kAccBytes = 4 * 64 * 64 * 16, kPanBytes = 4 * (RP / 16) * 4 * 64 * 16;
+    constexpr uint32_t kSlot = kAccBytes + kPanBytes;
+    const rsrc_t rP = make_rsrc(part + (size_t)tile * splits * (kSlot / 4), (uint32_t)splits * kSlot);
+    const uint32_t wa = ((uint32_t)wave * 64 * 64 + lane) * 16u;
+    const uint32_t wp = kAccBytes + ((uint32_t)wave * (RP / 16) * 4 * 64 + lane) * 16u;
+    const uint32_t own = (uint32_t)sp * kSlot;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) st_part(rP, own + wa + i * 1024u, acc[i]);
+#pragma unroll
+    for (int c = 0; c < RP / 16; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st_part(rP, own + wp + (c * 4 + j) * 1024u, pacc[c][j]);
+    wait_vmem();
+    __shared__ int s_last;
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(splits - 1);
+    __syncthreads();
+    if (!s_last) return;
+    // fixed order: ((p0 + p1) + p2) + ..., p_sp from registers; 16 blocks of loads in flight
+#pragma unroll
+    for (int c0 = 0; c0 < 64; c0 += 16) {
+      f32x4 tot[16];
+      for (int q = 0; q < splits; ++q) {
+        f32x4 v[16];
+        if (q == sp) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = acc[c0 + i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = ld_part(rP, (uint32_t)q * kSlot + wa + (c0 + i) * 1024u);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tot[i] = q == 0 ? v[i] : tot[i] + v[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c0 + i] = tot[i];
+    }
+#pragma unroll
+    for (int c = 0; c < RP / 16; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 t = fzero4();
+        for (int q = 0; q < splits; ++q) {
+          const f32x4 v = q == sp ? pacc[c][j] : ld_part(rP, (uint32_t)q * kSlot + wp + (c * 4 + j) * 1024u);
+          t = q == 0 ? v : t + v;
+        }
+        pacc[c][j] = t;
+      }
+    if (tid == 0) __hip_atomic_store(ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // ---- epilogue: G panel -> LDS (and HBM once per row tile); A tile -> LDS ----
   // The four freed tile buffers each take 64 rows of G (fp32, stride GS) followed by RP/4
@@ -373,13 +454,48 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   store_block_bf16(acc, stage, dX + (size_t)mw * K + kw, (size_t)K, M - mw, K - kw, lane);
 }
 
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile)); }
+
+// Number of N ranges of the input-gradient grid: the count that minimises the estimated time
+// (rounds of 256 resident workgroups x steps per unit, a split costing about 4 steps for its
+// partial), with at least 8 steps per unit and at most 8 ranges; ranks above 32 are unsplit.
+int dx_splits(int64_t M, int64_t N, int64_t K, int R) {
+  const int64_t tiles = dx_tiles(M, K), steps = N / kStep;
+  int best = 1;
+  if (R > 32) return 1;
+  int64_t best_cost = ((tiles + 255) / 256) * steps;
+  for (int64_t s = 2; s <= 8 && steps / s >= 8; ++s) {
+    const int64_t cost = ((tiles * s + 255) / 256) * ((steps + s - 1) / s + 4);
+    if (cost < best_cost) best = (int)s, best_cost = cost;
+  }
+  return best;
+}
+
+size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R) {
+  const int s = dx_splits(M, N, K, R);
+  if (s == 1) return 0;
+  const int rp = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
+  return (size_t)dx_tiles(M, K) * s * (4 * 64 * 64 * 16 + 4 * (rp / 16) * 4 * 64 * 16);
+}
+
 template <int RP, bool INT4>
 static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
-  const int tiles = (int)(((a.M + kTile - 1) / kTile) * ((a.K + kTile - 1) / kTile));
-  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4>), dim3(tiles), dim3(kThreads), 0, s,
+  const int tiles = dx_tiles(a.M, a.K);
+  const int splits = dx_splits(a.M, a.N, a.K, a.R);
+  if (splits > 1) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s, a.ctr, tiles);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4>), dim3(tiles * splits), dim3(kThreads), 0, s,
                      (const uint16_t*)a.dY, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.dX, a.G, (int)a.M, (int)a.N, (int)a.K,
-                     (int)a.R, a.scale);
+                     (int)a.R, a.scale, splits, a.part, a.ctr);
   return hipGetLastError();
 }
 

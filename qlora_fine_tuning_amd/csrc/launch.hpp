@@ -33,6 +33,8 @@ struct DxArgs {
   int64_t M, N, K;
   int R;
   float scale;
+  uint32_t* ctr;   // split-N path (bf16 / int4): dx_tiles() arrival counters,
+  float* part;     // and dx_part_bytes() bytes of split partials
 };
 
 struct DadbArgs {
@@ -53,6 +55,10 @@ struct DadbArgs {
 // bf16 / int4 MFMA paths
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s);
+// input-gradient grid: output tiles, N ranges per tile, bytes of split partials (0 if unsplit)
+int dx_tiles(int64_t M, int64_t K);
+int dx_splits(int64_t M, int64_t N, int64_t K, int R);
+size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R);
 hipError_t launch_dadb_partials_bf16(const DadbArgs& a, hipStream_t s);
 // fp32 paths
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);

@@ -48,17 +48,26 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 int64_t splits_for(int64_t M) { return (M + kSplitRows - 1) / kSplitRows; }
 
-// Backward workspace: G [M][R] fp32 | partA [splits][R][K] fp32 | partB [splits][R][N] fp32.
+// Backward workspace: G [M][R] fp32 | partA [splits][R][K] fp32 | partB [splits][R][N] fp32,
+// then, for an MFMA (bf16 / int4) input gradient whose N is split, its per-tile arrival
+// counters and split partials.
 struct BwdLayout {
-  size_t g, pa, pb, total;
+  size_t g, pa, pb, ctr, dxp, total;
 };
-BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R) {
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R, bool mfma) {
   const int64_t s = splits_for(M);
   BwdLayout l;
   l.g = 0;
   l.pa = align256((size_t)M * R * sizeof(float));
   l.pb = l.pa + align256((size_t)s * R * K * sizeof(float));
-  l.total = l.pb + align256((size_t)s * R * N * sizeof(float));
+  l.ctr = l.pb + align256((size_t)s * R * N * sizeof(float));
+  l.dxp = l.ctr;
+  l.total = l.ctr;
+  const size_t part = mfma ? dx_part_bytes(M, N, K, R) : 0;
+  if (part > 0) {
+    l.dxp = l.ctr + align256((size_t)dx_tiles(M, K) * sizeof(uint32_t));
+    l.total = l.dxp + part;
+  }
   return l;
 }
 
@@ -68,12 +77,14 @@ bool use_gemv(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K % 1024 == 0; 
 lora_status bwd_dx_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R,
                           float scale, const void* dY, const void* W, const void* Ws, const void* A,
                           const void* B, void* dX, void* ws, size_t ws_bytes, void* stream) {
-  const BwdLayout lay = bwd_layout(M, N, K, R);
+  const BwdLayout lay = bwd_layout(M, N, K, R, dt != LORA_F32);
   if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return LORA_ERR_ALIGN;
   if (M == 0) return LORA_OK;
-  float* G = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.g);
-  DxArgs a{dY, W, Ws, A, B, dX, G, M, N, K, R, scale};
+  char* base = static_cast<char*>(ws);
+  float* G = reinterpret_cast<float*>(base + lay.g);
+  DxArgs a{dY, W, Ws, A, B, dX, G, M, N, K, R, scale, reinterpret_cast<uint32_t*>(base + lay.ctr),
+           reinterpret_cast<float*>(base + lay.dxp)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip((dt == LORA_F32) ? launch_dx_f32(a, s) : launch_dx_mfma(a, int4, s));
 }
@@ -81,7 +92,7 @@ lora_status bwd_dx_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_
 lora_status bwd_dadb_common(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                             const void* dY, const void* X, const float* XA, float* dA, float* dB,
                             void* ws, size_t ws_bytes, void* stream) {
-  const BwdLayout lay = bwd_layout(M, N, K, R);
+  const BwdLayout lay = bwd_layout(M, N, K, R, dt != LORA_F32);
   if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return LORA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -139,7 +150,7 @@ lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
 size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R) {
   if (dt != LORA_F32 && dt != LORA_BF16) return 0;
   if (check_dims(M, N, K, R) != LORA_OK) return 0;
-  return bwd_layout(M, N, K, R).total;
+  return bwd_layout(M, N, K, R, dt != LORA_F32).total;
 }
 
 lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
@@ -236,7 +247,7 @@ lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
 
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
   if (check_dims(M, N, K, R) != LORA_OK) return 0;
-  return bwd_layout(M, N, K, R).total;
+  return bwd_layout(M, N, K, R, true).total;
 }
 
 lora_status qlora_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,

@@ -75,6 +75,33 @@ def test_bf16_shapes(gpu_lib, M, N, K, R):
     check_full(gpu_lib, make_inputs(M, N, K, R, seed=200 + M + R, dtype="bf16"))
 
 
+def _unsplit_ws_bytes(M, N, K, R):
+    # G + the dA / dB split partials (256-token splits), each region padded to 256 bytes
+    pad = lambda b: (b + 255) // 256 * 256
+    s = (M + 255) // 256
+    return pad(4 * M * R) + pad(4 * s * R * K) + pad(4 * s * R * N)
+
+
+# Few output tiles and a long N loop: the input gradient cuts N into 8, 4 or 2 ranges whose
+# partials the last-arriving unit of each tile adds (the workspace grows by the partials).
+@pytest.mark.parametrize("M,N,K,R", [(256, 4096, 256, 16), (513, 2048, 576, 8), (300, 1024, 320, 32)])
+def test_bf16_split_n_shapes(gpu_lib, M, N, K, R):
+    _say(f"case bf16 split-N M={M} N={N} K={K} R={R}")
+    assert gpu_lib.lora_bwd_workspace_bytes(gpu_lib.LORA_BF16, M, N, K, R) > _unsplit_ws_bytes(M, N, K, R)
+    check_full(gpu_lib, make_inputs(M, N, K, R, seed=250 + M + R, dtype="bf16"))
+
+
+def test_split_n_backward_is_bitwise_deterministic(gpu_lib):
+    # the partials are added in split order whichever unit arrives last
+    _say("case split-N determinism")
+    inp = make_inputs(300, 1024, 320, 32, seed=23, dtype="bf16")
+    r1 = run_lora(gpu_lib, inp)
+    for _ in range(3):
+        r2 = run_lora(gpu_lib, inp)
+        for a, b in zip(r1, r2):
+            assert torch.equal(a, b)
+
+
 def test_bf16_std_reading_of_b(gpu_lib):
     _say("case bf16 b_dist=std")
     check_full(gpu_lib, make_inputs(520, 512, 512, 16, seed=7, dtype="bf16", b_dist="std"))
@@ -154,6 +181,24 @@ def test_split_backward_matches_fused_call(gpu_lib, dtype):
                     dtype=torch.uint8, device=X.device)
     dX2 = lora.lora_bwd_dx(dY, W, A, B, inp.scale, ws=ws)
     dA2, dB2 = lora.lora_bwd_dadb(dY, X, XA, inp.scale, 16, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2) and torch.equal(dA, dA2) and torch.equal(dB, dB2)
+
+
+def test_split_backward_matches_fused_call_split_n(gpu_lib):
+    # the same with the input gradient's N split (its counters and partials in the workspace,
+    # which starts out filled with garbage: the call clears its counters itself)
+    _say("case split backward, split-N")
+    lora = gpu_lib
+    M, N, K, R = 513, 2048, 576, 8
+    inp = make_inputs(M, N, K, R, seed=29, dtype="bf16")
+    X, W, A, B, dY = (to_dev(inp, n) for n in ("X", "W", "A", "B", "dY"))
+    _, XA = lora.lora_fwd(X, W, A, B, inp.scale)
+    dX, dA, dB = lora.lora_bwd(dY, X, W, A, B, XA, inp.scale)
+    ws = torch.full((lora.lora_bwd_workspace_bytes(lora.LORA_BF16, M, N, K, R),), 0xFF,
+                    dtype=torch.uint8, device=X.device)
+    dX2 = lora.lora_bwd_dx(dY, W, A, B, inp.scale, ws=ws)
+    dA2, dB2 = lora.lora_bwd_dadb(dY, X, XA, inp.scale, R, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(dX, dX2) and torch.equal(dA, dA2) and torch.equal(dB, dB2)
 
@@ -276,7 +321,8 @@ def check_qlora(lora, inp, sampled: bool):
 @pytest.mark.parametrize("M,N,K,R", [(300, 576, 512, 16), (257, 256, 1024, 8), (9, 320, 768, 32),
                                      (1, 256, 512, 16), (5, 384, 1280, 16), (8, 320, 256, 64),
                                      (1, 64, 1024, 16), (5, 384, 2048, 16), (8, 320, 1024, 64),
-                                     (3, 192, 3072, 24), (7, 448, 4096, 8), (2, 128, 8192, 40)])
+                                     (3, 192, 3072, 24), (7, 448, 4096, 8), (2, 128, 8192, 40),
+                                     (200, 2048, 512, 24), (9, 4096, 256, 16)])
 def test_qlora_small_shapes(gpu_lib, M, N, K, R):
     _say(f"case qlora M={M} N={N} K={K} R={R}")
     check_qlora(gpu_lib, make_inputs(M, N, K, R, seed=300 + M, dtype="bf16", int4=True), sampled=False)
