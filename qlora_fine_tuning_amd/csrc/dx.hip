@@ -127,7 +127,10 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   auto store_w4_part = [&](const W4& v, uint16_t* w, int d) {  // packed dword d of the 64 codes
     uint16_t* row = w + qblk * 4096 + qrow * 64;
-    st16(row + ((d ^ wsw(qrow)) << 3), dequant8(v.q[d >> 2][d & 3], i4scale(half_bits_to_f32((uint16_t)v.s))));
+    const float sc = half_bits_to_f32((uint16_t)v.s);
+    if constexpr (RP <= 32) st16(row + ((d ^ wsw(qrow)) << 3), dequant8_mix(v.q[d >> 2][d & 3], i4mix(sc)));
+    else st16(row + ((d ^ wsw(qrow)) << 3), dequant8(v.q[d >> 2][d & 3], i4scale(sc)));  // (the fma form
+    // crashes the compiler at rank 64; both give the same bits)
   };
   auto store_w4 = [&](const W4& v, uint16_t* w) {
 #pragma unroll
@@ -290,12 +293,16 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       finish(wn, bn);  // the register-staged parts of step st+1
     }
     wait_all();
-    if constexpr (INT4 || RP > 32) {  // (interleaved, these two forms crash the compiler)
+    if constexpr ((INT4 && RP > 16) || RP > 32) {  // (interleaved, these forms crash the compiler)
       prefetch(st + 2, dc, wc, bc);
       if constexpr (INT4) load_w4(w4n, st + (AHEAD ? 3 : 2));  // after every copy
       phase(f1, f0, dn, wn, bn, 0, nocopy);
     } else {
-      phase(f1, f0, dn, wn, bn, 0, [&](int q) { prefetch_part(q, st + 2, dc, wc); });
+      phase(f1, f0, dn, wn, bn, 0, [&](int q) {
+        prefetch_part(q, st + 2, dc, wc);
+        if constexpr (INT4)
+          if (q == 15) load_w4(w4n, st + 3);  // after every copy
+      });
     }
   };
   int st = 0;
