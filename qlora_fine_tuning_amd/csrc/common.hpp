@@ -102,6 +102,8 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, uint32
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
+// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt 63 and expcnt 7: not waited for)
+constexpr int kLgkm0 = 0xC07F;
 // s_waitcnt vmcnt(0): this wave's outstanding vector-memory loads (LDS DMA included) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

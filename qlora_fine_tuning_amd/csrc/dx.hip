@@ -52,6 +52,12 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
                const uint16_t* __restrict__ Bm, uint16_t* __restrict__ dX,
                float* __restrict__ G, int M, int N, int K, int R, float scale, int splits,
                float* __restrict__ part, uint32_t* __restrict__ ctr) {
+  // Ranks up to 32: the accumulators stay in AGPRs through inline-asm MFMAs (this file is
+  // built with the panel MFMAs in VGPR form).  Rank 64 runs out of registers, and the compiler
+  // then moves accumulators between registers, which must not happen to an asm MFMA's result
+  // still in flight: those instances use builtin MFMAs, built in their own translation unit
+  // (dx64.hip) with the compiler's default register forms.
+  constexpr bool ASM = RP <= 32;
   constexpr int TT = kTile * kStep;  // 16384 elements: dY tile 256 x 64, W tile 64 x 256
   constexpr int BT = kStep * RP;     // B tile: 64 rows (n) x RP ranks
   constexpr int BQ = (BT / 8 + kThreads - 1) / kThreads;  // 16-byte chunks per thread
@@ -138,14 +144,16 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   // B: 64 rows x RP ranks, through registers (ranks >= R are zero); branch-free: chunks past
   // the tile read a valid row and land in the padding
+  // (ranks >= R read past the end of the buffer, which returns zeros: no select after the
+  // load, so nothing waits for it before the LDS store)
   u32x4 rb[BQ];
+  const rsrc_t rB = make_rsrc(Bm, (uint32_t)N * (uint32_t)R * 2u);
   auto load_b = [&](int n0) {
 #pragma unroll
     for (int q = 0; q < BQ; ++q) {
       const int c = q * kThreads + tid, row = (c / (RP / 8)) & 63, rk = (c % (RP / 8)) * 8;
-      const bool in = rk < R;
-      const u32x4 v = ld16(Bm + (size_t)(n0 + row) * R + (in ? rk : 0));
-      rb[q] = in ? v : zero4();
+      const uint32_t vo = rk < R ? ((uint32_t)(n0 + row) * (uint32_t)R + (uint32_t)rk) * 2u : 0x80000000u;
+      rb[q] = bload16(rB, vo, 0);
     }
   };
   auto store_b = [&](uint16_t* b) {
@@ -161,7 +169,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
-  mfma_acc_ready(acc);
+  if constexpr (ASM) mfma_acc_ready(acc);
 
   // transposing-read addresses: lane (l16, g4) reads rows 4 (l16 >> 2) + .. of its 16-lane
   // group, columns 4 (l16 & 3) ..; per 16-column block q of a 64-column W block the chunk is
@@ -193,12 +201,22 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      // every row of the next phase uses all eight dY fragments: they go out in rows 0-3
+      // (ranks up to 32; this order crashes the compiler at rank 64)
+      if constexpr (RP <= 32) {
+        if (i < 4) {
+          nx.d[2 * i] = ld16(d + lds_offf(wm * 128 + 2 * i * 16 + l16, ch));
+          nx.d[2 * i + 1] = ld16(d + lds_offf(wm * 128 + (2 * i + 1) * 16 + l16, ch));
+        }
+      } else {
+        nx.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
+      }
       nx.w[i] = wfrag(w, kk, i);
-      nx.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        mfma16_acc(acc[i * 8 + j], cu.w[i], cu.d[j]);
+        if constexpr (ASM) mfma16_acc(acc[i * 8 + j], cu.w[i], cu.d[j]);
+        else acc[i * 8 + j] = mfma16(cu.w[i], cu.d[j], acc[i * 8 + j]);
         if constexpr (!std::is_same_v<std::decay_t<decltype(copy)>, NoCopy>) {
           if (j == 1 || j == 5) {
             __builtin_amdgcn_sched_barrier(0);
@@ -307,9 +325,14 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   int st = 0;
   W4& w4odd = AHEAD ? w4b : w4a;  // the set of odd steps
+  // LDS reads drained at the loop edge (after the panel MFMAs that follow the last of them):
+  // a known state at the loop head, where the compiler would otherwise wait for the reads it
+  // has just issued
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
   for (; st + 2 <= nsteps; st += 2) {
     step(st, w4odd, sD0, sW0, sB0, sD1, sW1, sB1);
     step(st + 1, w4a, sD1, sW1, sB1, sD0, sW0, sB0);
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
   }
   if (st < nsteps) step(st, w4odd, sD0, sW0, sB0, sD1, sW1, sB1);
   // the A tile of the low-rank epilogue, loaded now so its latency overlaps the panel work
@@ -325,7 +348,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   }
   wait_vmem();
   __syncthreads();
-  mfma_drain(acc);
+  if constexpr (ASM) mfma_drain(acc);
 
   // ---- split N: store this unit's partial; the last unit of the tile adds them all ----
   // (ranks up to 32: the rank-64 instances crash the compiler with this block and run unsplit)
@@ -461,11 +484,12 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   store_block_bf16(acc, stage, dX + (size_t)mw * K + kw, (size_t)K, M - mw, K - kw, lane);
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int n) {
+static __global__ void zero_u32_kernel(uint32_t* p, int n) {  // the split arrival counters
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
 
+#ifndef LORA_DX_RANK64_TU
 int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile)); }
 
 // Number of N ranges of the input-gradient grid: the count that minimises the estimated time
@@ -489,6 +513,7 @@ size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R) {
   const int rp = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
   return (size_t)dx_tiles(M, K) * s * (4 * 64 * 64 * 16 + 4 * (rp / 16) * 4 * 64 * 16);
 }
+#endif
 
 template <int RP, bool INT4>
 static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
@@ -506,16 +531,17 @@ static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef LORA_DX_RANK64_TU
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
-  if (int4) {
-    if (rp == 16) return launch_dx_rp<16, true>(a, s);
-    if (rp == 32) return launch_dx_rp<32, true>(a, s);
-    return launch_dx_rp<64, true>(a, s);
-  }
-  if (rp == 16) return launch_dx_rp<16, false>(a, s);
-  if (rp == 32) return launch_dx_rp<32, false>(a, s);
-  return launch_dx_rp<64, false>(a, s);
+  if (rp == 64) return launch_dx_rank64(a, int4, s);
+  if (int4) return rp == 16 ? launch_dx_rp<16, true>(a, s) : launch_dx_rp<32, true>(a, s);
+  return rp == 16 ? launch_dx_rp<16, false>(a, s) : launch_dx_rp<32, false>(a, s);
 }
+#else
+hipError_t launch_dx_rank64(const DxArgs& a, bool int4, hipStream_t s) {
+  return int4 ? launch_dx_rp<64, true>(a, s) : launch_dx_rp<64, false>(a, s);
+}
+#endif
 
 }  // namespace lora

@@ -147,8 +147,12 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      // every row of the next phase uses all eight X fragments: they go out in rows 0-3
+      if (i < 4) {
+        nx.x[2 * i] = ld16(x + lds_offf(wm * 128 + 2 * i * 16 + l16, ch));
+        nx.x[2 * i + 1] = ld16(x + lds_offf(wm * 128 + (2 * i + 1) * 16 + l16, ch));
+      }
       nx.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
-      nx.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -177,10 +181,9 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   auto read_frags = [&](Frag& f, const uint16_t* x, const uint16_t* w, const uint16_t* a, int kk) {
     const int ch = kk * 4 + g4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
-      f.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
-    }
+    for (int i = 0; i < 8; ++i) f.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
 #pragma unroll
     for (int c = 0; c < RP / 16; ++c) f.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
   };

@@ -55,6 +55,7 @@ struct DadbArgs {
 // bf16 / int4 MFMA paths
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s);
+hipError_t launch_dx_rank64(const DxArgs& a, bool int4, hipStream_t s);  // ranks 33..64
 // input-gradient grid: output tiles, N ranges per tile, bytes of split partials (0 if unsplit)
 int dx_tiles(int64_t M, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K, int R);
