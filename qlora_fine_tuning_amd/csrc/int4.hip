@@ -198,8 +198,17 @@ __device__ void decode_adapter(const DecodeArgs& a, int xw, float* sred, int* sf
   if (!*sflag) return;
   for (int e = tid; e < M * a.R; e += 256) {
     const int tt = e / a.R, i = e - tt * a.R;
+    // the partials in order, eight loads in flight at a time
     float s = 0.f;
-    for (int x = 0; x < a.NXA; ++x) s += ld_dev(a.pxa + ((size_t)x * M + tt) * RP + i);
+    int x = 0;
+    for (; x + 8 <= a.NXA; x += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = ld_dev(a.pxa + ((size_t)(x + q) * M + tt) * RP + i);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; x < a.NXA; ++x) s += ld_dev(a.pxa + ((size_t)x * M + tt) * RP + i);
     st_dev(a.xaf + tt * RP + i, s);
     if (a.XA != nullptr) a.XA[e] = s;
   }
@@ -361,9 +370,19 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
       sflag = __hip_atomic_fetch_add(ctl + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(a.S - 1);
     __syncthreads();
     if (!sflag) return;
-    if (r16 < M) {
+    if (r16 < M) {  // the split partials in order, two splits' loads in flight at a time
       p = fzero4();
-      for (int s = 0; s < a.S; ++s) {
+      int s = 0;
+      for (; s + 2 <= a.S; s += 2) {
+        const float* s0 = a.part + (((size_t)s * T + tile) * M + r16) * kDecRows + nl;
+        const float* s1 = a.part + (((size_t)(s + 1) * T + tile) * M + r16) * kDecRows + nl;
+        float v0[4], v1[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) v0[v] = ld_dev(s0 + v), v1[v] = ld_dev(s1 + v);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) p[v] = (p[v] + v0[v]) + v1[v];
+      }
+      if (s < a.S) {
         const float* src = a.part + (((size_t)s * T + tile) * M + r16) * kDecRows + nl;
 #pragma unroll
         for (int v = 0; v < 4; ++v) p[v] += ld_dev(src + v);
