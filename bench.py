@@ -13,7 +13,8 @@ kernel of a lora_bwd_dx call), timed live with HIP events on its stream; its `tr
 per-launch HBM byte count recorded under profiles/ from rocprofv3 counters, or null when the
 kernel's sources have changed since the counters were taken.  `cpu_baseline` times the float64
 oracle on a bounded sample of the same workload.  `secondary` holds the QLoRA fwd+bwd rate
-on the int4 FFN projection and the decode matrix-vector bandwidth.
+on the int4 FFN projection, the decode matrix-vector bandwidth, and the same attention
+projection layer run unfused through torch (hipBLASLt GEMMs), for comparison.
 """
 from __future__ import annotations
 
@@ -119,6 +120,28 @@ def cpu_baseline(inp, min_seconds):
                       f"({fl:.3e} FLOP in {dt:.2f} s)"}
 
 
+def bench_torch_unfused(torch, X, W, A, B, dY, scale, reps):
+    """The same layer as separate library GEMMs (no fusion): Y = X W^T + s (X A^T) B^T and its
+    backward with W frozen, in bf16 through torch.matmul (hipBLASLt)."""
+    def step():
+        XA = X @ A.t()
+        Y = torch.addmm(X @ W.t(), XA, B.t(), alpha=scale)
+        G = dY @ B
+        dX = torch.addmm(dY @ W, G, A, alpha=scale)
+        dA = (G.t() @ X) * scale
+        dB = (dY.t() @ XA) * scale
+        return Y, dX, dA, dB
+
+    for _ in range(10):
+        step()
+    ms = event_time_ms(step, reps, torch.cuda.current_stream())
+    M, K = X.shape
+    N, R = W.shape[0], A.shape[0]
+    return {"workload": "attn_proj", "ms_per_step": round(ms, 4),
+            "TFLOP/s": round(lora_flops(M, N, K, R) / ms / 1e9, 2),
+            "note": "bf16 torch.matmul / addmm, one GEMM per product, fp32 accumulation inside each"}
+
+
 def bench_qlora_ffn(lora, torch, dev, reps):
     from qlora_fine_tuning_amd.workloads import workload_inputs
 
@@ -186,8 +209,10 @@ def bench_decode(lora, torch, dev, reps, copies=6):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clocks settle over the first tens of milliseconds of sustained matrix work: the
+    # timed steps come after 100 untimed ones (about 50 ms)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the QLoRA and decode lines")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -281,7 +306,8 @@ def main(argv=None):
     }
     if not args.no_secondary:
         result["secondary"] = {"qlora": bench_qlora_ffn(lora, torch, dev, 5),
-                               "decode": bench_decode(lora, torch, dev, 20)}
+                               "decode": bench_decode(lora, torch, dev, 20),
+                               "torch_unfused": bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}
     if args.calib_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
