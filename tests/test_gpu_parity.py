@@ -366,3 +366,34 @@ def test_decode_workspace_reuse(gpu_lib):
     Y, XA = lora.qlora_fwd(X8[:5].contiguous(), Wq, Ws, A, B, inp.scale)
     torch.cuda.synchronize()
     assert torch.equal(Y, first[5][0]) and torch.equal(XA, first[5][1])
+
+
+# ---------------------------------------------------------------------------
+# size limits: the longest rows the header allows (N, K <= 2^20) and many tokens
+# ---------------------------------------------------------------------------
+
+def test_bf16_longest_k(gpu_lib):
+    # forward: one output tile, 16384 K steps; dX: 4096 tiles of one N step
+    _say("case bf16 M=64 N=64 K=2^20 R=16")
+    check_full(gpu_lib, make_inputs(64, 64, 1 << 20, 16, seed=401, dtype="bf16"))
+
+
+def test_bf16_longest_n(gpu_lib):
+    # forward: 4096 output tiles; dX: one tile whose 16384 N steps are split over 8 units
+    _say("case bf16 M=64 N=2^20 K=64 R=16")
+    M, N, K, R = 64, 1 << 20, 64, 16
+    assert gpu_lib.lora_bwd_workspace_bytes(gpu_lib.LORA_BF16, M, N, K, R) > _unsplit_ws_bytes(M, N, K, R)
+    check_full(gpu_lib, make_inputs(M, N, K, R, seed=402, dtype="bf16"))
+
+
+def test_bf16_many_tokens(gpu_lib):
+    # 2^18 + 37 tokens: 1025 token splits of the dA / dB sums, a ragged last token tile
+    _say("case bf16 M=2^18+37 N=256 K=256 R=8")
+    check_sampled(gpu_lib, make_inputs((1 << 18) + 37, 256, 256, 8, seed=403, dtype="bf16"))
+
+
+def test_qlora_decode_longest_k(gpu_lib):
+    # K = 2^20 at M = 4: 1024 adapter workgroups (more than fit at once) ahead of the tile
+    # workgroup that waits for their X A^T
+    _say("case qlora decode M=4 N=64 K=2^20 R=16")
+    check_qlora(gpu_lib, make_inputs(4, 64, 1 << 20, 16, seed=404, dtype="bf16", int4=True), sampled=False)
