@@ -39,8 +39,7 @@ HIP_FLAGS = [
 
 # Per-source extra flags.  The MFMA kernels keep their main accumulators in AGPRs through
 # inline asm; the builtin MFMAs of their small rank-R panels are put in VGPRs so that the two
-# never compete for the AGPR file.  dx64.hip (the rank-64 input-gradient instances, builtin
-# MFMAs throughout) keeps the compiler's default forms.
+# never compete for the AGPR file.
 EXTRA_FLAGS = {
     "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "dx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],

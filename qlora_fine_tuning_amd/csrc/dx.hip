@@ -52,12 +52,17 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
                const uint16_t* __restrict__ Bm, uint16_t* __restrict__ dX,
                float* __restrict__ G, int M, int N, int K, int R, float scale, int splits,
                float* __restrict__ part, uint32_t* __restrict__ ctr) {
-  // Ranks up to 32: the accumulators stay in AGPRs through inline-asm MFMAs (this file is
-  // built with the panel MFMAs in VGPR form).  Rank 64 runs out of registers, and the compiler
-  // then moves accumulators between registers, which must not happen to an asm MFMA's result
-  // still in flight: those instances use builtin MFMAs, built in their own translation unit
-  // (dx64.hip) with the compiler's default register forms.
-  constexpr bool ASM = RP <= 32;
+  // The accumulators stay in AGPRs through inline-asm MFMAs (this file is built with the
+  // panel MFMAs in VGPR form).  That is only sound while the compiler never has to move an
+  // accumulator inside the loop (it cannot see an asm MFMA's result latency); the builtin
+  // path (ASM = false) is kept for instances where it would have to.
+  constexpr bool ASM = true;
+  // Ranks up to 32 compute the panel G = dY B here, from the dY fragments of the main loop.
+  // The rank-64 instances read G, computed by a pass of its own, in the epilogue: the panel's
+  // 16 accumulator blocks and B fragments do not fit next to the main tile's, and with them
+  // the compiler spills and moves accumulators.
+  constexpr bool PANEL = RP <= 32;
+  constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
   constexpr int TT = kTile * kStep;  // 16384 elements: dY tile 256 x 64, W tile 64 x 256
   constexpr int BT = kStep * RP;     // B tile: 64 rows (n) x RP ranks
   constexpr int BQ = (BT / 8 + kThreads - 1) / kThreads;  // 16-byte chunks per thread
@@ -162,11 +167,11 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
 
   f32x4 acc[64];  // acc[i * 8 + j]: dX^T rows (k) block i, columns (m) block j
-  f32x4 pacc[RP / 16][4];
+  f32x4 pacc[NB][4];
 #pragma unroll
   for (int i = 0; i < 64; ++i) acc[i] = fzero4();
 #pragma unroll
-  for (int c = 0; c < RP / 16; ++c)
+  for (int c = 0; c < NB; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
   if constexpr (ASM) mfma_acc_ready(acc);
@@ -183,7 +188,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   const int boff = trow * RP + (l16 & 3) * 4;
 
   struct Frag {
-    u32x4 w[8], d[8], b[RP / 16];
+    u32x4 w[8], d[8], b[NB];
   };
   auto wfrag = [&](const uint16_t* w, int kk, int i) -> u32x4 {
     const int kb = wk * 8 + i;  // 16-column block within the 256-column tile
@@ -227,16 +232,18 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (PANEL) {
 #pragma unroll
-    for (int c = 0; c < RP / 16; ++c) nx.b[c] = bfrag(b, kk, c);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < RP / 16; ++c) nx.b[c] = bfrag(b, kk, c);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 dp = wk ? cu.d[4 + j] : cu.d[j];
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 dp = wk ? cu.d[4 + j] : cu.d[j];
 #pragma unroll
-      for (int c = 0; c < RP / 16; ++c) pacc[c][j] = mfma16(cu.b[c], dp, pacc[c][j]);
+        for (int c = 0; c < RP / 16; ++c) pacc[c][j] = mfma16(cu.b[c], dp, pacc[c][j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
   auto read_frags = [&](Frag& f, const uint16_t* d, const uint16_t* w, const uint16_t* b, int kk) {
     const int ch = kk * 4 + g4;
@@ -245,8 +252,9 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       f.w[i] = wfrag(w, kk, i);
       f.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
     }
+    if constexpr (PANEL)
 #pragma unroll
-    for (int c = 0; c < RP / 16; ++c) f.b[c] = bfrag(b, kk, c);
+      for (int c = 0; c < RP / 16; ++c) f.b[c] = bfrag(b, kk, c);
   };
   // wait for the copies of the next step: for int4 W, the three register loads issued after
   // them stay in flight
@@ -259,7 +267,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const int n0 = nbase + min(st, nsteps - 1) * kStep;
     dma_d(dn, n0);
     if constexpr (!INT4) dma_w(wn, n0);
-    load_b(n0);
+    if constexpr (PANEL) load_b(n0);
     (void)bn;
   };
   // the same copies in 16 parts for phase(): the B rows first (a register load, waited for
@@ -267,7 +275,8 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   // or the int4 register loads
   auto prefetch_part = [&](int q, int st, uint16_t* dn, uint16_t* wn) {
     const int n0 = nbase + min(st, nsteps - 1) * kStep;
-    if (q == 0) load_b(n0);
+    if constexpr (PANEL)
+      if (q == 0) load_b(n0);
     if (q < 8) {
       dma16(rD, dn + (4 * q + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)q * 32u * rowD);
     } else if constexpr (!INT4) {
@@ -279,9 +288,13 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   const NoCopy nocopy;
   auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch (bf16)
     (void)wn;
-    store_b(bn);
+    if constexpr (PANEL) store_b(bn);
+    else (void)bn;
   };
-  auto finish_b = [&](uint16_t* bn) { store_b(bn); };
+  auto finish_b = [&](uint16_t* bn) {
+    if constexpr (PANEL) store_b(bn);
+    else (void)bn;
+  };
 
   // Same pipeline as the forward kernel (see there), over N steps of 64.
   Frag f0, f1;
@@ -423,16 +436,24 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   auto arow_ptr = [&](int r) -> uint16_t* {
     return reinterpret_cast<uint16_t*>(buf(r / AR) + GBYTES) + (r % AR) * AS;
   };
+  if constexpr (PANEL) {
 #pragma unroll
-  for (int c = 0; c < RP / 16; ++c)
+    for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ml = wm * 128 + (wk * 4 + j) * 16 + l16;
-      const int rk = c * 16 + g4 * 4;
-      *reinterpret_cast<f32x4*>(grow(ml) + rk) = pacc[c][j];
-      if (tk == 0 && m0 + ml < M && rk < R)
-        *reinterpret_cast<f32x4*>(G + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
+      for (int j = 0; j < 4; ++j) {
+        const int ml = wm * 128 + (wk * 4 + j) * 16 + l16;
+        const int rk = c * 16 + g4 * 4;
+        *reinterpret_cast<f32x4*>(grow(ml) + rk) = pacc[c][j];
+        if (tk == 0 && m0 + ml < M && rk < R)
+          *reinterpret_cast<f32x4*>(G + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
+      }
+  } else {  // G from the panel pass (ranks >= R and tokens >= M as zeros)
+    for (int e = tid; e < kTile * (RP / 4); e += kThreads) {
+      const int ml = e / (RP / 4), rk = (e % (RP / 4)) * 4;
+      const f32x4 v = (m0 + ml < M && rk < R) ? *reinterpret_cast<const f32x4*>(G + (size_t)(m0 + ml) * R + rk) : fzero4();
+      *reinterpret_cast<f32x4*>(grow(ml) + rk) = v;
     }
+  }
   if constexpr (RP <= 32) {
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
@@ -484,12 +505,11 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   store_block_bf16(acc, stage, dX + (size_t)mw * K + kw, (size_t)K, M - mw, K - kw, lane);
 }
 
-static __global__ void zero_u32_kernel(uint32_t* p, int n) {  // the split arrival counters
+__global__ void zero_u32_kernel(uint32_t* p, int n) {  // the split arrival counters
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
 
-#ifndef LORA_DX_RANK64_TU
 int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile)); }
 
 // Number of N ranges of the input-gradient grid: the count that minimises the estimated time
@@ -513,7 +533,6 @@ size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R) {
   const int rp = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
   return (size_t)dx_tiles(M, K) * s * (4 * 64 * 64 * 16 + 4 * (rp / 16) * 4 * 64 * 16);
 }
-#endif
 
 template <int RP, bool INT4>
 static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
@@ -531,17 +550,16 @@ static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef LORA_DX_RANK64_TU
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
-  if (rp == 64) return launch_dx_rank64(a, int4, s);
-  if (int4) return rp == 16 ? launch_dx_rp<16, true>(a, s) : launch_dx_rp<32, true>(a, s);
-  return rp == 16 ? launch_dx_rp<16, false>(a, s) : launch_dx_rp<32, false>(a, s);
+  if (int4) {
+    if (rp == 16) return launch_dx_rp<16, true>(a, s);
+    if (rp == 32) return launch_dx_rp<32, true>(a, s);
+    return launch_dx_rp<64, true>(a, s);
+  }
+  if (rp == 16) return launch_dx_rp<16, false>(a, s);
+  if (rp == 32) return launch_dx_rp<32, false>(a, s);
+  return launch_dx_rp<64, false>(a, s);
 }
-#else
-hipError_t launch_dx_rank64(const DxArgs& a, bool int4, hipStream_t s) {
-  return int4 ? launch_dx_rp<64, true>(a, s) : launch_dx_rp<64, false>(a, s);
-}
-#endif
 
 }  // namespace lora

@@ -55,7 +55,12 @@ struct DadbArgs {
 // bf16 / int4 MFMA paths
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s);
-hipError_t launch_dx_rank64(const DxArgs& a, bool int4, hipStream_t s);  // ranks 33..64
+// ranks 33..64: G = dY B as a pass of its own (written to G), ahead of the input-gradient kernel,
+// which then reads G in its epilogue; `ws` holds panel_workspace_bytes() bytes
+int panel_shares(int64_t M, int64_t C);
+size_t panel_workspace_bytes(int64_t M, int64_t N, int R);
+hipError_t launch_panel_g(const uint16_t* dY, const uint16_t* B, float* G, void* ws, int64_t M, int64_t N,
+                          int R, hipStream_t s);
 // input-gradient grid: output tiles, N ranges per tile, bytes of split partials (0 if unsplit)
 int dx_tiles(int64_t M, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K, int R);

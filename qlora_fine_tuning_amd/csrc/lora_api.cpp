@@ -50,9 +50,10 @@ int64_t splits_for(int64_t M) { return (M + kSplitRows - 1) / kSplitRows; }
 
 // Backward workspace: G [M][R] fp32 | partA [splits][R][K] fp32 | partB [splits][R][N] fp32,
 // then, for an MFMA (bf16 / int4) input gradient whose N is split, its per-tile arrival
-// counters and split partials.
+// counters and split partials, and for an MFMA input gradient of rank above 32, the scratch of
+// its G pass (B transposed, per-share partials).
 struct BwdLayout {
-  size_t g, pa, pb, ctr, dxp, total;
+  size_t g, pa, pb, ctr, dxp, pan, total;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R, bool mfma) {
   const int64_t s = splits_for(M);
@@ -66,8 +67,10 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R, bool mfma) {
   const size_t part = mfma ? dx_part_bytes(M, N, K, R) : 0;
   if (part > 0) {
     l.dxp = l.ctr + align256((size_t)dx_tiles(M, K) * sizeof(uint32_t));
-    l.total = l.dxp + part;
+    l.total = l.dxp + align256(part);
   }
+  l.pan = l.total;
+  if (mfma && R > 32) l.total = l.pan + align256(panel_workspace_bytes(M, N, R));
   return l;
 }
 
@@ -86,7 +89,13 @@ lora_status bwd_dx_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_
   DxArgs a{dY, W, Ws, A, B, dX, G, M, N, K, R, scale, reinterpret_cast<uint32_t*>(base + lay.ctr),
            reinterpret_cast<float*>(base + lay.dxp)};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip((dt == LORA_F32) ? launch_dx_f32(a, s) : launch_dx_mfma(a, int4, s));
+  if (dt == LORA_F32) return from_hip(launch_dx_f32(a, s));
+  if (R > 32) {  // the rank-64 input-gradient kernel reads G from this pass
+    const hipError_t e = launch_panel_g(static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(B), G,
+                                        base + lay.pan, M, N, R, s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return from_hip(launch_dx_mfma(a, int4, s));
 }
 
 lora_status bwd_dadb_common(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,

@@ -1,0 +1,143 @@
+// The rank-R panel of the input gradient as a pass of its own, for ranks above 32:
+//
+//   G = dY B        (M x R, fp32)
+//
+// tutorial ch. 5 "加速原理：Triton kernel 与 fused LoRA", §5.3 (the LoRA backward; gradients
+// derived by hand).  Up to rank 32 the input-gradient kernel computes G from the dY tiles it
+// already holds; at rank 64 the panel's accumulators and operands no longer fit next to the
+// main tile's, so G comes from here and the main kernel reads it in its epilogue.
+//
+//  * bt_transpose_kernel: B (N x R, rank-contiguous) -> Bt (R x N), so that both MFMA operands
+//    of the panel are contiguous along the contraction index n;
+//  * panel_kernel: one workgroup per (64 tokens, share of N); each wave owns 16 tokens and all
+//    64 ranks (4 MFMA blocks) and streams its dY rows and the Bt rows straight from memory
+//    (no LDS: dY is read once, Bt is small and stays in L2), writing an fp32 partial;
+//  * panel_reduce_kernel: adds the partials in share order into G.
+// The sums run in a fixed order: results are bitwise reproducible.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lora {
+
+constexpr int kPanelRows = 64;   // tokens per workgroup (16 per wave)
+constexpr int kPanelRanks = 64;  // ranks covered (R in 33..64; ranks >= R read as zero)
+
+// Bt[r][n] = B[n][r]: a 64 x R block of B per workgroup through LDS.
+__global__ void __launch_bounds__(256)
+bt_transpose_kernel(const uint16_t* __restrict__ B, uint16_t* __restrict__ Bt, int N, int R) {
+  __shared__ uint16_t tile[64][kPanelRanks + 2];
+  const int n0 = blockIdx.x * 64, tid = threadIdx.x;
+  for (int e = tid; e < 64 * R; e += 256) {
+    const int n = e / R, r = e - n * R;
+    tile[n][r] = B[(size_t)(n0 + n) * R + r];
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * R; e += 256) {
+    const int r = e >> 6, n = e & 63;
+    Bt[(size_t)r * N + n0 + n] = tile[n][r];
+  }
+}
+
+// part[s][m][0..63] = sum over c in share s of Q[m][c] * S[r][c]  (Q: M x C, S: R x C, bf16)
+__global__ void __launch_bounds__(256)
+panel_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ S, float* __restrict__ part,
+             int M, int C, int R, int share) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int m0 = blockIdx.x * kPanelRows + wave * 16;
+  const int cs = blockIdx.y;
+  const int c0 = cs * share, c1 = min(C, c0 + share);
+  const rsrc_t rQ = make_rsrc(Q + (size_t)m0 * C, (uint32_t)max(0, min(16, M - m0)) * (uint32_t)C * 2u);
+  const rsrc_t rS = make_rsrc(S, (uint32_t)R * (uint32_t)C * 2u);
+  const uint32_t qoff = ((uint32_t)l16 * (uint32_t)C + (uint32_t)(8 * g4)) * 2u;
+  f32x4 acc[4] = {fzero4(), fzero4(), fzero4(), fzero4()};
+  // four 32-wide steps per iteration: their 20 loads are issued before the first MFMA
+  int c = c0;
+  for (; c + 128 <= c1; c += 128) {
+    u32x4 a[4], s[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = bload16(rQ, qoff + (uint32_t)(c + 32 * u) * 2u, 0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        s[u][rb] = bload16(rS, ((uint32_t)(rb * 16 + l16) * (uint32_t)C + (uint32_t)(c + 32 * u + 8 * g4)) * 2u, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) acc[rb] = mfma16(s[u][rb], a[u], acc[rb]);
+  }
+  for (; c < c1; c += 32) {
+    const u32x4 a = bload16(rQ, qoff + (uint32_t)c * 2u, 0);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      acc[rb] = mfma16(bload16(rS, ((uint32_t)(rb * 16 + l16) * (uint32_t)C + (uint32_t)(c + 8 * g4)) * 2u, 0), a, acc[rb]);
+  }
+  // acc[rb]: ranks rb*16 + 4 g4 .. +3 of token m0 + l16
+  const int m = m0 + l16;
+  if (m < M) {
+    float* dst = part + ((size_t)cs * M + m) * kPanelRanks;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) *reinterpret_cast<f32x4*>(dst + rb * 16 + 4 * g4) = acc[rb];
+  }
+}
+
+// G[m][r] = sum_s part[s][m][r], s in order.
+__global__ void __launch_bounds__(256)
+panel_reduce_kernel(const float* __restrict__ part, float* __restrict__ G, int M, int R, int shares) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)M * R) return;
+  const int64_t m = e / R, r = e - m * R;
+  const float* src = part + m * kPanelRanks + r;
+  float s = 0.f;
+  int q = 0;
+  for (; q + 4 <= shares; q += 4) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[(int64_t)(q + u) * M * kPanelRanks];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += v[u];
+  }
+  for (; q < shares; ++q) s += src[(int64_t)q * M * kPanelRanks];
+  G[e] = s;
+}
+
+// Shares of N per 64-token block: enough workgroups to cover the chip twice, at least 256 wide.
+int panel_shares(int64_t M, int64_t C) {
+  const int64_t blocks = (M + kPanelRows - 1) / kPanelRows;
+  int64_t s = std::max<int64_t>(1, (512 + blocks - 1) / blocks);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, C / 256));
+  return (int)s;
+}
+static int64_t panel_share_len(int64_t C, int shares) { return ((C + shares - 1) / shares + 63) / 64 * 64; }
+
+size_t panel_workspace_bytes(int64_t M, int64_t N, int R) {
+  const int s = panel_shares(M, N);
+  const size_t bt = ((size_t)R * N * 2 + 255) & ~(size_t)255;
+  return bt + (size_t)s * M * kPanelRanks * 4;
+}
+
+hipError_t launch_panel_g(const uint16_t* dY, const uint16_t* B, float* G, void* ws, int64_t M, int64_t N,
+                          int R, hipStream_t s) {
+  const int shares = panel_shares(M, N);
+  const int64_t len = panel_share_len(N, shares);
+  const int used = (int)((N + len - 1) / len);
+  uint16_t* Bt = static_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)R * N * 2 + 255) & ~(size_t)255));
+  hipLaunchKernelGGL(bt_transpose_kernel, dim3((unsigned)(N / 64)), dim3(256), 0, s, B, Bt, (int)N, R);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(panel_kernel, dim3((unsigned)((M + kPanelRows - 1) / kPanelRows), (unsigned)used), dim3(256), 0, s,
+                     dY, Bt, part, (int)M, (int)N, R, (int)len);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = M * R;
+  hipLaunchKernelGGL(panel_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, G,
+                     (int)M, R, used);
+  return hipGetLastError();
+}
+
+}  // namespace lora
