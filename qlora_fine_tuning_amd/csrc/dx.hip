@@ -364,10 +364,9 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   if constexpr (ASM) mfma_drain(acc);
 
   // ---- split N: store this unit's partial; the last unit of the tile adds them all ----
-  // (ranks up to 32: the rank-64 instances crash the compiler with this block and run unsplit)
-  if constexpr (RP <= 32) if (splits > 1) {
-    // partial slot: [wave][acc block][lane] f32x4, then the G panel [wave][block][lane]
-    constexpr uint32_t kAccBytes = 4 * 64 * 64 * 16, kPanBytes = 4 * (RP / 16) * 4 * 64 * 16;
+  if (splits > 1) {
+    // partial slot: [wave][acc block][lane] f32x4, then (with a panel) the G panel [wave][block][lane]
+    constexpr uint32_t kAccBytes = 4 * 64 * 64 * 16, kPanBytes = PANEL ? 4 * (RP / 16) * 4 * 64 * 16 : 0;
     constexpr uint32_t kSlot = kAccBytes + kPanBytes;
     const rsrc_t rP = make_rsrc(part + (size_t)tile * splits * (kSlot / 4), (uint32_t)splits * kSlot);
     const uint32_t wa = ((uint32_t)wave * 64 * 64 + lane) * 16u;
@@ -375,10 +374,11 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const uint32_t own = (uint32_t)sp * kSlot;
 #pragma unroll
     for (int i = 0; i < 64; ++i) st_part(rP, own + wa + i * 1024u, acc[i]);
+    if constexpr (PANEL)
 #pragma unroll
-    for (int c = 0; c < RP / 16; ++c)
+      for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st_part(rP, own + wp + (c * 4 + j) * 1024u, pacc[c][j]);
+        for (int j = 0; j < 4; ++j) st_part(rP, own + wp + (c * 4 + j) * 1024u, pacc[c][j]);
     wait_vmem();
     __shared__ int s_last;
     __syncthreads();
@@ -406,6 +406,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[c0 + i] = tot[i];
     }
+    if constexpr (PANEL)
 #pragma unroll
     for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
@@ -514,11 +515,11 @@ int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((
 
 // Number of N ranges of the input-gradient grid: the count that minimises the estimated time
 // (rounds of 256 resident workgroups x steps per unit, a split costing about 4 steps for its
-// partial), with at least 8 steps per unit and at most 8 ranges; ranks above 32 are unsplit.
+// partial), with at least 8 steps per unit and at most 8 ranges.
 int dx_splits(int64_t M, int64_t N, int64_t K, int R) {
   const int64_t tiles = dx_tiles(M, K), steps = N / kStep;
   int best = 1;
-  if (R > 32) return 1;
+  (void)R;
   int64_t best_cost = ((tiles + 255) / 256) * steps;
   for (int64_t s = 2; s <= 8 && steps / s >= 8; ++s) {
     const int64_t cost = ((tiles * s + 255) / 256) * ((steps + s - 1) / s + 4);
@@ -531,7 +532,8 @@ size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R) {
   const int s = dx_splits(M, N, K, R);
   if (s == 1) return 0;
   const int rp = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
-  return (size_t)dx_tiles(M, K) * s * (4 * 64 * 64 * 16 + 4 * (rp / 16) * 4 * 64 * 16);
+  const size_t panel = rp <= 32 ? (size_t)4 * (rp / 16) * 4 * 64 * 16 : 0;  // rank 64: G from its own pass
+  return (size_t)dx_tiles(M, K) * s * ((size_t)4 * 64 * 64 * 16 + panel);
 }
 
 template <int RP, bool INT4>

@@ -84,7 +84,8 @@ def _unsplit_ws_bytes(M, N, K, R):
 
 # Few output tiles and a long N loop: the input gradient cuts N into 8, 4 or 2 ranges whose
 # partials the last-arriving unit of each tile adds (the workspace grows by the partials).
-@pytest.mark.parametrize("M,N,K,R", [(256, 4096, 256, 16), (513, 2048, 576, 8), (300, 1024, 320, 32)])
+@pytest.mark.parametrize("M,N,K,R", [(256, 4096, 256, 16), (513, 2048, 576, 8), (300, 1024, 320, 32),
+                                     (256, 4096, 256, 64), (300, 2048, 320, 48)])
 def test_bf16_split_n_shapes(gpu_lib, M, N, K, R):
     _say(f"case bf16 split-N M={M} N={N} K={K} R={R}")
     assert gpu_lib.lora_bwd_workspace_bytes(gpu_lib.LORA_BF16, M, N, K, R) > _unsplit_ws_bytes(M, N, K, R)
@@ -322,7 +323,7 @@ def check_qlora(lora, inp, sampled: bool):
                                      (1, 256, 512, 16), (5, 384, 1280, 16), (8, 320, 256, 64),
                                      (1, 64, 1024, 16), (5, 384, 2048, 16), (8, 320, 1024, 64),
                                      (3, 192, 3072, 24), (7, 448, 4096, 8), (2, 128, 8192, 40),
-                                     (200, 2048, 512, 24), (9, 4096, 256, 16)])
+                                     (200, 2048, 512, 24), (9, 4096, 256, 16), (200, 2048, 512, 64)])
 def test_qlora_small_shapes(gpu_lib, M, N, K, R):
     _say(f"case qlora M={M} N={N} K={K} R={R}")
     check_qlora(gpu_lib, make_inputs(M, N, K, R, seed=300 + M, dtype="bf16", int4=True), sampled=False)
