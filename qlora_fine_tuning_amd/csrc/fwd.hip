@@ -23,7 +23,10 @@
 
 namespace lora {
 
-template <int RP, bool INT4>
+// PANEL: the panel X A^T is accumulated here from the X fragments of the main loop.  Without
+// it (rank 64, when the caller keeps XA) XA has been computed by a pass of its own and is read
+// in the epilogue: the rank-64 panel's accumulators and A fragments make the main loop spill.
+template <int RP, bool INT4, bool PANEL>
 __global__ void __launch_bounds__(kThreads)
 fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
@@ -117,25 +120,27 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   };
 
   f32x4 acc[64];  // acc[i * 8 + j]: Y^T rows (W) block i, columns (X) block j
-  f32x4 pacc[RP / 16][4];
+  constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
+  f32x4 pacc[NB][4];
 #pragma unroll
   for (int i = 0; i < 64; ++i) acc[i] = fzero4();
   mfma_acc_ready(acc);
 #pragma unroll
-  for (int c = 0; c < RP / 16; ++c)
+  for (int c = 0; c < NB; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
 
   // adapter rows R .. AROWS-1 stay zero in both buffers
-  for (int e = R * kStep + tid * 8; e < AT; e += kThreads * 8) {
-    st16(sA0 + e, zero4());
-    st16(sA1 + e, zero4());
-  }
+  if constexpr (PANEL)
+    for (int e = R * kStep + tid * 8; e < AT; e += kThreads * 8) {
+      st16(sA0 + e, zero4());
+      st16(sA1 + e, zero4());
+    }
 
   // MFMA operands of one 32-wide half step: 8 W fragments (rows of Y^T), 8 X fragments
   // (columns of Y^T), RP/16 adapter fragments.
   struct Frag {
-    u32x4 w[8], x[8], a[RP / 16];
+    u32x4 w[8], x[8], a[NB];
   };
   // Reads the fragments of half step `kk` into `nx` while running the MFMAs of `cu`.  The
   // reads are spread between the MFMA rows so that LDS latency hides behind matrix work.
@@ -167,16 +172,18 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (PANEL) {
 #pragma unroll
-    for (int c = 0; c < RP / 16; ++c) nx.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
-    __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < RP / 16; ++c) nx.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 xp = wn ? cu.x[4 + j] : cu.x[j];  // this wave's half of the panel rows
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 xp = wn ? cu.x[4 + j] : cu.x[j];  // this wave's half of the panel rows
 #pragma unroll
-      for (int c = 0; c < RP / 16; ++c) pacc[c][j] = mfma16(cu.a[c], xp, pacc[c][j]);
+        for (int c = 0; c < RP / 16; ++c) pacc[c][j] = mfma16(cu.a[c], xp, pacc[c][j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
   auto read_frags = [&](Frag& f, const uint16_t* x, const uint16_t* w, const uint16_t* a, int kk) {
     const int ch = kk * 4 + g4;
@@ -184,8 +191,9 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     for (int i = 0; i < 8; ++i) f.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
 #pragma unroll
     for (int i = 0; i < 8; ++i) f.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
+    if constexpr (PANEL)
 #pragma unroll
-    for (int c = 0; c < RP / 16; ++c) f.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
+      for (int c = 0; c < RP / 16; ++c) f.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
   };
   // wait for the copies of the next step: for int4 W, the four register loads issued after
   // them (two steps ahead) stay in flight
@@ -200,13 +208,14 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     const int k1 = min(kn, nk - 1) * kStep;
     dma_tile(rX, xn, k1);
     if constexpr (!INT4) dma_tile(rW, wnx, k1);
-    dma_a(an, k1);
+    if constexpr (PANEL) dma_a(an, k1);
   };
   // The same copies in 16 parts for phase(): the adapter rows first, then X rows 8d.. (d < 8),
   // W rows (bf16) or the int4 register loads.
   auto prefetch_part = [&](int d, int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an) {
     const int k1 = min(kn, nk - 1) * kStep;
-    if (d == 0) dma_a(an, k1);
+    if constexpr (PANEL)
+      if (d == 0) dma_a(an, k1);
     if (d < 8) {
       dma16(rX, xn + (4 * d + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)d * 32u * rowb);
     } else if constexpr (!INT4) {
@@ -285,16 +294,24 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   auto xa_rows = [&](int q) -> float* {
     return reinterpret_cast<float*>(q == 0 ? sX0 : (q == 1 ? sX1 : (q == 2 ? sW0 : sW1)));
   };
+  if constexpr (PANEL) {
 #pragma unroll
-  for (int c = 0; c < RP / 16; ++c)
+    for (int c = 0; c < RP / 16; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ml = wm * 128 + (wn * 4 + j) * 16 + l16;
-      const int rk = c * 16 + g4 * 4;
-      *reinterpret_cast<f32x4*>(xa_rows(ml >> 6) + (ml & 63) * XS + rk) = pacc[c][j];
-      if (XA != nullptr && tn == 0 && m0 + ml < M && rk < R)
-        *reinterpret_cast<f32x4*>(XA + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
+      for (int j = 0; j < 4; ++j) {
+        const int ml = wm * 128 + (wn * 4 + j) * 16 + l16;
+        const int rk = c * 16 + g4 * 4;
+        *reinterpret_cast<f32x4*>(xa_rows(ml >> 6) + (ml & 63) * XS + rk) = pacc[c][j];
+        if (XA != nullptr && tn == 0 && m0 + ml < M && rk < R)
+          *reinterpret_cast<f32x4*>(XA + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
+      }
+  } else {  // XA from its own pass (ranks >= R and tokens >= M as zeros)
+    for (int e = tid; e < kTile * (RP / 4); e += kThreads) {
+      const int ml = e / (RP / 4), rk = (e % (RP / 4)) * 4;
+      const f32x4 v = (m0 + ml < M && rk < R) ? *reinterpret_cast<const f32x4*>(XA + (size_t)(m0 + ml) * R + rk) : fzero4();
+      *reinterpret_cast<f32x4*>(xa_rows(ml >> 6) + (ml & 63) * XS + rk) = v;
     }
+  }
   __syncthreads();
 
 #pragma unroll
@@ -328,10 +345,10 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   store_block_bf16(acc, stage, Y + (size_t)mw * N + nw, (size_t)N, M - mw, N - nw, lane);
 }
 
-template <int RP, bool INT4>
+template <int RP, bool INT4, bool PANEL>
 static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
   const int tiles = (int)(((a.M + kTile - 1) / kTile) * ((a.N + kTile - 1) / kTile));
-  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4>), dim3(tiles), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL>), dim3(tiles), dim3(kThreads), 0, s,
                      (const uint16_t*)a.X, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (int)a.M, (int)a.N, (int)a.K,
                      (int)a.R, a.scale);
@@ -340,14 +357,22 @@ static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
-  if (int4) {
-    if (rp == 16) return launch_fwd_rp<16, true>(a, s);
-    if (rp == 32) return launch_fwd_rp<32, true>(a, s);
-    return launch_fwd_rp<64, true>(a, s);
+  if (rp == 64 && a.XA != nullptr) {
+    // the panel as a pass of its own into XA (its partials in Y, which the kernel then
+    // overwrites), then the kernel without the panel
+    const hipError_t e = launch_panel_xa(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A),
+                                         a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
+    if (e != hipSuccess) return e;
+    return int4 ? launch_fwd_rp<64, true, false>(a, s) : launch_fwd_rp<64, false, false>(a, s);
   }
-  if (rp == 16) return launch_fwd_rp<16, false>(a, s);
-  if (rp == 32) return launch_fwd_rp<32, false>(a, s);
-  return launch_fwd_rp<64, false>(a, s);
+  if (int4) {
+    if (rp == 16) return launch_fwd_rp<16, true, true>(a, s);
+    if (rp == 32) return launch_fwd_rp<32, true, true>(a, s);
+    return launch_fwd_rp<64, true, true>(a, s);
+  }
+  if (rp == 16) return launch_fwd_rp<16, false, true>(a, s);
+  if (rp == 32) return launch_fwd_rp<32, false, true>(a, s);
+  return launch_fwd_rp<64, false, true>(a, s);
 }
 
 }  // namespace lora

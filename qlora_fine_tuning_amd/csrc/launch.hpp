@@ -61,6 +61,10 @@ int panel_shares(int64_t M, int64_t C);
 size_t panel_workspace_bytes(int64_t M, int64_t N, int R);
 hipError_t launch_panel_g(const uint16_t* dY, const uint16_t* B, float* G, void* ws, int64_t M, int64_t N,
                           int R, hipStream_t s);
+// ranks 33..64 of a forward that keeps XA: XA = X A^T as a pass of its own, its partials in
+// `scratch` (the forward's Y, overwritten afterwards)
+hipError_t launch_panel_xa(const uint16_t* X, const uint16_t* A, float* XA, void* scratch, size_t scratch_bytes,
+                           int64_t M, int64_t K, int R, hipStream_t s);
 // input-gradient grid: output tiles, N ranges per tile, bytes of split partials (0 if unsplit)
 int dx_tiles(int64_t M, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K, int R);

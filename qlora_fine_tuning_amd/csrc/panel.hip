@@ -40,10 +40,11 @@ bt_transpose_kernel(const uint16_t* __restrict__ B, uint16_t* __restrict__ Bt, i
   }
 }
 
-// part[s][m][0..63] = sum over c in share s of Q[m][c] * S[r][c]  (Q: M x C, S: R x C, bf16)
+// out[s][m][r] = sum over c in share s of Q[m][c] * S[r][c]  (Q: M x C, S: R x C, bf16), rows
+// of ldo floats: 64 for partials, or R when one share writes the panel itself (ranks < R only)
 __global__ void __launch_bounds__(256)
 panel_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ S, float* __restrict__ part,
-             int M, int C, int R, int share) {
+             int M, int C, int R, int share, int ldo) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -79,9 +80,10 @@ panel_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ S, flo
   // acc[rb]: ranks rb*16 + 4 g4 .. +3 of token m0 + l16
   const int m = m0 + l16;
   if (m < M) {
-    float* dst = part + ((size_t)cs * M + m) * kPanelRanks;
+    float* dst = part + ((size_t)cs * M + m) * ldo;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) *reinterpret_cast<f32x4*>(dst + rb * 16 + 4 * g4) = acc[rb];
+    for (int rb = 0; rb < 4; ++rb)
+      if (rb * 16 + 4 * g4 < ldo) *reinterpret_cast<f32x4*>(dst + rb * 16 + 4 * g4) = acc[rb];
   }
 }
 
@@ -131,11 +133,36 @@ hipError_t launch_panel_g(const uint16_t* dY, const uint16_t* B, float* G, void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(panel_kernel, dim3((unsigned)((M + kPanelRows - 1) / kPanelRows), (unsigned)used), dim3(256), 0, s,
-                     dY, Bt, part, (int)M, (int)N, R, (int)len);
+                     dY, Bt, part, (int)M, (int)N, R, (int)len, kPanelRanks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = M * R;
   hipLaunchKernelGGL(panel_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, G,
+                     (int)M, R, used);
+  return hipGetLastError();
+}
+
+// XA = X A^T (A is R x K, already contiguous along k).  The per-share partials go to `scratch`
+// (scratch_bytes of it); with room for fewer than two shares, one share writes XA directly.
+hipError_t launch_panel_xa(const uint16_t* X, const uint16_t* A, float* XA, void* scratch, size_t scratch_bytes,
+                           int64_t M, int64_t K, int R, hipStream_t s) {
+  int shares = panel_shares(M, K);
+  const int64_t cap = (int64_t)(scratch_bytes / ((size_t)M * kPanelRanks * 4));
+  if (cap < 2) shares = 1;
+  shares = (int)std::min<int64_t>(shares, std::max<int64_t>(cap, 1));
+  const int64_t len = panel_share_len(K, shares);
+  const int used = (int)((K + len - 1) / len);
+  const dim3 grid((unsigned)((M + kPanelRows - 1) / kPanelRows), (unsigned)used);
+  if (used == 1) {
+    hipLaunchKernelGGL(panel_kernel, grid, dim3(256), 0, s, X, A, XA, (int)M, (int)K, R, (int)len, R);
+    return hipGetLastError();
+  }
+  float* part = static_cast<float*>(scratch);
+  hipLaunchKernelGGL(panel_kernel, grid, dim3(256), 0, s, X, A, part, (int)M, (int)K, R, (int)len, kPanelRanks);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = M * R;
+  hipLaunchKernelGGL(panel_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, XA,
                      (int)M, R, used);
   return hipGetLastError();
 }

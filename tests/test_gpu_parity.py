@@ -69,6 +69,7 @@ def test_f32_shapes(gpu_lib, M, N, K, R):
     (65, 512, 256, 16),
     (300, 192, 704, 64),
     (700, 1024, 1024, 16),
+    (300, 64, 2048, 64),    # rank 64, Y too small to hold the XA pass's partials: one share
 ])
 def test_bf16_shapes(gpu_lib, M, N, K, R):
     _say(f"case bf16 M={M} N={N} K={K} R={R}")
@@ -398,3 +399,26 @@ def test_qlora_decode_longest_k(gpu_lib):
     # workgroup that waits for their X A^T
     _say("case qlora decode M=4 N=64 K=2^20 R=16")
     check_qlora(gpu_lib, make_inputs(4, 64, 1 << 20, 16, seed=404, dtype="bf16", int4=True), sampled=False)
+
+
+@pytest.mark.parametrize("int4", [False, True])
+def test_rank64_forward_without_xa(gpu_lib, int4):
+    # a caller that does not keep XA: rank 64 then accumulates the panel inside the forward
+    # kernel (with XA kept, a pass of its own computes it first)
+    _say(f"case rank-64 forward without XA int4={int4}")
+    lora = gpu_lib
+    inp = make_inputs(300, 576, 1024, 64, seed=405, dtype="bf16", int4=int4)
+    X, A, B = (to_dev(inp, n) for n in ("X", "A", "B"))
+    x, a, b = (values(inp, n) for n in ("X", "A", "B"))
+    if int4:
+        Wq, Ws, packed, sref = quantize_both(lora, inp)
+        Y, XA = lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale, save_xa=False)
+        w = oracle.dequant_int4(packed, sref)
+    else:
+        W = to_dev(inp, "W")
+        Y, XA = lora.lora_fwd(X, W, A, B, inp.scale, save_xa=False)
+        w = values(inp, "W")
+    torch.cuda.synchronize()
+    assert XA is None
+    Yr, _ = oracle.lora_forward(x, w, a, b, inp.scale)
+    assert_close("Y", host(Y), Yr)
