@@ -72,13 +72,18 @@ typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
  * that adds the low-rank term in its epilogue, so no intermediate reaches HBM).
  *   X  [M][K], W [N][K], A [R][K], B [N][R]  of type `dt`     (inputs)
  *   Y  [M][N] of type `dt`                                     (output)
- *   XA [M][R] fp32, unscaled X A^T, or NULL to skip saving it   (output) */
+ *   XA [M][R] fp32, unscaled X A^T, or NULL to skip saving it   (output)
+ * For R > 32 (bf16) with XA given, X A^T is computed by a pass of its own ahead of the main
+ * kernel, which parks its partial sums in Y before overwriting Y; with XA NULL the main
+ * kernel computes it (correct, but slower at that rank). */
 lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                      const void* X, const void* W, const void* A, const void* B,
                      void* Y, float* XA, void* stream);
 
-/* Bytes of device workspace lora_bwd needs for these sizes (holds G and the per-token-tile
- * partial sums of dA and dB). */
+/* Bytes of device workspace lora_bwd needs for these sizes: G, the per-token-tile partial sums
+ * of dA and dB and, for bf16, the input gradient's split partials (when its output has few
+ * tiles) and, for R > 32, the scratch of its G = dY B pass.  The workspace needs no
+ * initialisation: calls clear what they use. */
 size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R);
 
 /* Backward with W frozen (tutorial ch. 5, §5.3, fused backward; hand-derived gradients):
