@@ -115,14 +115,14 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   // W (int4): thread t unpacks row t >> 2, columns (t & 3) * 64 .. +63 (one scale group).
   // A step's codes and raw fp16 scale stay in registers from their load to their unpacking
-  // into LDS: two sets alternating by step, loaded two steps ahead, at rank 16; one set loaded
-  // one step ahead for larger ranks (the two-set form of those instances crashes the compiler).
+  // into LDS: two sets alternating by step, loaded two steps ahead, at ranks up to 32; one set
+  // loaded one step ahead at rank 64 (an earlier form of that instance crashed the compiler).
   struct W4 {
     u32x4 q[2];
     uint32_t s;  // fp16 bits; converted when used, so the load is not waited for early
   };
   W4 w4a, w4b;
-  constexpr bool AHEAD = INT4 && RP == 16;
+  constexpr bool AHEAD = INT4 && RP <= 32;
   rsrc_t rWq, rWs;
   if constexpr (INT4) {
     rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + k0 / 2, (uint32_t)((size_t)N * (K / 2) - k0 / 2));
@@ -324,7 +324,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       finish(wn, bn);  // the register-staged parts of step st+1
     }
     wait_all();
-    if constexpr ((INT4 && RP > 16) || RP > 32) {  // (interleaved, these forms crash the compiler)
+    if constexpr (RP > 32) {  // rank 64: the copies in one burst (interleaved, they crashed the compiler)
       prefetch(st + 2, dc, wc, bc);
       if constexpr (INT4) load_w4(w4n, st + (AHEAD ? 3 : 2));  // after every copy
       phase(f1, f0, dn, wn, bn, 0, nocopy);
