@@ -115,14 +115,13 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   // W (int4): thread t unpacks row t >> 2, columns (t & 3) * 64 .. +63 (one scale group).
   // A step's codes and raw fp16 scale stay in registers from their load to their unpacking
-  // into LDS: two sets alternating by step, loaded two steps ahead, at ranks up to 32; one set
-  // loaded one step ahead at rank 64 (an earlier form of that instance crashed the compiler).
+  // into LDS: two sets alternating by step, loaded two steps ahead.
   struct W4 {
     u32x4 q[2];
     uint32_t s;  // fp16 bits; converted when used, so the load is not waited for early
   };
   W4 w4a, w4b;
-  constexpr bool AHEAD = INT4 && RP <= 32;
+  constexpr bool AHEAD = INT4;  // two register sets, two steps ahead
   rsrc_t rWq, rWs;
   if constexpr (INT4) {
     rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + k0 / 2, (uint32_t)((size_t)N * (K / 2) - k0 / 2));
@@ -138,10 +137,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   auto store_w4_part = [&](const W4& v, uint16_t* w, int d) {  // packed dword d of the 64 codes
     uint16_t* row = w + qblk * 4096 + qrow * 64;
-    const float sc = half_bits_to_f32((uint16_t)v.s);
-    if constexpr (RP <= 32) st16(row + ((d ^ wsw(qrow)) << 3), dequant8_mix(v.q[d >> 2][d & 3], i4mix(sc)));
-    else st16(row + ((d ^ wsw(qrow)) << 3), dequant8(v.q[d >> 2][d & 3], i4scale(sc)));  // (the fma form
-    // crashes the compiler at rank 64; both give the same bits)
+    st16(row + ((d ^ wsw(qrow)) << 3), dequant8_mix(v.q[d >> 2][d & 3], i4mix(half_bits_to_f32((uint16_t)v.s))));
   };
   auto store_w4 = [&](const W4& v, uint16_t* w) {
 #pragma unroll
@@ -207,14 +203,9 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // every row of the next phase uses all eight dY fragments: they go out in rows 0-3
-      // (ranks up to 32; this order crashes the compiler at rank 64)
-      if constexpr (RP <= 32) {
-        if (i < 4) {
-          nx.d[2 * i] = ld16(d + lds_offf(wm * 128 + 2 * i * 16 + l16, ch));
-          nx.d[2 * i + 1] = ld16(d + lds_offf(wm * 128 + (2 * i + 1) * 16 + l16, ch));
-        }
-      } else {
-        nx.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
+      if (i < 4) {
+        nx.d[2 * i] = ld16(d + lds_offf(wm * 128 + 2 * i * 16 + l16, ch));
+        nx.d[2 * i + 1] = ld16(d + lds_offf(wm * 128 + (2 * i + 1) * 16 + l16, ch));
       }
       nx.w[i] = wfrag(w, kk, i);
       __builtin_amdgcn_sched_barrier(0);
@@ -324,17 +315,11 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       finish(wn, bn);  // the register-staged parts of step st+1
     }
     wait_all();
-    if constexpr (RP > 32) {  // rank 64: the copies in one burst (interleaved, they crashed the compiler)
-      prefetch(st + 2, dc, wc, bc);
-      if constexpr (INT4) load_w4(w4n, st + (AHEAD ? 3 : 2));  // after every copy
-      phase(f1, f0, dn, wn, bn, 0, nocopy);
-    } else {
-      phase(f1, f0, dn, wn, bn, 0, [&](int q) {
-        prefetch_part(q, st + 2, dc, wc);
-        if constexpr (INT4)
-          if (q == 15) load_w4(w4n, st + 3);  // after every copy
-      });
-    }
+    phase(f1, f0, dn, wn, bn, 0, [&](int q) {
+      prefetch_part(q, st + 2, dc, wc);
+      if constexpr (INT4)
+        if (q == 15) load_w4(w4n, st + 3);  // after every copy
+    });
   };
   int st = 0;
   W4& w4odd = AHEAD ? w4b : w4a;  // the set of odd steps

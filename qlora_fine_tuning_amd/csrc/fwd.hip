@@ -89,9 +89,10 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     uint32_t s[2];  // fp16 bits; converted when used, so the load is not waited for early
   };
   W4 w4a, w4b;
-  // Two sets, loaded two steps ahead, at ranks up to 32; rank 64 uses one set loaded one step
-  // ahead (the two-set form of its panel instance crashes the compiler).
-  constexpr bool AHEAD = INT4 && RP <= 32;
+  // Two sets, loaded two steps ahead; the rank-64 instance with the panel in the kernel (the
+  // fallback for callers that do not keep XA) uses one set loaded one step ahead (its two-set
+  // form crashes the compiler).
+  constexpr bool AHEAD = INT4 && (RP <= 32 || !PANEL);
   rsrc_t rWq, rWs;
   if constexpr (INT4) {
     const int nrows = min(N - n0, kTile);
