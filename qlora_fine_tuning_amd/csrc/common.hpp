@@ -146,26 +146,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
 //   (1024 + u) s - 1032 s = (u - 8) s   or   (1024 + 16 u) (s / 16) - 72 s = (u - 8) s,
 // exact: every product and addend fits fp32 exactly (s has at most 11 significant bits), so
 // the fma returns q s itself, and one RNE pack per pair gives bf16_rne(q s): dequant8_mix.
-// 17 VALU operations per 8 codes; dequant8 below (an fma on byte-to-float conversions) takes 23
-// and gives the same bits.
-// The same values through byte-to-float conversions: q * s = fma(u, s, -8 s), exact (the
-// product has at most 14 significant bits).  The even codes sit in the low nibble of each
-// byte, the odd codes (times 16) in the high nibble.  Used by the input-gradient kernel.
-struct I4Scale {
-  float s, s_16, m8s;  // s, s / 16, -8 s  (all exact)
-};
-__device__ __forceinline__ I4Scale i4scale(float s) { return {s, s * 0.0625f, -8.f * s}; }
-__device__ __forceinline__ float ubyte(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xffu); }
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, const I4Scale& sc) {
-  const uint32_t x = w ^ 0x88888888u;
-  const uint32_t lo = x & 0x0f0f0f0fu, hi = x & 0xf0f0f0f0u;
-  u32x4 o;
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-    o[b] = pack_bf16(fmaf(ubyte(lo, b), sc.s, sc.m8s), fmaf(ubyte(hi, b), sc.s_16, sc.m8s));
-  return o;
-}
-
+// 17 VALU operations per 8 codes.
 struct I4Mix {
   float s, s16, c0, c1;  // s, s / 16, -1032 s, -72 s
 };
