@@ -31,8 +31,11 @@ namespace lora {
 // W tile in LDS: 4 blocks of 64 columns, each 64 rows (n) x 128 bytes; 16-byte chunk c of row
 // r sits in slot c ^ wsw(r).  A transposing read covers 4 consecutive rows x 32 bytes; wsw
 // separates rows r, r+2 (bit 1) and the row groups of neighbouring 16-lane groups (bit 3),
-// so those reads hit distinct banks.
-__device__ __forceinline__ int wsw(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+// so those reads hit distinct banks; bit 2 of the row (the same for the 4 rows of a read)
+// spreads the int4 path's 16-byte stores of 16 consecutive rows over 16 distinct bank groups.
+__device__ __forceinline__ int wsw(int r) {
+  return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1);
+}
 
 // Split partials cross XCDs, whose L2 caches are not coherent with each other: they are
 // written and read with device-scope (sc1) accesses, and every writer waits for its stores
@@ -113,7 +116,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       dma16(rW, dst + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffW,
             (uint32_t)n0 * rowW + (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
   };
-  // W (int4): thread t unpacks row t >> 2, columns (t & 3) * 64 .. +63 (one scale group).
+  // W (int4): each thread unpacks one row's 64 codes of one 64-column block (one scale group).
   // A step's codes and raw fp16 scale stay in registers from their load to their unpacking
   // into LDS: two sets alternating by step, loaded two steps ahead.
   struct W4 {
@@ -127,7 +130,11 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + k0 / 2, (uint32_t)((size_t)N * (K / 2) - k0 / 2));
     rWs = make_rsrc(Wscale + k0 / 64, (uint32_t)((size_t)N * (K / 64) - k0 / 64) * 2u);
   }
-  const int qrow = tid >> 2, qblk = tid & 3;
+  // lanes 16 b .. 16 b + 15 of wave w: rows 16 w .. 16 w + 15 of 64-column block b.  (With the
+  // four blocks of a row on four consecutive lanes, which the blocks' 8 KB spacing puts on the
+  // same LDS banks, the unpacked stores conflicted 4-way.)  A load instruction still reads 16
+  // rows x 128 contiguous bytes.
+  const int qrow = (tid & 15) + 16 * (tid >> 6), qblk = (tid >> 4) & 3;
   auto load_w4 = [&](W4& v, int stn) {
     const uint32_t r = (uint32_t)(nbase + min(stn, nsteps - 1) * kStep + qrow);
     const uint32_t vo = r * (uint32_t)(K / 2) + (uint32_t)qblk * 32u;
@@ -173,14 +180,17 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   if constexpr (ASM) mfma_acc_ready(acc);
 
   // transposing-read addresses: lane (l16, g4) reads rows 4 (l16 >> 2) + .. of its 16-lane
-  // group, columns 4 (l16 & 3) ..; per 16-column block q of a 64-column W block the chunk is
-  // 2q + ((l16 & 3) >> 1), swizzled by wsw of a row whose bits 1 and 3 are fixed per lane.
-  const int trow = g4 * 8 + (l16 >> 2);  // + kk * 32 + h * 4
-  const int tsw = wsw(trow);
-  int woff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    woff[q] = trow * 64 + (((2 * q + ((l16 & 3) >> 1)) ^ tsw) << 3) + (l16 & 1) * 4;
+  // group (and the 4 rows after them), columns 4 (l16 & 3) ..; per 16-column block q of a
+  // 64-column W block the chunk is 2q + ((l16 & 3) >> 1), swizzled by wsw of a row whose bits
+  // 1..3 are fixed per lane (bit 2 flips for the second read).
+  const int trow = g4 * 8 + (l16 >> 2);  // + kk * 32 (+ 4)
+  // chunk 2q + x (x = (l16 & 3) >> 1) sits in slot (2q + x) ^ wsw(trow) = 2 (q ^ t2) + x, since
+  // bit 0 of wsw(trow) is 0 (bit 2 of trow is 0): offset wbase + 16 (q ^ t2), q known at
+  // compile time.  The rows 4 further on have bit 0 of the slot flipped: + woff4d.
+  const int t2 = wsw(trow) >> 1;
+  const int wbase = trow * 64 + (((l16 & 3) >> 1) << 3) + (l16 & 1) * 4;
+  const int woff4d = 4 * 64 + ((((l16 & 3) >> 1) & 1) ? -8 : 8);
+  auto woff = [&](int q) { return wbase + ((q ^ t2) << 4); };
   const int boff = trow * RP + (l16 & 3) * 4;
 
   struct Frag {
@@ -188,8 +198,9 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   auto wfrag = [&](const uint16_t* w, int kk, int i) -> u32x4 {
     const int kb = wk * 8 + i;  // 16-column block within the 256-column tile
-    const uint16_t* p = w + (kb >> 2) * 4096 + kk * 32 * 64 + woff[kb & 3];
-    return join(ld_tr(p), ld_tr(p + 4 * 64));
+    const uint16_t* p = w + (kb >> 2) * 4096 + kk * 32 * 64;
+    const int o = woff(kb & 3);
+    return join(ld_tr(p + o), ld_tr(p + o + woff4d));
   };
   auto bfrag = [&](const uint16_t* b, int kk, int c) -> u32x4 {
     const uint16_t* p = b + kk * 32 * RP + boff + c * 16;
