@@ -140,48 +140,35 @@ dadb_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__
 }
 
 // dA[rank][k] = scale * sum_s partA[s][rank][k];  dB[n][rank] = scale * sum_s partB[s][rank][n].
-// Each thread produces four outputs (dA: four consecutive k; dB: four consecutive ranks of one
-// n) and adds the splits in split order; the split loads are independent, so eight are kept in
-// flight at a time.
+// One output per thread, consecutive threads on consecutive k (dA) or n (dB), so every split's
+// loads are coalesced (dB is stored transposed, a small scattered write); the splits are added
+// in split order, eight loads in flight at a time.
 __global__ void __launch_bounds__(256)
 dadb_reduce_kernel(const float* __restrict__ partA, const float* __restrict__ partB,
                    float* __restrict__ dA, float* __restrict__ dB, int N, int K, int R,
                    int splits, float scale) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nA = (int64_t)R * K, nB = (int64_t)R * N;
-  const int64_t tA = nA / 4, tB = nB / 4;
-  if (t < tA) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(partA) + t;
-    f32x4 s = fzero4();
-    int sp = 0;
-    for (; sp + 8 <= splits; sp += 8) {
-      f32x4 v[8];
+  const bool isA = t < nA;
+  if (!isA && t >= nA + nB) return;
+  const int64_t e = isA ? t : t - nA;       // A: rank * K + k;  B: rank * N + n
+  const float* src = (isA ? partA : partB) + e;
+  const int64_t stride = isA ? nA : nB;
+  float s = 0.f;
+  int sp = 0;
+  for (; sp + 8 <= splits; sp += 8) {
+    float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(sp + u) * tA];
+    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(sp + u) * stride];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
-    }
-    for (; sp < splits; ++sp) s += src[(int64_t)sp * tA];
-    reinterpret_cast<f32x4*>(dA)[t] = scale * s;
-  } else if (t < tA + tB) {
-    const int64_t j = t - tA;
-    const int rq = (int)(j % (R / 4)), n = (int)(j / (R / 4));  // ranks 4 rq .. +3 of row n
-    const float* src = partB + (int64_t)(4 * rq) * N + n;
-    f32x4 s = fzero4();
-    int sp = 0;
-    for (; sp + 4 <= splits; sp += 4) {
-      f32x4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[u][e] = src[(int64_t)(sp + u) * nB + (int64_t)e * N];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) s += v[u];
-    }
-    for (; sp < splits; ++sp)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] += src[(int64_t)sp * nB + (int64_t)e * N];
-    reinterpret_cast<f32x4*>(dB + (int64_t)n * R)[rq] = scale * s;
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; sp < splits; ++sp) s += src[(int64_t)sp * stride];
+  if (isA) {
+    dA[e] = scale * s;
+  } else {
+    const int64_t r = e / N, n = e - r * N;
+    dB[n * R + r] = scale * s;
   }
 }
 
@@ -203,7 +190,7 @@ hipError_t launch_dadb_partials_bf16(const DadbArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dadb_reduce(const DadbArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)a.R * (a.K + a.N) / 4;  // four outputs per thread
+  const int64_t total = (int64_t)a.R * (a.K + a.N);  // one output per thread
   const int blocks = (int)((total + 255) / 256);
   hipLaunchKernelGGL(dadb_reduce_kernel, dim3(blocks), dim3(256), 0, s, a.partA, a.partB, a.dA, a.dB,
                      (int)a.N, (int)a.K, a.R, a.splits, a.scale);
