@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint32_t sS2[4 * 64];
   __shared__ __align__(16) uint32_t sTok[4 * 64];  // each wave's latest read of the ready token
   __shared__ __align__(16) float sXaf[2 * 256];     // XA_f [M][RP] as last read by waves 0 and 1
-  __shared__ __align__(16) uint32_t sJunk[2 * 64];  // waves 2 and 3: destination of a dummy load
+  __shared__ __align__(16) uint32_t sJunk[4 * 64];  // destination of the empty loads
   __shared__ int sflag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -268,6 +268,7 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) bpre[v][c] = (8 * c < a.R) ? ld16(a.B + (size_t)(n + v) * a.R + 8 * c) : zero4();
   }
+  uint32_t seen = 0, fresh = 0;  // fresh: an XA_f read was issued after the token was seen
   // Step st of this workgroup into stage (sW, sX, sS): per wave 2 + 4 + 2 + 1 loads straight
   // to LDS, the first two device-coherent reads of the tile's ready token and of XA_f.  Steps >= NST read past every buffer's end (zeros, no memory traffic) so that every
   // wave always has the same number of loads in flight.  The loads are issued as inline asm,
@@ -277,12 +278,13 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
   auto issue = [&](uint8_t* sW, uint8_t* sX, uint32_t* sS, int st) {
     const uint32_t oob = st < NST ? 0u : 0x40000000u;
     dma4_dev_asm(rC, sTok + w * 64, vTok);
-    // XA_f, read every step by waves 0 and 1 (1 KB each, device-coherent); it is valid once a
-    // read was issued after the wave had seen the token
-    if (w < 2)
+    // XA_f (1 KB for each of waves 0 and 1, device-coherent), read once, at the first step after
+    // the wave has seen the token; every other step issues an empty load in its place (the
+    // condition is taken wave-uniform so that exactly one load is issued either way)
+    if (w < 2 && __builtin_amdgcn_readfirstlane(seen && !fresh))
       dma16_dev_asm(rF, sXaf + w * 256, (uint32_t)(w * 1024 + lane * 16));
     else
-      dma4_asm(rF, sJunk + (w - 2) * 64, 0x40000000u);
+      dma4_asm(rF, sJunk + w * 64, 0x40000000u);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 4 * q + rq;
@@ -322,7 +324,6 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
   // wave is done with the stage that is refilled next
   auto step_sync = []() { asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  uint32_t seen = 0, fresh = 0;  // fresh: an XA_f read was issued after the token was seen
   sTok[w * 64 + lane] = 0u;  // read before the first token load lands (same wave: ordered)
   issue(sW0, sX0, sS0, 0);
   issue(sW1, sX1, sS1, 1);
