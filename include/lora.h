@@ -80,10 +80,12 @@ lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
                      const void* X, const void* W, const void* A, const void* B,
                      void* Y, float* XA, void* stream);
 
-/* Bytes of device workspace lora_bwd needs for these sizes: G, the per-token-tile partial sums
- * of dA and dB and, for bf16, the input gradient's split partials (when its output has few
- * tiles) and, for R > 32, the scratch of its G = dY B pass.  The workspace needs no
- * initialisation: calls clear what they use. */
+/* Bytes of device workspace lora_bwd needs for these sizes: G; the partial sums of dA and dB,
+ * one per split of the tokens (256 tokens per split for fp32; for bf16, 256 doubled while the
+ * partial pass keeps at least 512 workgroups, one per 256 columns of K + N per split, and at
+ * most 2048); for bf16, the input gradient's split partials (when its output has few tiles);
+ * and, for R > 32, the scratch of its G = dY B pass.  The workspace needs no initialisation:
+ * calls clear what they use. */
 size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R);
 
 /* Backward with W frozen (tutorial ch. 5, §5.3, fused backward; hand-derived gradients):

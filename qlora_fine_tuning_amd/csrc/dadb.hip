@@ -18,12 +18,14 @@
 
 namespace lora {
 
+static_assert(kDadbCols == kTile, "the host sizes the partial pass's grid with the tile width");
+
 template <int RP>
 __global__ void __launch_bounds__(kThreads)
 dadb_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY,
                     const float* __restrict__ G, const float* __restrict__ XA,
                     float* __restrict__ partA, float* __restrict__ partB,
-                    int M, int N, int K, int R, int tilesA) {
+                    int M, int N, int K, int R, int tilesA, int split_rows) {
   constexpr int TT = kTile * kStep;
   constexpr int PT = RP * kStep;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TT + 4 * PT];
@@ -37,8 +39,8 @@ dadb_partial_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__
   float* const part = jobA ? partA : partB;
   const int C = jobA ? K : N;
   const int c0 = (jobA ? (int)blockIdx.x : (int)blockIdx.x - tilesA) * kTile;
-  const int mbeg = (int)blockIdx.y * (int)kSplitRows;
-  const int mend = min(M, mbeg + (int)kSplitRows);
+  const int mbeg = (int)blockIdx.y * split_rows;
+  const int mend = min(M, mbeg + split_rows);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -178,7 +180,7 @@ static hipError_t launch_partials_rp(const DadbArgs& a, hipStream_t s) {
   const int tilesB = (int)((a.N + kTile - 1) / kTile);
   hipLaunchKernelGGL((dadb_partial_kernel<RP>), dim3(tilesA + tilesB, a.splits), dim3(kThreads), 0, s,
                      (const uint16_t*)a.X, (const uint16_t*)a.dY, a.G, a.XA, a.partA, a.partB,
-                     (int)a.M, (int)a.N, (int)a.K, a.R, tilesA);
+                     (int)a.M, (int)a.N, (int)a.K, a.R, tilesA, a.split_rows);
   return hipGetLastError();
 }
 

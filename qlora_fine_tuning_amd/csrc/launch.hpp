@@ -6,8 +6,10 @@
 
 namespace lora {
 
-// Rows of tokens reduced by one split of the token-dimension (split-K) dA / dB sums.
+// Rows of tokens reduced by one split of the token-dimension (split-K) dA / dB sums on the fp32
+// path, and the shortest split of the bf16 / int4 path (which may double it).
 constexpr int64_t kSplitRows = 256;
+constexpr int64_t kDadbCols = 256;  // columns (k or n) per workgroup of the dA / dB partial pass
 
 struct FwdArgs {
   const void* X;
@@ -50,6 +52,7 @@ struct DadbArgs {
   int R;
   float scale;
   int splits;
+  int split_rows;  // tokens per split (the last split may be shorter)
 };
 
 // bf16 / int4 MFMA paths

@@ -46,7 +46,20 @@ lora_status from_hip(hipError_t e) {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-int64_t splits_for(int64_t M) { return (M + kSplitRows - 1) / kSplitRows; }
+// Tokens per split of the dA/dB partial pass: 256 on the fp32 path; the bf16 / int4 path
+// doubles it while the grid keeps at least 512 workgroups, the number resident at once (two per
+// CU): longer-lived workgroups, fewer partials to write and add.
+int64_t dadb_split_rows(int64_t M, int64_t N, int64_t K, bool mfma) {
+  int64_t rows = kSplitRows;
+  if (!mfma) return rows;
+  const int64_t tiles = (K + kDadbCols - 1) / kDadbCols + (N + kDadbCols - 1) / kDadbCols;
+  while (rows < 2048 && tiles * ((M + 2 * rows - 1) / (2 * rows)) >= 512) rows *= 2;
+  return rows;
+}
+int64_t splits_for(int64_t M, int64_t N, int64_t K, bool mfma) {
+  const int64_t rows = dadb_split_rows(M, N, K, mfma);
+  return (M + rows - 1) / rows;
+}
 
 // Backward workspace: G [M][R] fp32 | partA [splits][R][K] fp32 | partB [splits][R][N] fp32,
 // then, for an MFMA (bf16 / int4) input gradient whose N is split, its per-tile arrival
@@ -56,7 +69,7 @@ struct BwdLayout {
   size_t g, pa, pb, ctr, dxp, pan, total;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t R, bool mfma) {
-  const int64_t s = splits_for(M);
+  const int64_t s = splits_for(M, N, K, mfma);
   BwdLayout l;
   l.g = 0;
   l.pa = align256((size_t)M * R * sizeof(float));
@@ -108,7 +121,8 @@ lora_status bwd_dadb_common(lora_dtype dt, int64_t M, int64_t N, int64_t K, int3
   char* base = static_cast<char*>(ws);
   DadbArgs d{X, dY, reinterpret_cast<const float*>(base + lay.g), XA,
              reinterpret_cast<float*>(base + lay.pa), reinterpret_cast<float*>(base + lay.pb),
-             dA, dB, M, N, K, R, scale, (int)splits_for(M)};
+             dA, dB, M, N, K, R, scale, (int)splits_for(M, N, K, dt != LORA_F32),
+             (int)dadb_split_rows(M, N, K, dt != LORA_F32)};
   if (M > 0) {
     const hipError_t e = (dt == LORA_F32) ? launch_dadb_partials_f32(d, s) : launch_dadb_partials_bf16(d, s);
     if (e != hipSuccess) return from_hip(e);

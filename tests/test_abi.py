@@ -96,12 +96,15 @@ def test_lora_bwd_validation(lib, kw, code):
 
 
 def test_workspace_sizes(lib):
-    # G (M x R fp32) + split partials of dA and dB, one split per 256 tokens
+    # G (M x R fp32) + split partials of dA and dB.  fp32: one split per 256 tokens.  bf16: the
+    # split length doubles from 256 while the partial pass keeps 512 workgroups (one per 256
+    # columns of K + N per split): 32 column tiles here, so 512-token splits (16 x 32 = 512).
     M, N, K, R = 8192, 4096, 4096, 16
+    for dt, splits in ((0, M // 256), (1, M // 512)):
+        need = lib.lora_bwd_workspace_bytes(dt, M, N, K, R)
+        assert need >= 4 * (M * R + splits * R * (K + N)), dt
+        assert need < 4 * (M * R + splits * R * (K + N)) + 3 * 256, dt
     need = lib.lora_bwd_workspace_bytes(1, M, N, K, R)
-    splits = M // 256
-    assert need >= 4 * (M * R + splits * R * (K + N))
-    assert need < 4 * (M * R + splits * R * (K + N)) + 3 * 256
     assert lib.lora_bwd_workspace_bytes(1, M, N, K, 12) == 0  # invalid rank
     assert lib.qlora_bwd_workspace_bytes(M, N, K, R) == need
     # the decode path keeps split partial sums; the large-M path needs none

@@ -76,10 +76,19 @@ def test_bf16_shapes(gpu_lib, M, N, K, R):
     check_full(gpu_lib, make_inputs(M, N, K, R, seed=200 + M + R, dtype="bf16"))
 
 
+def _dadb_split_rows(M, N, K):
+    # tokens per dA / dB split on the bf16 path: 256, doubled while 512 workgroups remain
+    rows, tiles = 256, -(-K // 256) + -(-N // 256)
+    while rows < 2048 and tiles * -(-M // (2 * rows)) >= 512:
+        rows *= 2
+    return rows
+
+
 def _unsplit_ws_bytes(M, N, K, R):
-    # G + the dA / dB split partials (256-token splits), each region padded to 256 bytes
+    # G + the dA / dB split partials, each region padded to 256 bytes
     pad = lambda b: (b + 255) // 256 * 256
-    s = (M + 255) // 256
+    rows = _dadb_split_rows(M, N, K)
+    s = (M + rows - 1) // rows
     return pad(4 * M * R) + pad(4 * s * R * K) + pad(4 * s * R * N)
 
 
@@ -389,7 +398,9 @@ def test_bf16_longest_n(gpu_lib):
 
 
 def test_bf16_many_tokens(gpu_lib):
-    # 2^18 + 37 tokens: 1025 token splits of the dA / dB sums, a ragged last token tile
+    # 2^18 + 37 tokens: 257 token splits of 1024 for the dA / dB sums (two column tiles, so the
+    # split length grows to 1024), a ragged last split and token tile
+    assert _dadb_split_rows((1 << 18) + 37, 256, 256) == 1024
     _say("case bf16 M=2^18+37 N=256 K=256 R=8")
     check_sampled(gpu_lib, make_inputs((1 << 18) + 37, 256, 256, 8, seed=403, dtype="bf16"))
 
