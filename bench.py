@@ -170,6 +170,39 @@ def bench_qlora_ffn(lora, torch, dev, reps):
             "TFLOP/s": round(fl / ms / 1e9, 2), "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
+def bench_mlp(lora, torch, dev, reps):
+    """The MLP projections of the same layer type (bf16): gate/up K=4096 -> N=14336 and down
+    K=14336 -> N=4096, M=8192, r=16; fwd+bwd TFLOP/s of each."""
+    from qlora_fine_tuning_amd.workloads import workload_inputs
+
+    out = []
+    for name in ("mlp_gate_up", "mlp_down"):
+        inp = workload_inputs(name)
+        M, N, K, R = inp.M, inp.N, inp.K, inp.R
+        X, W, A, B, dY = (dev_bits(getattr(inp, n), dev) for n in ("X", "W", "A", "B", "dY"))
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        XA = torch.empty(M, R, dtype=torch.float32, device=dev)
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        dA = torch.empty(R, K, dtype=torch.float32, device=dev)
+        dB = torch.empty(N, R, dtype=torch.float32, device=dev)
+        ws = torch.empty(lora.lora_bwd_workspace_bytes(lora.LORA_BF16, M, N, K, R), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream()
+
+        def step():
+            lora.lora_fwd(X, W, A, B, inp.scale, Y=Y, XA=XA, stream=stream)
+            lora.lora_bwd(dY, X, W, A, B, XA, inp.scale, dX=dX, dA=dA, dB=dB, ws=ws, stream=stream)
+
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        ms = event_time_ms(step, reps, stream)
+        fl = lora_flops(M, N, K, R)
+        out.append({"workload": name, "M": M, "N": N, "K": K, "r": R, "ms_per_step": round(ms, 4),
+                    "TFLOP/s": round(fl / ms / 1e9, 2), "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)})
+        del X, W, A, B, dY, Y, XA, dX, dA, dB, ws
+    return out
+
+
 def bench_decode(lora, torch, dev, reps, copies=6):
     """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL)."""
     from qlora_fine_tuning_amd.workloads import workload_inputs
@@ -306,7 +339,8 @@ def main(argv=None):
         "roofline": roofline,
     }
     if not args.no_secondary:
-        result["secondary"] = {"qlora": bench_qlora_ffn(lora, torch, dev, 20),
+        result["secondary"] = {"mlp": bench_mlp(lora, torch, dev, 20),
+                               "qlora": bench_qlora_ffn(lora, torch, dev, 20),
                                "decode": bench_decode(lora, torch, dev, 20),
                                "torch_unfused": bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}
     if args.calib_copy:
