@@ -512,13 +512,17 @@ int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((
 // Number of N ranges of the input-gradient grid: the count that minimises the estimated time
 // (rounds of 256 resident workgroups x steps per unit, a split costing about 4 steps for its
 // partial), with at least 8 steps per unit and at most 8 ranges.
+// Split of N: cost in tile-steps (x 256) = rounds x steps per unit, plus the units' partials:
+// each stores 256 KB of fp32 and the tile's last unit reads them back, which costs about 40
+// tile-steps per unit on each CU (measured on the QLoRA FFN input gradient, 320 tiles x 432
+// steps: S = 2, 3, 4, 8 took 1.13, 1.09, 1.15, 1.73 ms; a flat 4 steps per unit chose 4).
 int dx_splits(int64_t M, int64_t N, int64_t K, int R) {
   const int64_t tiles = dx_tiles(M, K), steps = N / kStep;
   int best = 1;
   (void)R;
-  int64_t best_cost = ((tiles + 255) / 256) * steps;
+  int64_t best_cost = ((tiles + 255) / 256) * steps * 256;
   for (int64_t s = 2; s <= 8 && steps / s >= 8; ++s) {
-    const int64_t cost = ((tiles * s + 255) / 256) * ((steps + s - 1) / s + 4);
+    const int64_t cost = ((tiles * s + 255) / 256) * ((steps + s - 1) / s) * 256 + 40 * tiles * s;
     if (cost < best_cost) best = (int)s, best_cost = cost;
   }
   return best;
