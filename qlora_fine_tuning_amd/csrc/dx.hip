@@ -364,6 +364,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     // partial slot: [wave][acc block][lane] f32x4, then (with a panel) the G panel [wave][block][lane]
     constexpr uint32_t kAccBytes = 4 * 64 * 64 * 16, kPanBytes = PANEL ? 4 * (RP / 16) * 4 * 64 * 16 : 0;
     constexpr uint32_t kSlot = kAccBytes + kPanBytes;
+    static_assert(kSlot == dx_slot_bytes(RP), "the host sizes the partials with dx_slot_bytes");
     const rsrc_t rP = make_rsrc(part + (size_t)tile * splits * (kSlot / 4), (uint32_t)splits * kSlot);
     const uint32_t wa = ((uint32_t)wave * 64 * 64 + lane) * 16u;
     const uint32_t wp = kAccBytes + ((uint32_t)wave * (RP / 16) * 4 * 64 + lane) * 16u;
@@ -505,35 +506,6 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
 __global__ void zero_u32_kernel(uint32_t* p, int n) {  // the split arrival counters
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
-}
-
-int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile)); }
-
-// Number of N ranges of the input-gradient grid: the count that minimises the estimated time
-// (rounds of 256 resident workgroups x steps per unit, a split costing about 4 steps for its
-// partial), with at least 8 steps per unit and at most 8 ranges.
-// Split of N: cost in tile-steps (x 256) = rounds x steps per unit, plus the units' partials:
-// each stores 256 KB of fp32 and the tile's last unit reads them back, which costs about 40
-// tile-steps per unit on each CU (measured on the QLoRA FFN input gradient, 320 tiles x 432
-// steps: S = 2, 3, 4, 8 took 1.13, 1.09, 1.15, 1.73 ms; a flat 4 steps per unit chose 4).
-int dx_splits(int64_t M, int64_t N, int64_t K, int R) {
-  const int64_t tiles = dx_tiles(M, K), steps = N / kStep;
-  int best = 1;
-  (void)R;
-  int64_t best_cost = ((tiles + 255) / 256) * steps * 256;
-  for (int64_t s = 2; s <= 8 && steps / s >= 8; ++s) {
-    const int64_t cost = ((tiles * s + 255) / 256) * ((steps + s - 1) / s) * 256 + 40 * tiles * s;
-    if (cost < best_cost) best = (int)s, best_cost = cost;
-  }
-  return best;
-}
-
-size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R) {
-  const int s = dx_splits(M, N, K, R);
-  if (s == 1) return 0;
-  const int rp = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
-  const size_t panel = rp <= 32 ? (size_t)4 * (rp / 16) * 4 * 64 * 16 : 0;  // rank 64: G from its own pass
-  return (size_t)dx_tiles(M, K) * s * ((size_t)4 * 64 * 64 * 16 + panel);
 }
 
 template <int RP, bool INT4>

@@ -68,6 +68,11 @@ hipError_t launch_panel_g(const uint16_t* dY, const uint16_t* B, float* G, void*
 // `scratch` (the forward's Y, overwritten afterwards)
 hipError_t launch_panel_xa(const uint16_t* X, const uint16_t* A, float* XA, void* scratch, size_t scratch_bytes,
                            int64_t M, int64_t K, int R, hipStream_t s);
+// Bytes of one split partial of the input-gradient kernel: its 256 x 256 fp32 tile in MFMA
+// fragment order (4 waves x 64 blocks x 1 KB) and, for ranks up to 32, its G panel.
+constexpr size_t dx_slot_bytes(int rp) {
+  return (size_t)4 * 64 * 64 * 16 + (rp <= 32 ? (size_t)4 * (rp / 16) * 4 * 64 * 16 : 0);
+}
 // input-gradient grid: output tiles, N ranges per tile, bytes of split partials (0 if unsplit)
 int dx_tiles(int64_t M, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K, int R);
