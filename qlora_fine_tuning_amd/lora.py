@@ -291,3 +291,21 @@ class LoRALinearFunction(torch.autograd.Function):
         X, W, A, B, XA = ctx.saved_tensors
         dX, dA, dB = lora_bwd(dY.contiguous(), X, W, A, B, XA, ctx.scale)
         return dX, None, dA.to(A.dtype), dB.to(B.dtype), None
+
+
+class QLoRALinearFunction(torch.autograd.Function):
+    """Autograd wrapper for the int4 base weight: Wq and Ws are frozen (no gradient), the forward
+    saves X A^T (fp32) for the backward, and A, B receive their gradients in their own dtype."""
+
+    @staticmethod
+    def forward(ctx, X, Wq, Ws, A, B, scale):
+        Y, XA = qlora_fwd(X, Wq, Ws, A, B, scale)
+        ctx.save_for_backward(X, Wq, Ws, A, B, XA)
+        ctx.scale = scale
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, Wq, Ws, A, B, XA = ctx.saved_tensors
+        dX, dA, dB = qlora_bwd(dY.contiguous(), X, Wq, Ws, A, B, XA, ctx.scale)
+        return dX, None, None, dA.to(A.dtype), dB.to(B.dtype), None
