@@ -112,6 +112,22 @@ def test_workspace_sizes(lib):
     assert lib.qlora_fwd_workspace_bytes(4096, 27648, 5120, 16) == 0
 
 
+def test_workspace_plan_qlora_ffn(lib):
+    # M=4096, N=27648, K=5120, R=16 (bf16 / int4 backward), region by region, each 256-byte
+    # aligned: G; dA / dB partials over 4 token splits of 1024 (128 column tiles: 256 tokens
+    # doubled while 512 workgroups remain); one arrival counter per dX output tile (16 x 20);
+    # the dX split partials: N cut into 3 ranges (the cost model's choice for 320 tiles of 432
+    # steps), each slot a 256 x 256 fp32 tile plus a rank-16 G panel.
+    M, N, K, R = 4096, 27648, 5120, 16
+    pad = lambda b: (b + 255) // 256 * 256
+    splits, tiles, n_split = 4, 16 * 20, 3
+    slot = 4 * 64 * 64 * 16 + 4 * 1 * 4 * 64 * 16
+    want = (pad(4 * M * R) + pad(4 * splits * R * K) + pad(4 * splits * R * N) + pad(4 * tiles)
+            + pad(tiles * n_split * slot))
+    assert lib.lora_bwd_workspace_bytes(1, M, N, K, R) == want
+    assert lib.qlora_bwd_workspace_bytes(M, N, K, R) == want
+
+
 def test_split_backward_validation(lib):
     need = lib.lora_bwd_workspace_bytes(1, 64, 256, 256, 16)
     assert lib.lora_bwd_dx(1, 64, 256, 256, 16, 2.0, P, P, P, P, NUL, P, need, None) == 1
