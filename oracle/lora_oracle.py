@@ -19,6 +19,10 @@ Sources are the web pages on Unsloth.  They are cited by page title and section:
   "if trained", and here W is frozen) and the hand-derived-backward section of
   the wisestudy.cn Unsloth essay.  The gradients below are derived by hand from
   the loss convention ``L = <dY, Y>_F``.
+* SwiGLU gate/up pair: tutorial ch. 5 §5.6 "fused SwiGLU",
+  ``SwiGLU(x) = (W_g x ⊙ σ(W_g x)) ⊙ W_u x`` (σ the logistic function; the output
+  projection W_d is another linear layer), with §5.3's LoRA update on the gate and
+  on the up projection; gradients derived by hand from ``L = <dH, H>_F``.
 * 4-bit weights: "探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3
   (4-bit weights read compactly, unpacked in registers by a scaling coefficient,
   restored to FP16/BF16 before the matrix units).  The concrete format (symmetric
@@ -210,3 +214,66 @@ def lora_backward_dx_rows(dY, W, A, B, scale, rows):
     rows = np.asarray(rows)
     dYr, W, A, B = _f64(np.asarray(dY)[rows], W, A, B)
     return dYr @ W + float(scale) * ((dYr @ B) @ A)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU gate/up pair with LoRA on both projections
+# (tutorial ch. 5 §5.6, fused SwiGLU: SwiGLU(x) = (W_g x ⊙ σ(W_g x)) ⊙ W_u x, the output
+# projection W_d being a separate linear layer; §5.3's LoRA update on the gate and the up
+# projection; gradients derived by hand from L = <dH, H>_F)
+# ---------------------------------------------------------------------------
+
+
+def sigmoid(g):
+    """Logistic function 1 / (1 + exp(-g)) in float64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):  # exp(-g) = inf for g < -709 gives exactly 0
+        return 1.0 / (1.0 + np.exp(-g))
+
+
+def silu(g):
+    """g * sigmoid(g): the gate's activation in §5.6's SwiGLU."""
+    g = np.asarray(g, dtype=np.float64)
+    return g * sigmoid(g)
+
+
+def silu_grad(g):
+    """d silu / d g = sigmoid(g) * (1 + g * (1 - sigmoid(g)))."""
+    g = np.asarray(g, dtype=np.float64)
+    s = sigmoid(g)
+    return s * (1.0 + g * (1.0 - s))
+
+
+def swiglu_lora_forward(X, Wg, Wu, Ag, Au, Bg, Bu, scale):
+    """H = silu(G) ⊙ U with G = X Wg^T + scale (X Ag^T) Bg^T and U likewise with Wu, Au, Bu.
+
+    X: M x K; Wg, Wu: N x K; Ag, Au: R x K; Bg, Bu: N x R.
+    Returns (H, G, U, XAg, XAu), float64: H, G, U are M x N, XAg, XAu are M x R.
+    """
+    G, xag = lora_forward(X, Wg, Ag, Bg, scale)
+    U, xau = lora_forward(X, Wu, Au, Bu, scale)
+    return silu(G) * U, G, U, xag, xau
+
+
+def swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, scale):
+    """Gradients of L = <dH, H>_F with Wg, Wu frozen.
+
+    dU = dH ⊙ silu(G),  dG = dH ⊙ U ⊙ silu'(G), then the LoRA backward of each projection:
+    dX = dXg + dXu; returns (dX, dAg, dAu, dBg, dBu).
+    """
+    dH = np.asarray(dH, dtype=np.float64)
+    G, _ = lora_forward(X, Wg, Ag, Bg, scale)
+    U, _ = lora_forward(X, Wu, Au, Bu, scale)
+    dU = dH * silu(G)
+    dG = dH * U * silu_grad(G)
+    dXg, dAg, dBg = lora_backward(dG, X, Wg, Ag, Bg, scale)
+    dXu, dAu, dBu = lora_backward(dU, X, Wu, Au, Bu, scale)
+    return dXg + dXu, dAg, dAu, dBg, dBu
+
+
+def swiglu_lora_rows(X, Wg, Wu, Ag, Au, Bg, Bu, scale, rows):
+    """Rows ``rows`` of (H, G, U) (for full-size sampling)."""
+    rows = np.asarray(rows)
+    G, _ = lora_forward_rows(X, Wg, Ag, Bg, scale, rows)
+    U, _ = lora_forward_rows(X, Wu, Au, Bu, scale, rows)
+    return silu(G) * U, G, U

@@ -358,3 +358,102 @@ def test_qlora_forward_uses_dequantised_weight():
             ex = sum(Xf[m][k] * (Wf[n][k] + 2 * sum(Bf[n][i] * Af[i][k] for i in range(R)))
                      for k in range(K))
             assert abs(Y[m, n] - float(ex)) <= 1e-12 * max(1.0, abs(float(ex)))
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU gate/up pair with LoRA (tutorial ch. 5 §5.6)
+# ---------------------------------------------------------------------------
+
+def test_silu_closed_forms():
+    # sigmoid(0) = 1/2, sigmoid(x) + sigmoid(-x) = 1; silu(0) = 0, silu'(0) = 1/2;
+    # silu(g) -> g and silu'(g) -> 1 for large g, silu(g) -> 0 for very negative g;
+    # silu(ln 3) = ln(3) * 3/4 exactly in the reals (sigmoid(ln 3) = 3/4)
+    x = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(oracle.sigmoid(x) + oracle.sigmoid(-x), 1.0, rtol=0, atol=1e-15)
+    assert oracle.sigmoid(0.0) == 0.5 and oracle.silu(0.0) == 0.0 and oracle.silu_grad(0.0) == 0.5
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12 and abs(oracle.silu_grad(40.0) - 1.0) < 1e-12
+    assert oracle.silu(-800.0) == 0.0
+    assert abs(oracle.silu(np.log(3.0)) - 0.75 * np.log(3.0)) < 1e-15
+    # derivative of silu against a central difference of silu itself
+    g = np.linspace(-8, 8, 33)
+    h = 1e-5
+    fd = (oracle.silu(g + h) - oracle.silu(g - h)) / (2 * h)
+    np.testing.assert_allclose(oracle.silu_grad(g), fd, rtol=0, atol=1e-9)
+
+
+def _swiglu_case(rng, M, K, N, R):
+    X = rng.standard_normal((M, K))
+    Wg, Wu = rng.standard_normal((N, K)) / np.sqrt(K), rng.standard_normal((N, K)) / np.sqrt(K)
+    Ag, Au = rng.uniform(-0.3, 0.3, (R, K)), rng.uniform(-0.3, 0.3, (R, K))
+    Bg, Bu = rng.standard_normal((N, R)) * 0.14, rng.standard_normal((N, R)) * 0.14
+    dH = rng.standard_normal((M, N))
+    return X, Wg, Wu, Ag, Au, Bg, Bu, dH
+
+
+@pytest.mark.parametrize("M,K,N,R", [(5, 7, 6, 2), (9, 16, 12, 4)])
+def test_swiglu_backward_central_differences(M, K, N, R):
+    """L = <dH, H> is smooth: central differences agree with the hand-derived gradients to
+    O(h^2) (here ~1e-9 relative)."""
+    rng = np.random.default_rng(40 + M)
+    X, Wg, Wu, Ag, Au, Bg, Bu, dH = _swiglu_case(rng, M, K, N, R)
+    s = 2.0
+    args = [X, Wg, Wu, Ag, Au, Bg, Bu]
+
+    def loss(a):
+        H, *_ = oracle.swiglu_lora_forward(*a, s)
+        return np.sum(dH * H)
+
+    grads = oracle.swiglu_lora_backward(dH, *args, s)
+    h = 1e-5
+    for gi, ai in zip(grads, (0, 3, 4, 5, 6)):  # dX, dAg, dAu, dBg, dBu
+        fd = np.zeros_like(args[ai])
+        for idx in np.ndindex(*args[ai].shape):
+            p = [a.copy() for a in args]
+            p[ai][idx] += h
+            lp = loss(p)
+            p[ai][idx] -= 2 * h
+            fd[idx] = (lp - loss(p)) / (2 * h)
+        np.testing.assert_allclose(gi, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_swiglu_against_torch_autograd_float64():
+    rng = np.random.default_rng(47)
+    M, K, N, R, s = 33, 40, 24, 6, 2.0
+    X, Wg, Wu, Ag, Au, Bg, Bu, dH = _swiglu_case(rng, M, K, N, R)
+    t = lambda v, g=False: torch.tensor(v, dtype=torch.float64, requires_grad=g)
+    tX, tAg, tAu, tBg, tBu = t(X, True), t(Ag, True), t(Au, True), t(Bg, True), t(Bu, True)
+    tWg, tWu = t(Wg), t(Wu)
+    G = tX @ tWg.T + (tX @ tAg.T @ tBg.T) * s
+    U = tX @ tWu.T + (tX @ tAu.T @ tBu.T) * s
+    H = torch.nn.functional.silu(G) * U
+    H.backward(t(dH))
+    Ho, Go, Uo, _, _ = oracle.swiglu_lora_forward(X, Wg, Wu, Ag, Au, Bg, Bu, s)
+    np.testing.assert_allclose(Ho, H.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Go, G.detach().numpy(), rtol=1e-12, atol=1e-12)
+    got = oracle.swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, s)
+    for g, ref in zip(got, (tX, tAg, tAu, tBg, tBu)):
+        np.testing.assert_allclose(g, ref.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_swiglu_rows_matches_full():
+    rng = np.random.default_rng(48)
+    X, Wg, Wu, Ag, Au, Bg, Bu, _ = _swiglu_case(rng, 40, 24, 16, 4)
+    rows = np.array([0, 7, 39, 13])
+    H, G, U, _, _ = oracle.swiglu_lora_forward(X, Wg, Wu, Ag, Au, Bg, Bu, 2.0)
+    Hr, Gr, Ur = oracle.swiglu_lora_rows(X, Wg, Wu, Ag, Au, Bg, Bu, 2.0, rows)
+    np.testing.assert_array_equal(Hr, H[rows])
+    np.testing.assert_array_equal(Gr, G[rows])
+    np.testing.assert_array_equal(Ur, U[rows])
+
+
+def test_swiglu_planted_mistake_fails_the_difference_pin():
+    # dropping the (1 + g (1 - sigmoid)) factor of silu' (a plausible slip) is caught
+    rng = np.random.default_rng(49)
+    X, Wg, Wu, Ag, Au, Bg, Bu, dH = _swiglu_case(rng, 4, 6, 5, 2)
+    s = 2.0
+    G, _ = oracle.lora_forward(X, Wg, Ag, Bg, s)
+    U, _ = oracle.lora_forward(X, Wu, Au, Bu, s)
+    wrong = oracle.lora_backward(dH * U * oracle.sigmoid(G), X, Wg, Ag, Bg, s)[0] + \
+        oracle.lora_backward(dH * oracle.silu(G), X, Wu, Au, Bu, s)[0]
+    right = oracle.swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, s)[0]
+    assert np.max(np.abs(wrong - right)) > 1e-3
