@@ -161,6 +161,45 @@ lora_status qlora_bwd_dx(int64_t M, int64_t N, int64_t K, int32_t R, float scale
                          const void* dY, const uint8_t* Wq, const void* Ws, const void* A,
                          const void* B, void* dX, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- SwiGLU gate/up pair with LoRA on both projections ----------------------------------
+ * Tutorial ch. 5 §5.6 ("fused SwiGLU": SwiGLU(x) = (W_g x ⊙ sigmoid(W_g x)) ⊙ W_u x, the gate's
+ * SiLU and the product with the up projection; the output projection W_d is a plain lora_fwd
+ * layer) with §5.3's LoRA update on the gate and on the up projection:
+ *   G = X Wg^T + scale (X Ag^T) Bg^T,  U = X Wu^T + scale (X Au^T) Bu^T,  H = silu(G) ⊙ U,
+ *   silu(g) = g sigmoid(g).
+ * bf16 tensors, row-major, 16-byte aligned: X (M x K); Wgu (2N x K): the frozen gate and up
+ * weights stacked by rows, [Wg; Wu]; Ag, Au (R x K); Bg, Bu (N x R); R a multiple of 8 in
+ * [8, 32]; N, K multiples of 64.  The two projections run as one LoRA GEMM over Wgu (each X
+ * tile read once for both) at rank 2R with the adapters stacked as [Ag; Au] and
+ * [Bg 0; 0 Bu], which the call assembles in its workspace.
+ * Errors as for lora_fwd / lora_bwd; the workspace needs no initialisation. */
+
+/* Bytes of device workspace lora_swiglu_fwd needs (the stacked adapters). */
+size_t lora_swiglu_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
+
+/* Forward.  Outputs: H (M x N bf16); GU (M x 2N bf16) = [G | U], G in columns 0..N-1 and U in
+ * N..2N-1, kept for the backward; XA (M x 2R fp32) = [X Ag^T | X Au^T], unscaled, kept for the
+ * backward (may be NULL for inference).  M = 0 is an empty batch. */
+lora_status lora_swiglu_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                            const void* X, const void* Wgu, const void* Ag, const void* Au,
+                            const void* Bg, const void* Bu, void* H, void* GU, float* XA,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace lora_swiglu_bwd needs. */
+size_t lora_swiglu_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
+
+/* Backward with Wg, Wu frozen (hand-derived from L = <dH, H>): from the saved GU,
+ *   dU = dH ⊙ silu(G),  dG = dH ⊙ U ⊙ silu'(G),  silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))),
+ * then the LoRA backward of each projection: dX = dG Wg + dU Wu + scale ((dG Bg) Ag + (dU Bu) Au),
+ * dAg = scale (dG Bg)^T X, dAu likewise, dBg = scale dG^T (X Ag^T), dBu likewise.  dH, X, GU
+ * and dX bf16; XA (M x 2R fp32) from the forward; dAg, dAu (R x K) and dBg, dBu (N x R) fp32,
+ * overwritten. */
+lora_status lora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                            const void* dH, const void* X, const void* Wgu, const void* Ag,
+                            const void* Au, const void* Bg, const void* Bu, const void* GU,
+                            const float* XA, void* dX, float* dAg, float* dAu, float* dBg,
+                            float* dBu, void* ws, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* lora_status_str(lora_status s);
 

@@ -277,3 +277,14 @@ def swiglu_lora_rows(X, Wg, Wu, Ag, Au, Bg, Bu, scale, rows):
     G, _ = lora_forward_rows(X, Wg, Ag, Bg, scale, rows)
     U, _ = lora_forward_rows(X, Wu, Au, Bu, scale, rows)
     return silu(G) * U, G, U
+
+
+def swiglu_lora_backward_dx_rows(dH, X, Wg, Wu, Ag, Au, Bg, Bu, scale, rows):
+    """Rows ``rows`` of dX of the SwiGLU pair (each row needs only its own G, U and dH)."""
+    rows = np.asarray(rows)
+    H, G, U = swiglu_lora_rows(X, Wg, Wu, Ag, Au, Bg, Bu, scale, rows)
+    dHr = np.asarray(dH, dtype=np.float64)[rows]
+    dU = dHr * silu(G)
+    dG = dHr * U * silu_grad(G)
+    return (lora_backward_dx_rows(dG, Wg, Ag, Bg, scale, np.arange(len(rows)))
+            + lora_backward_dx_rows(dU, Wu, Au, Bu, scale, np.arange(len(rows))))

@@ -78,6 +78,15 @@ int dx_tiles(int64_t M, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K, int R);
 size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R);
 hipError_t launch_dadb_partials_bf16(const DadbArgs& a, hipStream_t s);
+// SwiGLU gate/up pair over the stacked weight [Wg; Wu]: stacked adapters, activation, upstream
+// gradient of the stacked GEMM, and the split of the stacked adapter gradients
+hipError_t launch_swiglu_stack(const uint16_t* Ag, const uint16_t* Au, const uint16_t* Bg, const uint16_t* Bu,
+                               uint16_t* As, uint16_t* Bs, int64_t N, int64_t K, int R, hipStream_t s);
+hipError_t launch_swiglu_fwd(const uint16_t* GU, uint16_t* H, int64_t M, int64_t N, hipStream_t s);
+hipError_t launch_swiglu_bwd(const uint16_t* dH, const uint16_t* GU, uint16_t* dGU, int64_t M, int64_t N,
+                             hipStream_t s);
+hipError_t launch_swiglu_unstack(const float* dAs, const float* dBs, float* dAg, float* dAu, float* dBg,
+                                 float* dBu, int64_t N, int64_t K, int R, hipStream_t s);
 // fp32 paths
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_dx_f32(const DxArgs& a, hipStream_t s);

@@ -130,6 +130,33 @@ lora_status bwd_dadb_common(lora_dtype dt, int64_t M, int64_t N, int64_t K, int3
   return from_hip(launch_dadb_reduce(d, s));
 }
 
+// SwiGLU pair: the rank is that of each adapter (R), the stacked GEMM runs at 2N and 2R.
+lora_status check_swiglu(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (N <= 0 || N % 64 != 0 || N > kMaxRow / 2) return LORA_ERR_SHAPE;
+  if (R < 8 || R > 32 || R % 8 != 0) return LORA_ERR_RANK;
+  return check_dims(M, 2 * N, K, 2 * R);
+}
+// forward workspace: As [2R][K] bf16 | Bs [2N][2R] bf16
+struct SwigluLayout {
+  size_t as, bs, dgu, das, dbs, inner, total;
+};
+SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t K, int32_t R, bool bwd) {
+  SwigluLayout l;
+  l.as = 0;
+  l.bs = align256((size_t)2 * R * K * 2);
+  l.dgu = l.bs + align256((size_t)4 * N * R * 2);
+  l.total = l.dgu;
+  l.das = l.dbs = l.inner = l.total;
+  if (!bwd) return l;
+  // backward: then [dG | dU] (M x 2N bf16), the stacked dA (2R x K) and dB (2N x 2R) fp32, and
+  // the stacked problem's backward workspace
+  l.das = l.dgu + align256((size_t)M * 2 * N * 2);
+  l.dbs = l.das + align256((size_t)2 * R * K * 4);
+  l.inner = l.dbs + align256((size_t)4 * N * R * 4);
+  l.total = l.inner + bwd_layout(M, 2 * N, K, 2 * R, true).total;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,6 +327,83 @@ lora_status qlora_bwd_dx(int64_t M, int64_t N, int64_t K, int32_t R, float scale
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, dX)) != LORA_OK) return st;
   return bwd_dx_common(true, LORA_BF16, M, N, K, R, scale, dY, Wq, Ws, A, B, dX, ws, ws_bytes, stream);
+}
+
+size_t lora_swiglu_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (check_swiglu(M, N, K, R) != LORA_OK) return 0;
+  return swiglu_layout(M, N, K, R, false).total;
+}
+
+lora_status lora_swiglu_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, const void* X,
+                            const void* Wgu, const void* Ag, const void* Au, const void* Bg, const void* Bu,
+                            void* H, void* GU, float* XA, void* ws, size_t ws_bytes, void* stream) {
+  lora_status st = check_swiglu(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(Wgu, Ag, Au, Bg, Bu);
+  if (st != LORA_OK) return st;
+  if (M == 0) return LORA_OK;  // empty batch: X, H, GU and XA may be NULL
+  st = check_ptrs(X, H, GU);
+  if (st != LORA_OK) return st;
+  if (XA != nullptr && !aligned16(XA)) return LORA_ERR_ALIGN;
+  const SwigluLayout lay = swiglu_layout(M, N, K, R, false);
+  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  char* base = static_cast<char*>(ws);
+  uint16_t* As = reinterpret_cast<uint16_t*>(base + lay.as);
+  uint16_t* Bs = reinterpret_cast<uint16_t*>(base + lay.bs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_swiglu_stack(static_cast<const uint16_t*>(Ag), static_cast<const uint16_t*>(Au),
+                                     static_cast<const uint16_t*>(Bg), static_cast<const uint16_t*>(Bu), As, Bs,
+                                     N, K, R, s);
+  if (e != hipSuccess) return from_hip(e);
+  // [G | U] = X [Wg; Wu]^T + scale (X [Ag; Au]^T) [Bg 0; 0 Bu]^T: one GEMM over both projections
+  const FwdArgs a{X, Wgu, nullptr, As, Bs, GU, XA, M, 2 * N, K, 2 * R, scale};
+  e = launch_fwd_mfma(a, false, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(launch_swiglu_fwd(static_cast<const uint16_t*>(GU), static_cast<uint16_t*>(H), M, N, s));
+}
+
+size_t lora_swiglu_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (check_swiglu(M, N, K, R) != LORA_OK) return 0;
+  return swiglu_layout(M, N, K, R, true).total;
+}
+
+lora_status lora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, const void* dH,
+                            const void* X, const void* Wgu, const void* Ag, const void* Au, const void* Bg,
+                            const void* Bu, const void* GU, const float* XA, void* dX, float* dAg, float* dAu,
+                            float* dBg, float* dBu, void* ws, size_t ws_bytes, void* stream) {
+  lora_status st = check_swiglu(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(Wgu, Ag, Au, Bg, Bu, dAg, dAu, dBg, dBu);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(dH, X, GU, XA, dX)) != LORA_OK) return st;
+  const SwigluLayout lay = swiglu_layout(M, N, K, R, true);
+  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  char* base = static_cast<char*>(ws);
+  uint16_t* As = reinterpret_cast<uint16_t*>(base + lay.as);
+  uint16_t* Bs = reinterpret_cast<uint16_t*>(base + lay.bs);
+  uint16_t* dGU = reinterpret_cast<uint16_t*>(base + lay.dgu);
+  float* dAs = reinterpret_cast<float*>(base + lay.das);
+  float* dBs = reinterpret_cast<float*>(base + lay.dbs);
+  void* inner = base + lay.inner;
+  const size_t inner_bytes = ws_bytes - lay.inner;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_swiglu_stack(static_cast<const uint16_t*>(Ag), static_cast<const uint16_t*>(Au),
+                                     static_cast<const uint16_t*>(Bg), static_cast<const uint16_t*>(Bu), As, Bs,
+                                     N, K, R, s);
+  if (e != hipSuccess) return from_hip(e);
+  e = launch_swiglu_bwd(static_cast<const uint16_t*>(dH), static_cast<const uint16_t*>(GU), dGU, M, N, s);
+  if (e != hipSuccess) return from_hip(e);
+  // the LoRA backward of the stacked GEMM with [dG | dU] as its upstream gradient
+  st = bwd_dx_common(false, LORA_BF16, M, 2 * N, K, 2 * R, scale, dGU, Wgu, nullptr, As, Bs, dX, inner,
+                     inner_bytes, stream);
+  if (st != LORA_OK) return st;
+  st = bwd_dadb_common(LORA_BF16, M, 2 * N, K, 2 * R, scale, dGU, X, XA, dAs, dBs, inner, inner_bytes, stream);
+  if (st != LORA_OK) return st;
+  return from_hip(launch_swiglu_unstack(dAs, dBs, dAg, dAu, dBg, dBu, N, K, R, s));
 }
 
 }  // extern "C"

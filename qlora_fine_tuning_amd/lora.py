@@ -38,6 +38,10 @@ SIGNATURES = {
     "qlora_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "qlora_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "lora_swiglu_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "lora_swiglu_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "lora_swiglu_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "lora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32] + [_p] * 15 + [_sz, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -309,3 +313,67 @@ class QLoRALinearFunction(torch.autograd.Function):
         X, Wq, Ws, A, B, XA = ctx.saved_tensors
         dX, dA, dB = qlora_bwd(dY.contiguous(), X, Wq, Ws, A, B, XA, ctx.scale)
         return dX, None, None, dA.to(A.dtype), dB.to(B.dtype), None
+
+
+def lora_swiglu_fwd(X, Wgu, Ag, Au, Bg, Bu, scale: float, *, H=None, GU=None, XA=None, save_xa: bool = True,
+                    ws=None, stream=None):
+    """SwiGLU gate/up pair with LoRA on both: H = silu(G) * U over the stacked weight Wgu = [Wg; Wu]
+    (2N x K).  Returns (H, GU, XA): GU = [G | U] (M x 2N bf16) and XA = [X Ag^T | X Au^T] (fp32)."""
+    lib = load()
+    for t, n in ((X, "X"), (Wgu, "Wgu"), (Ag, "Ag"), (Au, "Au"), (Bg, "Bg"), (Bu, "Bu")):
+        _want(t, n, torch.bfloat16)
+    M, K = X.shape
+    N, R = Wgu.shape[0] // 2, Ag.shape[0]
+    dev = X.device
+    if H is None:
+        H = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if GU is None:
+        GU = torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev)
+    if XA is None and save_xa:
+        XA = torch.empty((M, 2 * R), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(int(lib.lora_swiglu_fwd_workspace_bytes(M, N, K, R)), 1), dtype=torch.uint8, device=dev)
+    st = lib.lora_swiglu_fwd(M, N, K, R, float(scale), _ptr(X), _ptr(Wgu), _ptr(Ag), _ptr(Au), _ptr(Bg), _ptr(Bu),
+                             _ptr(H), _ptr(GU), _ptr(XA), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("lora_swiglu_fwd", st)
+    return H, GU, XA
+
+
+def lora_swiglu_bwd(dH, X, Wgu, Ag, Au, Bg, Bu, GU, XA, scale: float, *, dX=None, dAg=None, dAu=None, dBg=None,
+                    dBu=None, ws=None, stream=None):
+    """Returns (dX, dAg, dAu, dBg, dBu): dX bf16, the adapter gradients fp32."""
+    lib = load()
+    M, K = X.shape
+    N, R = Wgu.shape[0] // 2, Ag.shape[0]
+    dev = X.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if dX is None else dX
+    dAg = torch.empty((R, K), **f32) if dAg is None else dAg
+    dAu = torch.empty((R, K), **f32) if dAu is None else dAu
+    dBg = torch.empty((N, R), **f32) if dBg is None else dBg
+    dBu = torch.empty((N, R), **f32) if dBu is None else dBu
+    if ws is None:
+        ws = torch.empty(max(int(lib.lora_swiglu_bwd_workspace_bytes(M, N, K, R)), 1), dtype=torch.uint8, device=dev)
+    st = lib.lora_swiglu_bwd(M, N, K, R, float(scale), _ptr(dH), _ptr(X), _ptr(Wgu), _ptr(Ag), _ptr(Au), _ptr(Bg),
+                             _ptr(Bu), _ptr(GU), _ptr(XA), _ptr(dX), _ptr(dAg), _ptr(dAu), _ptr(dBg), _ptr(dBu),
+                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("lora_swiglu_bwd", st)
+    return dX, dAg, dAu, dBg, dBu
+
+
+class SwiGLULoRAFunction(torch.autograd.Function):
+    """Autograd wrapper of the SwiGLU gate/up pair: Wgu frozen; the forward saves [G | U] and the
+    stacked X A^T, the backward recomputes sigmoid(G) from them."""
+
+    @staticmethod
+    def forward(ctx, X, Wgu, Ag, Au, Bg, Bu, scale):
+        H, GU, XA = lora_swiglu_fwd(X, Wgu, Ag, Au, Bg, Bu, scale)
+        ctx.save_for_backward(X, Wgu, Ag, Au, Bg, Bu, GU, XA)
+        ctx.scale = scale
+        return H
+
+    @staticmethod
+    def backward(ctx, dH):
+        X, Wgu, Ag, Au, Bg, Bu, GU, XA = ctx.saved_tensors
+        dX, dAg, dAu, dBg, dBu = lora_swiglu_bwd(dH.contiguous(), X, Wgu, Ag, Au, Bg, Bu, GU, XA, ctx.scale)
+        return dX, None, dAg.to(Ag.dtype), dAu.to(Au.dtype), dBg.to(Bg.dtype), dBu.to(Bu.dtype), None

@@ -115,3 +115,53 @@ def workload_inputs(name: str, *, M: Optional[int] = None, b_dist: str = "var",
     return make_inputs(w["M"], w["N"], w["K"], w["R"], seed=w["seed"], dtype=w["dtype"],
                        alpha=w["alpha"], int4=w["int4"], b_dist=b_dist,
                        with_dy=with_dy and not name.startswith("decode"))
+
+
+@dataclass
+class SwigluInputs:
+    """One input set of the SwiGLU gate/up pair (bf16 bit patterns, uint16)."""
+    M: int
+    N: int
+    K: int
+    R: int
+    alpha: float
+    seed: int
+    X: np.ndarray
+    Wg: np.ndarray
+    Wu: np.ndarray
+    Ag: np.ndarray
+    Au: np.ndarray
+    Bg: np.ndarray
+    Bu: np.ndarray
+    dH: Optional[np.ndarray]
+
+    @property
+    def scale(self) -> float:
+        return self.alpha / self.R
+
+    @property
+    def Wgu(self) -> np.ndarray:
+        """The gate and up weights stacked by rows, [Wg; Wu] (2N x K)."""
+        return np.concatenate([self.Wg, self.Wu], axis=0)
+
+
+def make_swiglu_inputs(M: int, N: int, K: int, R: int, *, seed: int, alpha: Optional[float] = None,
+                       with_dh: bool = True) -> SwigluInputs:
+    """Draw a SwiGLU input set: the distributions of make_inputs (X, dH ~ N(0,1); each W ~
+    N(0, 1/K); each A ~ U(+-1/sqrt K); each B ~ N(0, variance 0.02)), drawn in the order X, Wg,
+    Wu, Ag, Au, Bg, Bu, dH and rounded once to bf16."""
+    if alpha is None:
+        alpha = 2.0 * R
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = rng.standard_normal((M, K))
+    Wg = rng.standard_normal((N, K)) * np.sqrt(1.0 / K)
+    Wu = rng.standard_normal((N, K)) * np.sqrt(1.0 / K)
+    a = 1.0 / np.sqrt(K)
+    Ag = rng.uniform(-a, a, size=(R, K))
+    Au = rng.uniform(-a, a, size=(R, K))
+    Bg = rng.standard_normal((N, R)) * np.sqrt(0.02)
+    Bu = rng.standard_normal((N, R)) * np.sqrt(0.02)
+    dH = rng.standard_normal((M, N)) if with_dh else None
+    r = lambda v: None if v is None else _round(v, "bf16")
+    return SwigluInputs(M=M, N=N, K=K, R=R, alpha=float(alpha), seed=seed, X=r(X), Wg=r(Wg), Wu=r(Wu),
+                        Ag=r(Ag), Au=r(Au), Bg=r(Bg), Bu=r(Bu), dH=r(dH))

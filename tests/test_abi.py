@@ -158,3 +158,59 @@ def test_binding_refuses_to_run_without_the_library(tmp_path):
             lora.load(str(tmp_path / "missing.so"))
     finally:
         lora._LIB = saved
+
+
+# ---- SwiGLU gate/up pair ----------------------------------------------------------------
+
+def swiglu_fwd(lib, M=64, N=256, K=256, R=16, scale=2.0, ws=P, ws_bytes=None, **ptrs):
+    p = dict(X=P, Wgu=P, Ag=P, Au=P, Bg=P, Bu=P, H=P, GU=P, XA=P)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.lora_swiglu_fwd_workspace_bytes(M, N, K, R)
+    return lib.lora_swiglu_fwd(M, N, K, R, scale, p["X"], p["Wgu"], p["Ag"], p["Au"], p["Bg"], p["Bu"],
+                               p["H"], p["GU"], p["XA"], ws, ws_bytes, None)
+
+
+def swiglu_bwd(lib, M=64, N=256, K=256, R=16, scale=2.0, ws=P, ws_bytes=None, **ptrs):
+    names = ("dH", "X", "Wgu", "Ag", "Au", "Bg", "Bu", "GU", "XA", "dX", "dAg", "dAu", "dBg", "dBu")
+    p = {n: P for n in names}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.lora_swiglu_bwd_workspace_bytes(M, N, K, R)
+    return lib.lora_swiglu_bwd(M, N, K, R, scale, *(p[n] for n in names), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=100), 2), (dict(K=96), 2), (dict(M=-1), 2),
+    (dict(R=40), 3), (dict(R=12), 3), (dict(R=0), 3),  # each adapter's rank: 8..32 (stacked 16..64)
+    (dict(scale=float("nan")), 8),
+    (dict(X=NUL), 1), (dict(Wgu=NUL), 1), (dict(Au=NUL), 1), (dict(Bu=NUL), 1), (dict(GU=NUL), 1),
+    (dict(H=MIS), 4),
+    (dict(ws=NUL), 6), (dict(ws_bytes=16), 6),
+])
+def test_lora_swiglu_fwd_validation(lib, kw, code):
+    assert swiglu_fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=48), 3), (dict(N=32), 2),
+    (dict(dH=NUL), 1), (dict(GU=NUL), 1), (dict(XA=NUL), 1), (dict(dBu=NUL), 1),
+    (dict(dX=MIS), 4),
+    (dict(ws=NUL), 6), (dict(ws_bytes=1024), 6),
+])
+def test_lora_swiglu_bwd_validation(lib, kw, code):
+    assert swiglu_bwd(lib, **kw) == code
+
+
+def test_swiglu_workspace_sizes(lib):
+    # forward: the stacked adapters [Ag; Au] (2R x K) and [Bg 0; 0 Bu] (2N x 2R), bf16; backward:
+    # also [dG | dU] (M x 2N bf16), the stacked dA and dB (fp32), then the backward workspace of
+    # the stacked problem (2N outputs, rank 2R)
+    M, N, K, R = 8192, 14336, 4096, 16
+    pad = lambda b: (b + 255) // 256 * 256
+    fwd_need = pad(2 * R * K * 2) + pad(4 * N * R * 2)
+    assert lib.lora_swiglu_fwd_workspace_bytes(M, N, K, R) == fwd_need
+    bwd_need = (fwd_need + pad(M * 2 * N * 2) + pad(2 * R * K * 4) + pad(4 * N * R * 4)
+                + lib.lora_bwd_workspace_bytes(1, M, 2 * N, K, 2 * R))
+    assert lib.lora_swiglu_bwd_workspace_bytes(M, N, K, R) == bwd_need
+    assert lib.lora_swiglu_fwd_workspace_bytes(M, N, K, 40) == 0

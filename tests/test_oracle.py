@@ -457,3 +457,12 @@ def test_swiglu_planted_mistake_fails_the_difference_pin():
         oracle.lora_backward(dH * oracle.silu(G), X, Wu, Au, Bu, s)[0]
     right = oracle.swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, s)[0]
     assert np.max(np.abs(wrong - right)) > 1e-3
+
+
+def test_swiglu_dx_rows_matches_full():
+    rng = np.random.default_rng(50)
+    X, Wg, Wu, Ag, Au, Bg, Bu, dH = _swiglu_case(rng, 30, 24, 16, 4)
+    rows = np.array([29, 0, 11])
+    dX = oracle.swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, 2.0)[0]
+    got = oracle.swiglu_lora_backward_dx_rows(dH, X, Wg, Wu, Ag, Au, Bg, Bu, 2.0, rows)
+    np.testing.assert_allclose(got, dX[rows], rtol=1e-13, atol=1e-13)
