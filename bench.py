@@ -203,6 +203,47 @@ def bench_mlp(lora, torch, dev, reps):
     return out
 
 
+def bench_swiglu(lora, torch, dev, reps):
+    """The SwiGLU gate/up pair with LoRA on both projections at the MLP gate/up shape (M=8192,
+    K=4096 -> N=14336, r=16): fwd+bwd TFLOP/s counting the two projections' LoRA work."""
+    from qlora_fine_tuning_amd.workloads import make_swiglu_inputs
+
+    M, N, K, R = 8192, 14336, 4096, 16
+    inp = make_swiglu_inputs(M, N, K, R, seed=3)
+    X, Wgu, Ag, Au, Bg, Bu, dH = (dev_bits(getattr(inp, n), dev) for n in ("X", "Wgu", "Ag", "Au", "Bg", "Bu", "dH"))
+    H = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    GU = torch.empty(M, 2 * N, dtype=torch.bfloat16, device=dev)
+    XA = torch.empty(M, 2 * R, dtype=torch.float32, device=dev)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = [torch.empty(R, K, dtype=torch.float32, device=dev) for _ in range(2)]
+    dB = [torch.empty(N, R, dtype=torch.float32, device=dev) for _ in range(2)]
+    wsf = torch.empty(lora.lora_swiglu_fwd_workspace_bytes(M, N, K, R), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(lora.lora_swiglu_bwd_workspace_bytes(M, N, K, R), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        lora.lora_swiglu_fwd(X, Wgu, Ag, Au, Bg, Bu, inp.scale, H=H, GU=GU, XA=XA, ws=wsf, stream=stream)
+
+    def bwd():
+        lora.lora_swiglu_bwd(dH, X, Wgu, Ag, Au, Bg, Bu, GU, XA, inp.scale, dX=dX, dAg=dA[0], dAu=dA[1],
+                             dBg=dB[0], dBu=dB[1], ws=wsb, stream=stream)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    ms = event_time_ms(step, reps, stream)
+    fwd_ms = event_time_ms(fwd, reps, stream)
+    fl = 2 * lora_flops(M, N, K, R)
+    return {"workload": "mlp_swiglu", "M": M, "N": N, "K": K, "r": R, "ms_per_step": round(ms, 4),
+            "fwd_ms": round(fwd_ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
+            "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "note": "gate and up projections as one LoRA GEMM over the stacked weight, then silu(G) * U"}
+
+
 def bench_decode(lora, torch, dev, reps, copies=6):
     """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL)."""
     from qlora_fine_tuning_amd.workloads import workload_inputs
@@ -340,6 +381,7 @@ def main(argv=None):
     }
     if not args.no_secondary:
         result["secondary"] = {"mlp": bench_mlp(lora, torch, dev, 20),
+                               "mlp_swiglu": bench_swiglu(lora, torch, dev, 20),
                                "qlora": bench_qlora_ffn(lora, torch, dev, 20),
                                "decode": bench_decode(lora, torch, dev, 20),
                                "torch_unfused": bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}

@@ -315,6 +315,14 @@ class QLoRALinearFunction(torch.autograd.Function):
         return dX, None, None, dA.to(A.dtype), dB.to(B.dtype), None
 
 
+def lora_swiglu_fwd_workspace_bytes(M: int, N: int, K: int, R: int) -> int:
+    return int(load().lora_swiglu_fwd_workspace_bytes(M, N, K, R))
+
+
+def lora_swiglu_bwd_workspace_bytes(M: int, N: int, K: int, R: int) -> int:
+    return int(load().lora_swiglu_bwd_workspace_bytes(M, N, K, R))
+
+
 def lora_swiglu_fwd(X, Wgu, Ag, Au, Bg, Bu, scale: float, *, H=None, GU=None, XA=None, save_xa: bool = True,
                     ws=None, stream=None):
     """SwiGLU gate/up pair with LoRA on both: H = silu(G) * U over the stacked weight Wgu = [Wg; Wu]

@@ -214,3 +214,6 @@ def test_swiglu_workspace_sizes(lib):
                 + lib.lora_bwd_workspace_bytes(1, M, 2 * N, K, 2 * R))
     assert lib.lora_swiglu_bwd_workspace_bytes(M, N, K, R) == bwd_need
     assert lib.lora_swiglu_fwd_workspace_bytes(M, N, K, 40) == 0
+    # the binding's wrappers return the same sizes
+    assert lora.lora_swiglu_fwd_workspace_bytes(M, N, K, R) == fwd_need
+    assert lora.lora_swiglu_bwd_workspace_bytes(M, N, K, R) == bwd_need
