@@ -15,6 +15,10 @@
 //  * the epilogue puts scale * XA through LDS, splits it into bf16 hi + lo parts and adds
 //    B (hi + lo)^T into the fp32 accumulators with one more MFMA per 16 ranks, then
 //    rounds Y to bf16 once.
+// SwiGLU pair (tutorial ch. 5 §5.6): with W = [Wg; Wu] (2 Nh x K) the 256 W rows of a tile
+// are 128 gate rows and the 128 up rows of the same outputs, so the two waves that share an X
+// slice hold G and U of the same 128 x 128 block; they trade fp32 halves through LDS, and
+// H = silu(G) U leaves the epilogue with G and U (bf16, for the backward).
 // QLoRA ("探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3): the W tile
 // arrives as packed int4 codes plus one fp16 scale per 64 k; each thread unpacks its
 // codes in registers to bf16_rne(q * s) on the way into LDS.
@@ -23,15 +27,49 @@
 
 namespace lora {
 
+// sigmoid from the hardware exp2 and reciprocal (about 1 ulp of fp32 each, far below the bf16
+// rounding of H); the correctly rounded expf and division cost ~35 VALU operations per element,
+// which the epilogue cannot hide behind matrix work
+__device__ __forceinline__ float silu_sigmoid(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
+
+// A 128 x 64 block of Y (rows m, columns n: accumulator rows i < 4 of acc[i * 8 + j]) to bf16,
+// staged through 16 KB of LDS so that each row leaves as full 16-byte chunks; 8 chunks per row,
+// swizzled by the row's low 3 bits.
+__device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stage, uint16_t* out, size_t ld,
+                                                int rows_valid, int cols_valid, int lane) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 2 * i + (g4 >> 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 v = acc[i * 8 + j];
+      const u32x2 o = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(stage + (j * 16 + l16) * 64 + ((c ^ (l16 & 7)) << 3) + (g4 & 1) * 4) = o;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes have landed
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int row = p * 8 + (lane >> 3), c = lane & 7;
+    const u32x4 v = ld16(stage + row * 64 + ((c ^ (row & 7)) << 3));
+    if (row < rows_valid && c * 8 < cols_valid) st16(out + (size_t)row * ld + c * 8, v);
+  }
+}
+
 // PANEL: the panel X A^T is accumulated here from the X fragments of the main loop.  Without
 // it (rank 64, when the caller keeps XA) XA has been computed by a pass of its own and is read
 // in the epilogue: the rank-64 panel's accumulators and A fragments make the main loop spill.
-template <int RP, bool INT4, bool PANEL>
+// SWIGLU (bf16 W only): N = 2 Nh stacked rows, Y = [G | U] (M x 2 Nh) and H (M x Nh) out.
+template <int RP, bool INT4, bool PANEL, bool SWIGLU>
 __global__ void __launch_bounds__(kThreads)
 fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
                 const uint16_t* __restrict__ Bm, uint16_t* __restrict__ Y,
-                float* __restrict__ XA, int M, int N, int K, int R, float scale) {
+                float* __restrict__ XA, uint16_t* __restrict__ H, int M, int N, int K, int R,
+                float scale) {
+  static_assert(!(SWIGLU && INT4), "the SwiGLU pair takes a bf16 weight");
   constexpr int TT = kTile * kStep;  // elements of one 256 x 64 operand tile
   constexpr int AROWS = RP < 32 ? 32 : RP;  // adapter rows in LDS: each wave copies 8k of them
   constexpr int AT = AROWS * kStep;
@@ -54,9 +92,17 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
 
   const rsrc_t rX = make_rsrc(X + (size_t)m0 * K, (uint32_t)min(M - m0, kTile) * rowb);
   const rsrc_t rA = make_rsrc(A, (uint32_t)R * rowb);
-  rsrc_t rW;
-  if constexpr (!INT4) rW = make_rsrc(static_cast<const uint16_t*>(Wp) + (size_t)n0 * K,
-                                      (uint32_t)min(N - n0, kTile) * rowb);
+  // SwiGLU: output columns ng .. ng+127 of H; tile rows 0-127 are those gate rows of W (rW),
+  // rows 128-255 the up rows (rWu, Nh rows further on)
+  const int nh = SWIGLU ? N / 2 : N, ng = SWIGLU ? tn * (kTile / 2) : n0;
+  rsrc_t rW, rWu;
+  if constexpr (SWIGLU) {
+    const uint32_t bytes = (uint32_t)min(nh - ng, kTile / 2) * rowb;
+    rW = make_rsrc(static_cast<const uint16_t*>(Wp) + (size_t)ng * K, bytes);
+    rWu = make_rsrc(static_cast<const uint16_t*>(Wp) + (size_t)(nh + ng) * K, bytes);
+  } else if constexpr (!INT4) {
+    rW = make_rsrc(static_cast<const uint16_t*>(Wp) + (size_t)n0 * K, (uint32_t)min(N - n0, kTile) * rowb);
+  }
 
   // Lane offsets of the 16-byte LDS-DMA chunks: instruction i of wave w fills rows
   // (4i + w) * 8 .. +7 of a 256-row tile; lane l goes to physical chunk l & 7 of row
@@ -70,6 +116,15 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       dma16(rs, dst + (4 * i + wave) * 512, tile_voff, (uint32_t)k0 * 2u + (uint32_t)i * 32u * rowb);
+  };
+  // instruction i of the W tile (rows (4i + w) * 8 ..): SwiGLU takes i < 4 from the gate rows
+  // and i >= 4 from the up rows
+  auto dma_w_part = [&](uint16_t* dst, int k0, int i) {
+    if constexpr (SWIGLU)
+      dma16(i < 4 ? rW : rWu, dst + (4 * i + wave) * 512, tile_voff,
+            (uint32_t)k0 * 2u + (uint32_t)(i & 3) * 32u * rowb);
+    else
+      dma16(rW, dst + (4 * i + wave) * 512, tile_voff, (uint32_t)k0 * 2u + (uint32_t)i * 32u * rowb);
   };
   auto dma_a = [&](uint16_t* dst, int k0) {
 #pragma unroll
@@ -208,7 +263,9 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   auto prefetch = [&](int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an) {
     const int k1 = min(kn, nk - 1) * kStep;
     dma_tile(rX, xn, k1);
-    if constexpr (!INT4) dma_tile(rW, wnx, k1);
+    if constexpr (!INT4)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma_w_part(wnx, k1, i);
     if constexpr (PANEL) dma_a(an, k1);
   };
   // The same copies in 16 parts for phase(): the adapter rows first, then X rows 8d.. (d < 8),
@@ -220,7 +277,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     if (d < 8) {
       dma16(rX, xn + (4 * d + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)d * 32u * rowb);
     } else if constexpr (!INT4) {
-      dma16(rW, wnx + (4 * (d - 8) + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)(d - 8) * 32u * rowb);
+      dma_w_part(wnx, k1, d - 8);
     }
   };
   const NoCopy nocopy;
@@ -276,8 +333,10 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     const int rk = c * 16 + (g4 & 1) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + i * 16 + l16;
-      f[i] = (n < N && rk < R) ? ld16(Bm + (size_t)n * R + rk) : zero4();
+      // SwiGLU: B rows of the gate (wn = 0) or up (wn = 1) block of the stacked B
+      const int n = (SWIGLU ? ng : n0 + wn * 128) + i * 16 + l16;
+      const size_t row = (SWIGLU && wn) ? (size_t)(nh + n) : (size_t)n;
+      f[i] = (n < nh && rk < R) ? ld16(Bm + row * R + rk) : zero4();
     }
   };
   if constexpr (RP <= 32) {
@@ -341,30 +400,88 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
 
   // ---- store Y (bf16, one rounding), staged through this wave's freed tile buffer ----
   __syncthreads();  // every wave is done with the panel rows in LDS
-  uint16_t* const stage = wave == 0 ? sX0 : (wave == 1 ? sX1 : (wave == 2 ? sW0 : sW1));
-  const int mw = m0 + wm * 128, nw = n0 + wn * 128;
-  store_block_bf16(acc, stage, Y + (size_t)mw * N + nw, (size_t)N, M - mw, N - nw, lane);
+  auto buf = [&](int w) { return w == 0 ? sX0 : (w == 1 ? sX1 : (w == 2 ? sW0 : sW1)); };
+  uint16_t* const stage = buf(wave);
+  const int mw = m0 + wm * 128;
+  if constexpr (!SWIGLU) {
+    const int nw = n0 + wn * 128;
+    store_block_bf16(acc, stage, Y + (size_t)mw * N + nw, (size_t)N, M - mw, N - nw, lane);
+  } else {
+    // G (gate waves) or U (up waves) of outputs ng .. ng+127 into [G | U]
+    store_block_bf16(acc, stage, Y + (size_t)mw * N + (wn ? nh : 0) + ng, (size_t)N, M - mw, nh - ng, lane);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the staging reads are done
+    // The gate wave finishes H for accumulator rows i < 4 (outputs ng .. ng+63), the up wave
+    // for i >= 4; each hands the other half of its fp32 accumulators to its partner
+    // (wave ^ 2, the same X slice) through its own buffer, lane-linear.
+    float* const mine = reinterpret_cast<float*>(stage);
+    const float* const theirs = reinterpret_cast<const float*>(buf(wave ^ 2));
+    // (the branches on wn are wave-uniform; the barriers stay outside them)
+    auto give = [&](auto keep_c) {
+      constexpr int GIVE = 4 - decltype(keep_c)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<f32x4*>(mine + ((q * 8 + j) * 64 + lane) * 4) = acc[(GIVE + q) * 8 + j];
+    };
+    auto combine = [&](auto keep_c) {
+      constexpr int KEEP = decltype(keep_c)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(theirs + ((q * 8 + j) * 64 + lane) * 4);
+          f32x4& a = acc[(KEEP + q) * 8 + j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = KEEP == 0 ? a[e] : o[e], u = KEEP == 0 ? o[e] : a[e];
+            a[e] = g * silu_sigmoid(g) * u;
+          }
+        }
+    };
+    auto put = [&](auto keep_c) {
+      constexpr int KEEP = decltype(keep_c)::value;
+      store_half_bf16(acc + KEEP * 8, stage, H + (size_t)mw * nh + ng + KEEP * 16, (size_t)nh, M - mw,
+                      nh - ng - KEEP * 16, lane);
+    };
+    const std::integral_constant<int, 0> gate_half;
+    const std::integral_constant<int, 4> up_half;
+    if (wn) give(up_half); else give(gate_half);
+    __syncthreads();
+    if (wn) combine(up_half); else combine(gate_half);
+    __syncthreads();  // the partner is done reading this wave's buffer
+    if (wn) put(up_half); else put(gate_half);
+  }
 }
 
-template <int RP, bool INT4, bool PANEL>
+template <int RP, bool INT4, bool PANEL, bool SWIGLU = false>
 static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
+  // SwiGLU: N = 2 Nh stacked rows, one tile per 128 outputs of H: ceil(2 Nh / 256) of them
   const int tiles = (int)(((a.M + kTile - 1) / kTile) * ((a.N + kTile - 1) / kTile));
-  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL>), dim3(tiles), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, SWIGLU>), dim3(tiles), dim3(kThreads), 0, s,
                      (const uint16_t*)a.X, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
-                     (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (int)a.M, (int)a.N, (int)a.K,
-                     (int)a.R, a.scale);
+                     (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (uint16_t*)a.H, (int)a.M, (int)a.N,
+                     (int)a.K, (int)a.R, a.scale);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
+  const bool swiglu = a.H != nullptr;
+  if (swiglu && int4) return hipErrorInvalidValue;
   if (rp == 64 && a.XA != nullptr) {
     // the panel as a pass of its own into XA (its partials in Y, which the kernel then
     // overwrites), then the kernel without the panel
     const hipError_t e = launch_panel_xa(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A),
                                          a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
     if (e != hipSuccess) return e;
+    if (swiglu) return launch_fwd_rp<64, false, false, true>(a, s);
     return int4 ? launch_fwd_rp<64, true, false>(a, s) : launch_fwd_rp<64, false, false>(a, s);
+  }
+  if (swiglu) {
+    if (rp == 16) return launch_fwd_rp<16, false, true, true>(a, s);
+    if (rp == 32) return launch_fwd_rp<32, false, true, true>(a, s);
+    return launch_fwd_rp<64, false, true, true>(a, s);
   }
   if (int4) {
     if (rp == 16) return launch_fwd_rp<16, true, true>(a, s);

@@ -22,6 +22,7 @@ struct FwdArgs {
   int64_t M, N, K;
   int R;
   float scale;
+  void* H = nullptr;  // SwiGLU pair (bf16 W = [Wg; Wu], N = 2 Nh): H = silu(G) U, M x Nh
 };
 
 struct DxArgs {
@@ -82,7 +83,6 @@ hipError_t launch_dadb_partials_bf16(const DadbArgs& a, hipStream_t s);
 // gradient of the stacked GEMM, and the split of the stacked adapter gradients
 hipError_t launch_swiglu_stack(const uint16_t* Ag, const uint16_t* Au, const uint16_t* Bg, const uint16_t* Bu,
                                uint16_t* As, uint16_t* Bs, int64_t N, int64_t K, int R, hipStream_t s);
-hipError_t launch_swiglu_fwd(const uint16_t* GU, uint16_t* H, int64_t M, int64_t N, hipStream_t s);
 hipError_t launch_swiglu_bwd(const uint16_t* dH, const uint16_t* GU, uint16_t* dGU, int64_t M, int64_t N,
                              hipStream_t s);
 hipError_t launch_swiglu_unstack(const float* dAs, const float* dBs, float* dAg, float* dAu, float* dBg,

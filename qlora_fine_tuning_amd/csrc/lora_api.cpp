@@ -357,11 +357,10 @@ lora_status lora_swiglu_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float sc
                                      static_cast<const uint16_t*>(Bg), static_cast<const uint16_t*>(Bu), As, Bs,
                                      N, K, R, s);
   if (e != hipSuccess) return from_hip(e);
-  // [G | U] = X [Wg; Wu]^T + scale (X [Ag; Au]^T) [Bg 0; 0 Bu]^T: one GEMM over both projections
-  const FwdArgs a{X, Wgu, nullptr, As, Bs, GU, XA, M, 2 * N, K, 2 * R, scale};
-  e = launch_fwd_mfma(a, false, s);
-  if (e != hipSuccess) return from_hip(e);
-  return from_hip(launch_swiglu_fwd(static_cast<const uint16_t*>(GU), static_cast<uint16_t*>(H), M, N, s));
+  // [G | U] = X [Wg; Wu]^T + scale (X [Ag; Au]^T) [Bg 0; 0 Bu]^T: one GEMM over both
+  // projections, whose epilogue also forms H = silu(G) U from the fp32 accumulators
+  const FwdArgs a{X, Wgu, nullptr, As, Bs, GU, XA, M, 2 * N, K, 2 * R, scale, H};
+  return from_hip(launch_fwd_mfma(a, false, s));
 }
 
 size_t lora_swiglu_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {

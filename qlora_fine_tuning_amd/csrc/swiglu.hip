@@ -5,21 +5,23 @@
 // The two projections run as ONE LoRA GEMM over the stacked frozen weight [Wg; Wu] (2N x K),
 // so each X tile is read once for both.  The adapters are stacked to match: A as [Ag; Au]
 // (2R x K), B block-diagonally as [Bg 0; 0 Bu] (2N x 2R), so the rank-2R update gives the
-// gate columns Bg (X Ag^T) and the up columns Bu (X Au^T) and nothing across.  The kernels here:
+// gate columns Bg (X Ag^T) and the up columns Bu (X Au^T) and nothing across.  The forward
+// GEMM's epilogue (fwd.hip) pairs gate and up rows in each tile and writes H = silu(G) U next
+// to [G | U] (bf16, kept for the backward).  The kernels here:
 //  * swiglu_stack_kernel: assembles the stacked A and B (small, per call: A and B are trained);
-//  * swiglu_fwd_kernel: H = silu(G) * U from the GEMM output [G | U] (bf16, kept for backward);
 //  * swiglu_bwd_kernel: [dG | dU] = [dH * U * silu'(G) | dH * silu(G)], the upstream gradient of
 //    the stacked GEMM, whose LoRA backward (at 2N, 2R) gives dX and the stacked adapter
 //    gradients;
 //  * swiglu_unstack_kernel: splits those into dAg, dAu and the diagonal blocks dBg, dBu.
-// silu(g) = g * sigmoid(g), silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))), in fp32 with the
-// device expf; each output is rounded to bf16 once.
+// silu(g) = g * sigmoid(g), silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))), in fp32; each output
+// is rounded to bf16 once.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace lora {
 
-__device__ __forceinline__ float sigmoid_f(float g) { return 1.f / (1.f + expf(-g)); }
+// hardware exp2 and reciprocal (about 1 ulp of fp32 each; every output is rounded to bf16)
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 __device__ __forceinline__ float bf16_at(const u32x4& v, int i) {
   const uint32_t w = v[i >> 1];
   return (i & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -43,23 +45,6 @@ swiglu_stack_kernel(const uint16_t* __restrict__ Ag, const uint16_t* __restrict_
     else if (n >= N && j >= R) v = ld16(Bu + (n - N) * R + (j - R));
     st16(Bs + e, v);
   }
-}
-
-// H[m][n] = silu(G[m][n]) * U[m][n], with G = GU[m][n] and U = GU[m][N + n]; 8 columns per thread
-__global__ void __launch_bounds__(256)
-swiglu_fwd_kernel(const uint16_t* __restrict__ GU, uint16_t* __restrict__ H, int64_t M, int64_t N) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t cpr = N / 8;
-  if (t >= M * cpr) return;
-  const int64_t m = t / cpr, n = (t - m * cpr) * 8;
-  const u32x4 g = ld16(GU + m * 2 * N + n), u = ld16(GU + m * 2 * N + N + n);
-  u32x4 h;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float g0 = bf16_at(g, 2 * p), g1 = bf16_at(g, 2 * p + 1);
-    h[p] = pack_bf16(g0 * sigmoid_f(g0) * bf16_at(u, 2 * p), g1 * sigmoid_f(g1) * bf16_at(u, 2 * p + 1));
-  }
-  st16(H + m * N + n, h);
 }
 
 // dGU[m][n] = dH U silu'(G), dGU[m][N + n] = dH silu(G); 8 columns per thread
@@ -116,12 +101,6 @@ hipError_t launch_swiglu_stack(const uint16_t* Ag, const uint16_t* Au, const uin
                                uint16_t* As, uint16_t* Bs, int64_t N, int64_t K, int R, hipStream_t s) {
   const int64_t n = (int64_t)2 * R * K / 8 + (int64_t)4 * N * R / 8;
   hipLaunchKernelGGL(swiglu_stack_kernel, dim3(blocks_for(n)), dim3(256), 0, s, Ag, Au, Bg, Bu, As, Bs, N, K, R);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_fwd(const uint16_t* GU, uint16_t* H, int64_t M, int64_t N, hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(blocks_for(M * (N / 8))), dim3(256), 0, s, GU, H, M, N);
   return hipGetLastError();
 }
 

@@ -48,6 +48,24 @@ def test_swiglu_small_shapes(gpu_lib, M, N, K, R):
         assert_close(name, host(got), r)
 
 
+@pytest.mark.parametrize("R", [16, 32])
+def test_swiglu_forward_without_xa(gpu_lib, R):
+    # XA not kept: the panel X [Ag; Au]^T is formed inside the GEMM at every rank (at 2R = 64 the
+    # instance with the in-kernel rank-64 panel); N = 192 leaves the last tile's up half empty
+    M, N, K = 300, 192, 256
+    print(f"case swiglu no-XA M={M} N={N} K={K} R={R}", flush=True)
+    inp = make_swiglu_inputs(M, N, K, R, seed=77 + R)
+    X, Wgu, Ag, Au, Bg, Bu = _dev(inp)
+    H, GU, XA = gpu_lib.lora_swiglu_fwd(X, Wgu, Ag, Au, Bg, Bu, inp.scale, save_xa=False)
+    torch.cuda.synchronize()
+    assert XA is None
+    x, wg, wu, ag, au, bg, bu = _vals(inp, "X", "Wg", "Wu", "Ag", "Au", "Bg", "Bu")
+    Hr, Gr, Ur, _, _ = oracle.swiglu_lora_forward(x, wg, wu, ag, au, bg, bu, inp.scale)
+    assert_close("H", host(H), Hr)
+    assert_close("G", host(GU[:, :N]), Gr)
+    assert_close("U", host(GU[:, N:]), Ur)
+
+
 def test_swiglu_mlp_full_size_sampled(gpu_lib):
     # the MLP gate/up workload: M = 8192 (4 x 2048), K = 4096 -> N = 14336, r = 16
     print("case swiglu M=8192 N=14336 K=4096 R=16 (sampled rows)", flush=True)
