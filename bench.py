@@ -241,7 +241,7 @@ def bench_swiglu(lora, torch, dev, reps):
     return {"workload": "mlp_swiglu", "M": M, "N": N, "K": K, "r": R, "ms_per_step": round(ms, 4),
             "fwd_ms": round(fwd_ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
             "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-            "note": "gate and up projections as one LoRA GEMM over the stacked weight, then silu(G) * U"}
+            "note": "gate and up projections as one LoRA GEMM over the stacked weight, H = silu(G) * U in its epilogue"}
 
 
 def bench_decode(lora, torch, dev, reps, copies=6):

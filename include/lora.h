@@ -179,7 +179,9 @@ size_t lora_swiglu_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t 
 
 /* Forward.  Outputs: H (M x N bf16); GU (M x 2N bf16) = [G | U], G in columns 0..N-1 and U in
  * N..2N-1, kept for the backward; XA (M x 2R fp32) = [X Ag^T | X Au^T], unscaled, kept for the
- * backward (may be NULL for inference).  M = 0 is an empty batch. */
+ * backward (may be NULL for inference).  H is formed in the GEMM's epilogue from the fp32 G and
+ * U (sigmoid from the hardware exp2 and reciprocal) and rounded to bf16 once, as are G and U.
+ * M = 0 is an empty batch. */
 lora_status lora_swiglu_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                             const void* X, const void* Wgu, const void* Ag, const void* Au,
                             const void* Bg, const void* Bu, void* H, void* GU, float* XA,
