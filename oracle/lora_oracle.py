@@ -23,6 +23,9 @@ Sources are the web pages on Unsloth.  They are cited by page title and section:
   ``SwiGLU(x) = (W_g x ⊙ σ(W_g x)) ⊙ W_u x`` (σ the logistic function; the output
   projection W_d is another linear layer), with §5.3's LoRA update on the gate and
   on the up projection; gradients derived by hand from ``L = <dH, H>_F``.
+* RMSNorm: tutorial ch. 5 §5.4 "fused RMSNorm", ``x / sqrt(mean(x^2) + eps) * g``
+  over the hidden dimension, g a learnable per-feature scale; the gradients are
+  derived by hand from ``L = <dY, Y>_F``.
 * 4-bit weights: "探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3
   (4-bit weights read compactly, unpacked in registers by a scaling coefficient,
   restored to FP16/BF16 before the matrix units).  The concrete format (symmetric
@@ -288,3 +291,39 @@ def swiglu_lora_backward_dx_rows(dH, X, Wg, Wu, Ag, Au, Bg, Bu, scale, rows):
     dG = dHr * U * silu_grad(G)
     return (lora_backward_dx_rows(dG, Wg, Ag, Bg, scale, np.arange(len(rows)))
             + lora_backward_dx_rows(dU, Wu, Au, Bu, scale, np.arange(len(rows))))
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm (tutorial ch. 5 §5.4, fused RMSNorm: each row divided by the root of its mean
+# square plus eps, then scaled per feature by g; gradients derived by hand from L = <dY, Y>_F)
+# ---------------------------------------------------------------------------
+
+
+def rmsnorm_forward(X, g, eps):
+    """Y[m, k] = X[m, k] * r[m] * g[k] with r[m] = 1 / sqrt(mean_k X[m, k]^2 + eps).
+
+    X: M x K, g: K.  Returns (Y, r), float64: Y is M x K, r (the reciprocal RMS the
+    backward reuses) has M entries.
+    """
+    X, g = _f64(X, g)
+    ms = np.mean(X * X, axis=1)
+    r = 1.0 / np.sqrt(ms + float(eps))
+    return X * r[:, None] * g[None, :], r
+
+
+def rmsnorm_backward(dY, X, g, eps):
+    """Gradients of L = <dY, Y>_F: returns (dX, dg), float64.
+
+    With xh = X * r (row-wise) and dr / dX[m, j] = -r^3 X[m, j] / K:
+      dX[m, j] = r (g[j] dY[m, j] - xh[m, j] * (1/K) sum_k g[k] dY[m, k] xh[m, k]),
+      dg[k]    = sum_m dY[m, k] xh[m, k].
+    """
+    dY, X, g = _f64(dY, X, g)
+    K = X.shape[1]
+    _, r = rmsnorm_forward(X, g, eps)
+    xh = X * r[:, None]
+    gdy = dY * g[None, :]
+    c = np.sum(gdy * xh, axis=1) / K
+    dX = r[:, None] * (gdy - xh * c[:, None])
+    dg = np.sum(dY * xh, axis=0)
+    return dX, dg

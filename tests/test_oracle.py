@@ -466,3 +466,115 @@ def test_swiglu_dx_rows_matches_full():
     dX = oracle.swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, 2.0)[0]
     got = oracle.swiglu_lora_backward_dx_rows(dH, X, Wg, Wu, Ag, Au, Bg, Bu, 2.0, rows)
     np.testing.assert_allclose(got, dX[rows], rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm (tutorial ch. 5 §5.4)
+# ---------------------------------------------------------------------------
+
+
+def _rmsnorm_fixture(case):
+    f = _read_fixture("rmsnorm_worked_example.txt")
+    get = lambda k: [float(Fraction(v)) for v in f[f"{case}.{k}"]]
+    M, K = int(f[f"{case}.M"][0]), int(f[f"{case}.K"][0])
+    mat = lambda k: np.array(get(k)).reshape(M, K)
+    return dict(eps=get("eps")[0], g=np.array(get("g")), x=mat("x"), r=np.array(get("r")), y=mat("y"),
+                dy=mat("dy"), dx=mat("dx"), dg=np.array(get("dg")))
+
+
+@pytest.mark.parametrize("case", ["A", "B"])
+def test_rmsnorm_hand_worked_examples(case):
+    f = _rmsnorm_fixture(case)
+    Y, r = oracle.rmsnorm_forward(f["x"], f["g"], f["eps"])
+    np.testing.assert_allclose(r, f["r"], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(Y, f["y"], rtol=1e-15, atol=0)
+    dX, dg = oracle.rmsnorm_backward(f["dy"], f["x"], f["g"], f["eps"])
+    np.testing.assert_allclose(dX, f["dx"], rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(dg, f["dg"], rtol=1e-15, atol=1e-16)
+
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(60)
+    M, K = 7, 48
+    X = rng.standard_normal((M, K))
+    g = rng.uniform(0.5, 1.5, K)
+    # eps = 0: the output does not change when a row is scaled by a positive number
+    Y0, _ = oracle.rmsnorm_forward(X, g, 0.0)
+    for a in (1e-3, 7.0, 1e5):
+        np.testing.assert_allclose(oracle.rmsnorm_forward(a * X, g, 0.0)[0], Y0, rtol=1e-13, atol=0)
+    # the RMS of Y / g over a row is sqrt(ms / (ms + eps)); r from the Euclidean norm
+    eps = 0.3
+    Y, r = oracle.rmsnorm_forward(X, g, eps)
+    ms = np.linalg.norm(X, axis=1) ** 2 / K
+    np.testing.assert_allclose(np.sqrt(np.mean((Y / g) ** 2, axis=1)), np.sqrt(ms / (ms + eps)), rtol=1e-13)
+    np.testing.assert_allclose(r, (ms + eps) ** -0.5, rtol=1e-14)
+    # a constant row c gives c / sqrt(c^2 + eps) g
+    c = -2.5
+    Yc, _ = oracle.rmsnorm_forward(np.full((1, K), c), g, eps)
+    np.testing.assert_allclose(Yc[0], c / np.sqrt(c * c + eps) * g, rtol=1e-14)
+
+
+def _rmsnorm_case(rng, M, K):
+    return (rng.standard_normal((M, K)), rng.uniform(0.5, 1.5, K), rng.standard_normal((M, K)))
+
+
+def test_rmsnorm_backward_central_differences():
+    """L = <dY, Y> is smooth in X and g: central differences agree with the hand-derived
+    gradients to O(h^2)."""
+    rng = np.random.default_rng(61)
+    X, g, dY = _rmsnorm_case(rng, 5, 24)
+    eps = 0.05
+    dX, dg = oracle.rmsnorm_backward(dY, X, g, eps)
+    L = lambda X_, g_: float(np.sum(dY * oracle.rmsnorm_forward(X_, g_, eps)[0]))
+    h = 1e-5
+    num = np.zeros_like(X)
+    for idx in np.ndindex(*X.shape):
+        E = np.zeros_like(X)
+        E[idx] = h
+        num[idx] = (L(X + E, g) - L(X - E, g)) / (2 * h)
+    np.testing.assert_allclose(num, dX, rtol=1e-6, atol=1e-8)
+    numg = np.array([(L(X, g + h * np.eye(len(g))[k]) - L(X, g - h * np.eye(len(g))[k])) / (2 * h)
+                     for k in range(len(g))])
+    np.testing.assert_allclose(numg, dg, rtol=1e-6, atol=1e-8)
+
+
+def test_rmsnorm_against_torch_autograd_float64():
+    rng = np.random.default_rng(62)
+    X, g, dY = _rmsnorm_case(rng, 9, 40)
+    eps = 1e-5
+    tX = torch.tensor(X, requires_grad=True)
+    tg = torch.tensor(g, requires_grad=True)
+    tY = tX / torch.sqrt(torch.mean(tX * tX, dim=1, keepdim=True) + eps) * tg
+    tY.backward(torch.tensor(dY))
+    Y, _ = oracle.rmsnorm_forward(X, g, eps)
+    dX, dg = oracle.rmsnorm_backward(dY, X, g, eps)
+    np.testing.assert_allclose(Y, tY.detach().numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dX, tX.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dg, tg.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_rmsnorm_backward_invariants():
+    # <dX_m, X_m> = <dY_m, Y_m> eps r_m^2 per row (scaling a row changes Y only through eps);
+    # <dg, g> = <dY, Y> (Y is linear in g)
+    rng = np.random.default_rng(63)
+    X, g, dY = _rmsnorm_case(rng, 6, 32)
+    for eps in (0.0, 0.7):
+        Y, r = oracle.rmsnorm_forward(X, g, eps)
+        dX, dg = oracle.rmsnorm_backward(dY, X, g, eps)
+        np.testing.assert_allclose(np.sum(dX * X, axis=1), np.sum(dY * Y, axis=1) * eps * r * r, rtol=1e-10,
+                                   atol=1e-12)
+        np.testing.assert_allclose(np.dot(dg, g), np.sum(dY * Y), rtol=1e-12)
+
+
+def test_rmsnorm_planted_mistakes_fail_the_pins():
+    rng = np.random.default_rng(64)
+    X, g, dY = _rmsnorm_case(rng, 4, 16)
+    eps = 0.0
+    Y, r = oracle.rmsnorm_forward(X, g, eps)
+    # backward without the mean term: dX = r g dY breaks <dX, X> = 0 at eps = 0
+    wrong_dx = r[:, None] * g[None, :] * dY
+    assert np.max(np.abs(np.sum(wrong_dx * X, axis=1))) > 1e-3
+    # sum instead of mean of the squares breaks the RMS closed form
+    wrong_r = 1.0 / np.sqrt(np.sum(X * X, axis=1) + eps)
+    assert not np.allclose(np.sqrt(np.mean((X * wrong_r[:, None]) ** 2, axis=1)), 1.0, rtol=1e-3)
+    np.testing.assert_allclose(np.sqrt(np.mean((Y / g) ** 2, axis=1)), 1.0, rtol=1e-13)
