@@ -19,6 +19,7 @@ projection layer run unfused through torch (hipBLASLt GEMMs), for comparison.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -244,6 +245,66 @@ def bench_swiglu(lora, torch, dev, reps):
             "note": "gate and up projections as one LoRA GEMM over the stacked weight, H = silu(G) * U in its epilogue"}
 
 
+def bench_rmsnorm(lora, torch, dev, reps):
+    """RMSNorm ahead of a projection at the hidden-state shapes of the attention projection
+    (M=8192, K=4096) and the QLoRA FFN (M=4096, K=5120): forward, backward with g frozen and with
+    dg, rotating over buffer sets whose total exceeds the 256 MB MALL so that HBM is measured.
+    Algorithmic bytes: every row read and written once (forward X in, Y out; backward dY and X in,
+    dX out), plus g, r and dg."""
+    from qlora_fine_tuning_amd.workloads import make_norm_inputs
+
+    out = []
+    stream = torch.cuda.current_stream()
+    for M, K in ((8192, 4096), (4096, 5120)):
+        inp = make_norm_inputs(M, K, seed=7)
+        copies = max(3, -(-640 * 2**20 // (6 * M * K)))  # > 640 MB touched per rotation
+        X0 = dev_bits(inp.X, dev)
+        g = dev_bits(inp.g, dev)
+        Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
+        dYs = [dev_bits(inp.dY, dev)] + [None] * (copies - 1)
+        for i in range(1, copies):
+            dYs[i] = dYs[0].clone()
+        Ys = [torch.empty_like(X0) for _ in range(copies)]
+        rs = [torch.empty(M, dtype=torch.float32, device=dev) for _ in range(copies)]
+        dXs = [torch.empty_like(X0) for _ in range(copies)]
+        dg = torch.empty(K, dtype=torch.float32, device=dev)
+        ws = torch.empty(lora.lora_rmsnorm_bwd_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+        # the calls are ~20 us: the C entry points are called with arguments marshalled once, so
+        # that Python's per-call cost does not set the pace
+        lib, sp = lora.load(), ctypes.c_void_p(stream.cuda_stream)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        fargs = [(M, K, inp.eps, p(Xs[i]), p(g), p(Ys[i]), p(rs[i]), sp) for i in range(copies)]
+        bargs = {dgf: [(M, K, p(dYs[i]), p(Xs[i]), p(g), p(rs[i]), p(dXs[i]), p(dg) if dgf else None,
+                        p(ws) if dgf else None, ws.numel() if dgf else 0, sp) for i in range(copies)]
+                 for dgf in (False, True)}
+        state = {"i": 0}
+
+        def fwd():
+            i = state["i"] = (state["i"] + 1) % copies
+            assert lib.lora_rmsnorm_fwd(*fargs[i]) == 0
+
+        def bwd(need_dg):
+            def call():
+                i = state["i"] = (state["i"] + 1) % copies
+                assert lib.lora_rmsnorm_bwd(*bargs[need_dg][i]) == 0
+            return call
+
+        row = {"workload": "rmsnorm", "M": M, "K": K}
+        for name, fn, nbytes in (("fwd", fwd, 4 * M * K + 2 * K + 4 * M),
+                                 ("bwd", bwd(False), 6 * M * K + 2 * K + 4 * M),
+                                 ("bwd_dg", bwd(True), 6 * M * K + 2 * K + 4 * M + 4 * K)):
+            for _ in range(copies):
+                fn()
+            torch.cuda.synchronize()
+            ms = event_time_ms(fn, reps * copies, stream)
+            row[name + "_us"] = round(ms * 1e3, 2)
+            row[name + "_GB/s"] = round(nbytes / ms / 1e6, 1)
+            row[name + "_frac_hbm_peak"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)
+        out.append(row)
+        del Xs, dYs, Ys, dXs
+    return out
+
+
 def bench_decode(lora, torch, dev, reps, copies=6):
     """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL)."""
     from qlora_fine_tuning_amd.workloads import workload_inputs
@@ -384,6 +445,7 @@ def main(argv=None):
                                "mlp_swiglu": bench_swiglu(lora, torch, dev, 20),
                                "qlora": bench_qlora_ffn(lora, torch, dev, 20),
                                "decode": bench_decode(lora, torch, dev, 20),
+                               "rmsnorm": bench_rmsnorm(lora, torch, dev, 20),
                                "torch_unfused": bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}
     if args.calib_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -61,7 +61,7 @@ typedef enum lora_status {
   LORA_ERR_DTYPE = 5,     /* unknown element type */
   LORA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the matching *_workspace_bytes() */
   LORA_ERR_GROUP = 7,     /* int4 group size other than 64 */
-  LORA_ERR_VALUE = 8,     /* scale not finite */
+  LORA_ERR_VALUE = 8,     /* scale not finite, or eps not finite and >= 0 */
   LORA_ERR_HIP = 9        /* a HIP launch failed; lora_last_hip_error() names it */
 } lora_status;
 
@@ -201,6 +201,34 @@ lora_status lora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float sc
                             const void* Au, const void* Bg, const void* Bu, const void* GU,
                             const float* XA, void* dX, float* dAg, float* dAu, float* dBg,
                             float* dBu, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- RMSNorm ahead of a projection ------------------------------------------------------
+ * Tutorial ch. 5 §5.4 (fused RMSNorm: the mean square of each row, eps, the root and the
+ * per-feature scale g in one kernel that reads and writes the hidden state once):
+ *   r[m] = 1 / sqrt((1/K) sum_k X[m][k]^2 + eps),   Y[m][k] = X[m][k] r[m] g[k].
+ * Y is the X of the following lora_fwd / qlora_fwd / lora_swiglu_fwd, and of their backward
+ * (dA needs it), so the caller keeps it.  X, Y (M x K) and g (K) bf16, r (M) fp32; K a multiple
+ * of 64 in [64, 16384]; M >= 0; eps finite and >= 0 (with eps = 0 an all-zero row gives
+ * non-finite output, as the formula does).  Sums and products in fp32, Y rounded to bf16 once.
+ * X, Y, g 16-byte aligned; r 4-byte aligned.  Errors: LORA_ERR_SHAPE, LORA_ERR_VALUE (eps),
+ * LORA_ERR_NULL, LORA_ERR_ALIGN, LORA_ERR_HIP.  M = 0 is an empty batch (X, Y, r may be NULL). */
+lora_status lora_rmsnorm_fwd(int64_t M, int64_t K, float eps, const void* X, const void* g,
+                             void* Y, float* r, void* stream);
+
+/* Bytes of device workspace lora_rmsnorm_bwd needs when it computes dg (the per-workgroup dg
+ * partials); none is needed without dg. */
+size_t lora_rmsnorm_bwd_workspace_bytes(int64_t M, int64_t K);
+
+/* Backward, hand-derived from L = <dY, Y> with xh = X r (r from the forward):
+ *   dX[m][j] = r[m] (g[j] dY[m][j] - xh[m][j] c[m]),  c[m] = (1/K) sum_k g[k] dY[m][k] xh[m][k],
+ *   dg[k]    = sum_m dY[m][k] xh[m][k].
+ * dY, X, dX (M x K) and g bf16; r (M) fp32 as the forward wrote it; dg (K) fp32, overwritten, or
+ * NULL when g is frozen (the LoRA / QLoRA case; then ws may be NULL).  With dg the workspace
+ * holds lora_rmsnorm_bwd_workspace_bytes(M, K) bytes (16-byte aligned, no initialisation) and
+ * the partials are added in a fixed order.  M = 0 gives dg = 0. */
+lora_status lora_rmsnorm_bwd(int64_t M, int64_t K, const void* dY, const void* X, const void* g,
+                             const float* r, void* dX, float* dg, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* lora_status_str(lora_status s);

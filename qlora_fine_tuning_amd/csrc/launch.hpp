@@ -79,6 +79,17 @@ int dx_tiles(int64_t M, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K, int R);
 size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R);
 hipError_t launch_dadb_partials_bf16(const DadbArgs& a, hipStream_t s);
+// RMSNorm ahead of a projection: forward (Y, reciprocal RMS r) and backward (dX, optional dg
+// from per-workgroup partials and their slice sums in `part`, rmsnorm_bwd_part_floats() fp32)
+constexpr int kNormCUs = 256;         // MI355X compute units: the persistent grids' unit
+constexpr int64_t kNormMaxK = 16384;  // the forward holds a row in registers: 32 chunks per lane
+int rmsnorm_bwd_grid(int64_t M, int64_t K, bool dg);
+size_t rmsnorm_bwd_part_floats(int64_t M, int64_t K);
+hipError_t launch_rmsnorm_fwd(const uint16_t* X, const uint16_t* g, uint16_t* Y, float* r, int64_t M, int64_t K,
+                              float eps, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g, const float* r, uint16_t* dX,
+                              float* dg, float* part, int64_t M, int64_t K, hipStream_t s);
+
 // SwiGLU gate/up pair over the stacked weight [Wg; Wu]: stacked adapters, activation, upstream
 // gradient of the stacked GEMM, and the split of the stacked adapter gradients
 hipError_t launch_swiglu_stack(const uint16_t* Ag, const uint16_t* Au, const uint16_t* Bg, const uint16_t* Bu,

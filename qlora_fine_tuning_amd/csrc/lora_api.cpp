@@ -406,3 +406,64 @@ lora_status lora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float sc
 }
 
 }  // extern "C"
+
+// ---- RMSNorm ahead of a projection ----
+
+namespace {
+
+lora_status check_norm(int64_t M, int64_t K) {
+  if (M < 0 || M >= kMaxElems || K < 64 || K % 64 != 0 || K > kNormMaxK) return LORA_ERR_SHAPE;
+  if (M * K >= kMaxElems) return LORA_ERR_SHAPE;
+  return LORA_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+lora_status lora_rmsnorm_fwd(int64_t M, int64_t K, float eps, const void* X, const void* g, void* Y, float* r,
+                             void* stream) {
+  lora_status st = check_norm(M, K);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.f) return LORA_ERR_VALUE;
+  st = check_ptrs(g);
+  if (st != LORA_OK) return st;
+  if (M == 0) return LORA_OK;  // empty batch: X, Y and r may be NULL
+  st = check_ptrs(X, Y);
+  if (st != LORA_OK) return st;
+  if (r == nullptr) return LORA_ERR_NULL;
+  if (!aligned4(r)) return LORA_ERR_ALIGN;
+  return from_hip(launch_rmsnorm_fwd(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(g),
+                                     static_cast<uint16_t*>(Y), r, M, K, eps, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_rmsnorm_bwd_workspace_bytes(int64_t M, int64_t K) {
+  if (check_norm(M, K) != LORA_OK) return 0;
+  return rmsnorm_bwd_part_floats(M, K) * 4;
+}
+
+lora_status lora_rmsnorm_bwd(int64_t M, int64_t K, const void* dY, const void* X, const void* g, const float* r,
+                             void* dX, float* dg, void* ws, size_t ws_bytes, void* stream) {
+  lora_status st = check_norm(M, K);
+  if (st != LORA_OK) return st;
+  st = check_ptrs(g);
+  if (st != LORA_OK) return st;
+  if (dg != nullptr) {  // dg comes from per-workgroup partials in the workspace
+    if (!aligned4(dg)) return LORA_ERR_ALIGN;
+    if (M > 0 && (ws == nullptr || ws_bytes < lora_rmsnorm_bwd_workspace_bytes(M, K))) return LORA_ERR_WORKSPACE;
+    if (ws != nullptr && !aligned16(ws)) return LORA_ERR_ALIGN;
+  }
+  if (M > 0) {  // empty batch: dY, X, r and dX may be NULL
+    st = check_ptrs(dY, X, dX);
+    if (st != LORA_OK) return st;
+    if (r == nullptr) return LORA_ERR_NULL;
+    if (!aligned4(r)) return LORA_ERR_ALIGN;
+  }
+  return from_hip(launch_rmsnorm_bwd(static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(X),
+                                     static_cast<const uint16_t*>(g), r, static_cast<uint16_t*>(dX), dg,
+                                     static_cast<float*>(ws), M, K, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -42,6 +42,9 @@ SIGNATURES = {
     "lora_swiglu_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "lora_swiglu_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "lora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32] + [_p] * 15 + [_sz, _p]),
+    "lora_rmsnorm_fwd": (_i32, [_i64, _i64, _f32, _p, _p, _p, _p, _p]),
+    "lora_rmsnorm_bwd_workspace_bytes": (_sz, [_i64, _i64]),
+    "lora_rmsnorm_bwd": (_i32, [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -385,3 +388,64 @@ class SwiGLULoRAFunction(torch.autograd.Function):
         X, Wgu, Ag, Au, Bg, Bu, GU, XA = ctx.saved_tensors
         dX, dAg, dAu, dBg, dBu = lora_swiglu_bwd(dH.contiguous(), X, Wgu, Ag, Au, Bg, Bu, GU, XA, ctx.scale)
         return dX, None, dAg.to(Ag.dtype), dAu.to(Au.dtype), dBg.to(Bg.dtype), dBu.to(Bu.dtype), None
+
+
+def lora_rmsnorm_fwd(X, g, eps: float, *, Y=None, r=None, stream=None):
+    """RMSNorm of the rows of X (M x K bf16) with the per-feature scale g (K bf16).  Returns
+    (Y, r): Y (M x K bf16), the input of the following projection; r (M fp32), the reciprocal RMS
+    the backward reuses."""
+    lib = load()
+    _want(X, "X", torch.bfloat16)
+    _want(g, "g", torch.bfloat16)
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty_like(X)
+    if r is None:
+        r = torch.empty(M, dtype=torch.float32, device=X.device)
+    st = lib.lora_rmsnorm_fwd(M, K, float(eps), _ptr(X), _ptr(g), _ptr(Y), _ptr(r), _stream(stream))
+    _check("lora_rmsnorm_fwd", st)
+    return Y, r
+
+
+def lora_rmsnorm_bwd_workspace_bytes(M: int, K: int) -> int:
+    return int(load().lora_rmsnorm_bwd_workspace_bytes(M, K))
+
+
+def lora_rmsnorm_bwd(dY, X, g, r, *, need_dg: bool = True, dX=None, dg=None, ws=None, stream=None):
+    """Returns (dX, dg): dX (M x K bf16); dg (K fp32), or None when need_dg is False (g frozen)."""
+    lib = load()
+    for t, n in ((dY, "dY"), (X, "X"), (g, "g")):
+        _want(t, n, torch.bfloat16)
+    _want(r, "r", torch.float32)
+    M, K = X.shape
+    if dX is None:
+        dX = torch.empty_like(X)
+    if need_dg:
+        if dg is None:
+            dg = torch.empty(K, dtype=torch.float32, device=X.device)
+        if ws is None:
+            ws = torch.empty(max(lora_rmsnorm_bwd_workspace_bytes(M, K), 1), dtype=torch.uint8, device=X.device)
+    else:
+        dg = None
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib.lora_rmsnorm_bwd(M, K, _ptr(dY), _ptr(X), _ptr(g), _ptr(r), _ptr(dX), _ptr(dg), _ptr(ws), nbytes,
+                              _stream(stream))
+    _check("lora_rmsnorm_bwd", st)
+    return dX, dg
+
+
+class RMSNormFunction(torch.autograd.Function):
+    """Autograd wrapper of the RMSNorm ahead of a projection: the forward saves X and the
+    reciprocal RMS; dg is computed only when g requires a gradient."""
+
+    @staticmethod
+    def forward(ctx, X, g, eps):
+        Y, r = lora_rmsnorm_fwd(X, g, eps)
+        ctx.save_for_backward(X, g, r)
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, g, r = ctx.saved_tensors
+        dX, dg = lora_rmsnorm_bwd(dY.contiguous(), X, g, r, need_dg=ctx.needs_input_grad[1])
+        return dX, (dg.to(g.dtype) if dg is not None else None), None

@@ -165,3 +165,27 @@ def make_swiglu_inputs(M: int, N: int, K: int, R: int, *, seed: int, alpha: Opti
     r = lambda v: None if v is None else _round(v, "bf16")
     return SwigluInputs(M=M, N=N, K=K, R=R, alpha=float(alpha), seed=seed, X=r(X), Wg=r(Wg), Wu=r(Wu),
                         Ag=r(Ag), Au=r(Au), Bg=r(Bg), Bu=r(Bu), dH=r(dH))
+
+
+@dataclass
+class NormInputs:
+    """Seeded inputs of the RMSNorm ahead of a projection, as bf16 bit patterns (uint16)."""
+    M: int
+    K: int
+    eps: float
+    seed: int
+    X: np.ndarray   # M x K
+    g: np.ndarray   # K
+    dY: Optional[np.ndarray]  # M x K
+
+
+def make_norm_inputs(M: int, K: int, *, seed: int, eps: float = 1e-5, with_dy: bool = True) -> NormInputs:
+    """Draw an RMSNorm input set: hidden-state rows X ~ N(0, 1) each scaled by exp(U(-2, 2)) (rows
+    of different magnitude, so the reciprocal RMS varies over e^4), the per-feature scale
+    g ~ U(0.5, 1.5), and dY ~ N(0, 1); drawn in that order and rounded once to bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = rng.standard_normal((M, K)) * np.exp(rng.uniform(-2.0, 2.0, size=(M, 1)))
+    g = rng.uniform(0.5, 1.5, size=K)
+    dY = rng.standard_normal((M, K)) if with_dy else None
+    return NormInputs(M=M, K=K, eps=float(eps), seed=seed, X=_round(X, "bf16"), g=_round(g, "bf16"),
+                      dY=None if dY is None else _round(dY, "bf16"))

@@ -217,3 +217,58 @@ def test_swiglu_workspace_sizes(lib):
     # the binding's wrappers return the same sizes
     assert lora.lora_swiglu_fwd_workspace_bytes(M, N, K, R) == fwd_need
     assert lora.lora_swiglu_bwd_workspace_bytes(M, N, K, R) == bwd_need
+
+
+# ---- RMSNorm ahead of a projection ------------------------------------------------------
+
+def norm_fwd(lib, M=64, K=256, eps=1e-5, **ptrs):
+    p = dict(X=P, g=P, Y=P, r=P)
+    p.update(ptrs)
+    return lib.lora_rmsnorm_fwd(M, K, eps, p["X"], p["g"], p["Y"], p["r"], None)
+
+
+def norm_bwd(lib, M=64, K=256, ws=P, ws_bytes=None, **ptrs):
+    names = ("dY", "X", "g", "r", "dX", "dg")
+    p = {n: P for n in names}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.lora_rmsnorm_bwd_workspace_bytes(M, K)
+    return lib.lora_rmsnorm_bwd(M, K, *(p[n] for n in names), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=96), 2), (dict(K=0), 2), (dict(K=32768), 2), (dict(M=-1), 2),
+    (dict(eps=-1.0), 8), (dict(eps=float("inf")), 8), (dict(eps=float("nan")), 8),
+    (dict(X=NUL), 1), (dict(g=NUL), 1), (dict(Y=NUL), 1), (dict(r=NUL), 1),
+    (dict(Y=MIS), 4), (dict(r=ctypes.c_void_p(0x1002)), 4),
+])
+def test_lora_rmsnorm_fwd_validation(lib, kw, code):
+    assert norm_fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=16448), 2), (dict(M=-1), 2),
+    (dict(dY=NUL), 1), (dict(X=NUL), 1), (dict(g=NUL), 1), (dict(r=NUL), 1), (dict(dX=NUL), 1),
+    (dict(dX=MIS), 4), (dict(ws=MIS), 4),
+    (dict(ws=NUL), 6), (dict(ws_bytes=1024), 6),
+])
+def test_lora_rmsnorm_bwd_validation(lib, kw, code):
+    assert norm_bwd(lib, **kw) == code
+
+
+def test_lora_rmsnorm_empty_batch_and_frozen_g(lib):
+    # M = 0 needs no row pointers; without dg no workspace is needed at all
+    assert norm_fwd(lib, M=0, X=NUL, Y=NUL, r=NUL) == 0
+    # dg = NULL, ws = NULL: the call is refused for the NULL dX, not for the workspace
+    assert lib.lora_rmsnorm_bwd(64, 256, P, P, P, P, None, None, None, 0, None) == 1
+    assert norm_bwd(lib, M=0, dY=NUL, X=NUL, r=NUL, dX=NUL, ws=NUL, ws_bytes=0, dg=NUL) == 0
+
+
+def test_rmsnorm_workspace_sizes(lib):
+    # one fp32 dg partial of K per workgroup of the backward (min(M, 512) of them), then one sum
+    # per slice of 32 partials
+    assert lib.lora_rmsnorm_bwd_workspace_bytes(8192, 4096) == (512 + 16) * 4096 * 4
+    assert lib.lora_rmsnorm_bwd_workspace_bytes(100, 5120) == (100 + 4) * 5120 * 4
+    assert lib.lora_rmsnorm_bwd_workspace_bytes(0, 4096) == 0
+    assert lib.lora_rmsnorm_bwd_workspace_bytes(64, 100) == 0
+    assert lora.lora_rmsnorm_bwd_workspace_bytes(8192, 4096) == (512 + 16) * 4096 * 4
