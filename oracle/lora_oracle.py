@@ -26,6 +26,11 @@ Sources are the web pages on Unsloth.  They are cited by page title and section:
 * RMSNorm: tutorial ch. 5 §5.4 "fused RMSNorm", ``x / sqrt(mean(x^2) + eps) * g``
   over the hidden dimension, g a learnable per-feature scale; the gradients are
   derived by hand from ``L = <dY, Y>_F``.
+* FP4 weights: the same page names FP4 beside INT4 for the 4-bit weights.  Its
+  format is read as the OCP Microscaling (MX) FP4: blocks of 32 consecutive k share
+  a power-of-two scale 2^(E-127) (E8M0), each element an E2M1 value (sign, 2
+  exponent bits with bias 1, 1 mantissa bit; no infinities or NaN), the block
+  exponent floor(log2(absmax)) - 2, round to nearest even with saturation at 6.
 * 4-bit weights: "探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3
   (4-bit weights read compactly, unpacked in registers by a scaling coefficient,
   restored to FP16/BF16 before the matrix units).  The concrete format (symmetric
@@ -327,3 +332,78 @@ def rmsnorm_backward(dY, X, g, eps):
     dX = r[:, None] * (gdy - xh * c[:, None])
     dg = np.sum(dY * xh, axis=0)
     return dX, dg
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 weights ("探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3 names FP4
+# beside INT4; the block format is the OCP Microscaling FP4: 32 E2M1 elements per E8M0 scale)
+# ---------------------------------------------------------------------------
+
+FP4_BLOCK = 32
+
+
+def fp4_e2m1_value(code):
+    """Value of 4-bit E2M1 codes from the bit fields: sign s (bit 3), exponent e (bits 2..1,
+    bias 1), mantissa m (bit 0); e = 0 is subnormal: m * 0.5, else (1 + m/2) * 2^(e-1)."""
+    c = np.asarray(code, dtype=np.int64)
+    s, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(s == 1, -mag, mag)
+
+
+def mxfp4_block_exponent(amax):
+    """Shared exponent of a block: floor(log2(amax)) - 2 (2 is E2M1's largest exponent), clamped to
+    [-125, 125] so that every nonzero element and the largest value stay normal in bf16; a block
+    of zeros takes 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))  # amax = f 2^ex, f in [0.5, 1)
+    se = np.clip(ex - 1 - 2, -125, 125)
+    return np.where(amax > 0, se, 0).astype(np.int64)
+
+
+def quantize_mxfp4(w):
+    """MXFP4 codes of an fp32 weight W (N x K, K a multiple of 32), decided on exact values.
+
+    Each element's magnitude |w| / 2^se is rounded to the nearest E2M1 magnitude
+    {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the one with mantissa bit 0, values past 6 to 6; the
+    sign bit is set for w < 0 (also when the magnitude rounds to 0).  Returns (codes, E): codes
+    uint8 in 0..15 (N x K), E = se + 127 as uint8 (N x K/32).
+    """
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    N, K = w.shape
+    if K % FP4_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blk = w.reshape(N, K // FP4_BLOCK, FP4_BLOCK)
+    se = mxfp4_block_exponent(np.max(np.abs(blk), axis=2))
+    x = np.abs(blk) / np.exp2(se)[:, :, None]  # exact: a power-of-two scaling
+    grid = fp4_e2m1_value(np.arange(8))
+    dist = np.abs(x[..., None] - grid)
+    best = dist.min(axis=-1, keepdims=True)
+    tied = dist == best
+    # among the nearest (one, or two at a midpoint) take the even code: its mantissa bit is 0
+    even = tied & (np.arange(8) % 2 == 0)
+    mag = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tied, axis=-1))
+    codes = (mag | np.where(blk < 0, 8, 0)).astype(np.uint8).reshape(N, K)
+    return codes, (se + 127).astype(np.uint8)
+
+
+def pack_fp4(codes):
+    """Two codes per byte, even k in the low nibble: N x K -> N x K/2 uint8."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_fp4(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = p & 15
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def dequant_mxfp4(packed, E):
+    """W~[n][k] = e2m1(code) * 2^(E[n][k/32] - 127), float64 (exact; also exact in bf16, since it has
+    at most two significant bits and the clamped exponents keep it normal)."""
+    codes = unpack_fp4(packed)
+    se = np.asarray(E, dtype=np.int64) - 127
+    return fp4_e2m1_value(codes) * np.exp2(np.repeat(se, FP4_BLOCK, axis=1))

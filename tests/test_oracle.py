@@ -578,3 +578,82 @@ def test_rmsnorm_planted_mistakes_fail_the_pins():
     wrong_r = 1.0 / np.sqrt(np.sum(X * X, axis=1) + eps)
     assert not np.allclose(np.sqrt(np.mean((X * wrong_r[:, None]) ** 2, axis=1)), 1.0, rtol=1e-3)
     np.testing.assert_allclose(np.sqrt(np.mean((Y / g) ** 2, axis=1)), 1.0, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 weights
+# ---------------------------------------------------------------------------
+
+
+def _mx_fixture():
+    f = _read_fixture("mxfp4_format_example.txt")
+    return f
+
+
+def test_mxfp4_code_table():
+    f = _mx_fixture()
+    np.testing.assert_array_equal(oracle.fp4_e2m1_value(np.arange(16)), [float(v) for v in f["values"]])
+    # the sign of code 8 is kept: -0.0
+    assert np.signbit(oracle.fp4_e2m1_value(8))
+
+
+@pytest.mark.parametrize("blk", ["A", "B", "C"])
+def test_mxfp4_hand_worked_blocks(blk):
+    f = _mx_fixture()
+    vals = [float(Fraction(v)) for v in f[f"{blk}.w"]]
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, :len(vals)] = vals
+    codes, E = oracle.quantize_mxfp4(w)
+    assert int(E[0, 0]) == int(f[f"{blk}.E"][0])
+    np.testing.assert_array_equal(codes[0, :len(vals)], [int(c) for c in f[f"{blk}.codes"]])
+    assert not codes[0, len(vals):].any()
+
+
+def test_mxfp4_packing():
+    f = _mx_fixture()
+    line = f["pack"]
+    i = line.index("->")
+    codes = np.array([[int(c) for c in line[:i]]], dtype=np.uint8)
+    want = [int(b, 16) for b in line[i + 1:]]
+    np.testing.assert_array_equal(oracle.pack_fp4(codes)[0], want)
+    np.testing.assert_array_equal(oracle.unpack_fp4(oracle.pack_fp4(codes)), codes)
+
+
+def test_mxfp4_round_trip_and_error_bound():
+    rng = np.random.default_rng(70)
+    N, K = 16, 256
+    w = (rng.standard_normal((N, K)) * np.exp(rng.uniform(-8, 8, size=(N, 1)))).astype(np.float32)
+    codes, E = oracle.quantize_mxfp4(w)
+    wt = oracle.dequant_mxfp4(oracle.pack_fp4(codes), E)
+    se = np.repeat(E.astype(np.int64) - 127, 32, axis=1)
+    x = np.abs(w.astype(np.float64)) / np.exp2(se)
+    # error within half the grid spacing at x (0.25 below 2, 0.5 below 4, 1 below 6), or the
+    # saturation gap past 6; the block's largest element is never below 4 after scaling
+    half = np.where(x <= 2, 0.25, np.where(x <= 4, 0.5, 1.0))
+    err = np.abs(w - wt) / np.exp2(se)
+    assert np.all(err <= np.maximum(half, x - 6) + 1e-12)
+    amax = np.abs(w).reshape(N, K // 32, 32).max(axis=2) / np.exp2(E.astype(np.int64) - 127)
+    assert np.all((amax >= 4) & (amax < 8))
+    # values already on the scaled grid come back exactly
+    g = oracle.fp4_e2m1_value(codes) * np.exp2(se)
+    c2, E2 = oracle.quantize_mxfp4(g.astype(np.float32))
+    np.testing.assert_array_equal(oracle.dequant_mxfp4(oracle.pack_fp4(c2), E2), oracle.fp4_e2m1_value(codes) * np.exp2(se))
+
+
+def test_mxfp4_exponent_clamps_and_zero_blocks():
+    w = np.zeros((1, 96), dtype=np.float32)
+    w[0, 32] = 2.0 ** -130  # tiny block: exponent clamped to -125 -> rounds to 0
+    w[0, 64] = 3.0e38        # huge block: floor(log2) = 127, se = 125
+    codes, E = oracle.quantize_mxfp4(w)
+    np.testing.assert_array_equal(E[0], [127, 2, 252])
+    assert codes[0, 32] == 0 and codes[0, 64] == 7 and not codes[0, :32].any()
+
+
+def test_mxfp4_planted_mistakes_fail_the_fixture():
+    # ties rounded away from zero would turn 2.5 into 3 and 0.25 into 0.5
+    grid = oracle.fp4_e2m1_value(np.arange(8))
+    x = np.array([5, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25])
+    away = np.array([np.argmin(np.abs(v - grid) - 1e-9 * grid) for v in x])
+    assert list(away) != [6, 6, 4, 4, 2, 2, 0]
+    # swapped nibbles would pack 6, 14 as 0x6E
+    assert int(oracle.pack_fp4(np.array([[6, 14]], dtype=np.uint8))[0, 0]) == 0xE6
