@@ -306,39 +306,49 @@ def bench_rmsnorm(lora, torch, dev, reps):
 
 
 def bench_decode(lora, torch, dev, reps, copies=6):
-    """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL)."""
+    """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL), with
+    the int4 weight (group 64, fp16 scales) and with the MXFP4 weight (blocks of 32, E8M0 scales):
+    both move 0.5 + 1/32 bytes per weight."""
     from qlora_fine_tuning_amd.workloads import workload_inputs
 
     out = []
-    for name in ("decode_up", "decode_down"):
-        inp = workload_inputs(name, M=8)
-        N, K, R = inp.N, inp.K, inp.R
-        Wq0, Ws0 = lora.qlora_quantize(torch.from_numpy(inp.W).to(dev))
-        Wqs = [Wq0] + [Wq0.clone() for _ in range(copies - 1)]
-        Wss = [Ws0] + [Ws0.clone() for _ in range(copies - 1)]
-        A, B = dev_bits(inp.A, dev), dev_bits(inp.B, dev)
-        Xall = dev_bits(inp.X, dev)
-        stream = torch.cuda.current_stream()
-        for M in (1, 4, 8):
-            X = Xall[:M].contiguous()
-            Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            ws = torch.zeros(max(lora.qlora_fwd_workspace_bytes(M, N, K, R), 256), dtype=torch.uint8, device=dev)
-            state = {"i": 0}
+    for fmt in ("int4", "mxfp4"):
+        for name in ("decode_up", "decode_down"):
+            inp = workload_inputs(name, M=8)
+            N, K, R = inp.N, inp.K, inp.R
+            W32 = torch.from_numpy(inp.W).to(dev)
+            Wq0, Ws0 = lora.qlora_quantize(W32) if fmt == "int4" else lora.mxfp4_quantize(W32)
+            del W32
+            Wqs = [Wq0] + [Wq0.clone() for _ in range(copies - 1)]
+            Wss = [Ws0] + [Ws0.clone() for _ in range(copies - 1)]
+            A, B = dev_bits(inp.A, dev), dev_bits(inp.B, dev)
+            Xall = dev_bits(inp.X, dev)
+            stream = torch.cuda.current_stream()
+            for M in (1, 4, 8):
+                X = Xall[:M].contiguous()
+                Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+                ws = torch.zeros(max(lora.qlora_fwd_workspace_bytes(M, N, K, R), 256), dtype=torch.uint8,
+                                 device=dev)
+                state = {"i": 0}
 
-            def call():
-                i = state["i"]
-                state["i"] = (i + 1) % copies
-                lora.qlora_fwd(X, Wqs[i], Wss[i], A, B, inp.scale, Y=Y, save_xa=False, ws=ws)
+                def call():
+                    i = state["i"]
+                    state["i"] = (i + 1) % copies
+                    if fmt == "int4":
+                        lora.qlora_fwd(X, Wqs[i], Wss[i], A, B, inp.scale, Y=Y, save_xa=False, ws=ws)
+                    else:
+                        lora.mxfp4_decode_fwd(X, Wqs[i], Wss[i], A, B, inp.scale, Y=Y, save_xa=False, ws=ws)
 
-            for _ in range(copies):
-                call()
-            torch.cuda.synchronize()
-            ms = event_time_ms(call, reps * copies, stream)
-            nbytes = N * K // 2 + N * (K // 64) * 2 + R * K * 2 + N * R * 2 + M * K * 2 + M * N * 2
-            out.append({"workload": name, "M": M, "N": N, "K": K, "us_per_call": round(ms * 1e3, 3),
-                        "GB/s": round(nbytes / ms / 1e6, 1),
-                        "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)})
-        del Wqs, Wss
+                for _ in range(copies):
+                    call()
+                torch.cuda.synchronize()
+                ms = event_time_ms(call, reps * copies, stream)
+                wbytes = N * K // 2 + (N * (K // 64) * 2 if fmt == "int4" else N * (K // 32))
+                nbytes = wbytes + R * K * 2 + N * R * 2 + M * K * 2 + M * N * 2
+                out.append({"workload": name, "weights": fmt, "M": M, "N": N, "K": K,
+                            "us_per_call": round(ms * 1e3, 3), "GB/s": round(nbytes / ms / 1e6, 1),
+                            "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)})
+            del Wqs, Wss
     return out
 
 

@@ -230,6 +230,41 @@ lora_status lora_rmsnorm_bwd(int64_t M, int64_t K, const void* dY, const void* X
                              const float* r, void* dX, float* dg, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* ---- MXFP4 weights (decode) ---------------------------------------------------------------
+ * "探微索隐：Unsloth 如何加速 LLM 推理？（以 Qwen 27B 为例）", §二.3 names FP4 beside INT4 for the
+ * 4-bit weights streamed in decode.  The format is the OCP Microscaling FP4: 32 consecutive k of a
+ * row share a scale 2^(E-127) stored as one byte E (E8M0); each element is a 4-bit E2M1 code (sign
+ * bit 3, exponent bits 2..1 with bias 1, mantissa bit 0; exponent 0 is subnormal: m/2), two per
+ * byte with even k in the low nibble.
+ *   Wq: N x K/2 bytes of codes;  We: N x K/32 bytes of E;  W~[n][k] = e2m1(code) * 2^(E - 127)
+ * (exact in bf16).  Bytes per weight: 0.5 + 1/32, as for the int4 format. */
+
+/* Quantise an fp32 weight (N x K, K a multiple of 64, finite values): per block of 32,
+ * se = floor(log2(absmax)) - 2 clamped to [-125, 125] (0 for a zero block), E = se + 127; each
+ * |w| / 2^se is rounded to the nearest E2M1 magnitude {0, 1/2, 1, 3/2, 2, 3, 4, 6}, ties to the
+ * one with mantissa bit 0 and values past 6 to 6, decided exactly; the sign bit is set for w < 0.
+ * W, Wq, We 16-byte aligned.  Errors: LORA_ERR_SHAPE, LORA_ERR_NULL, LORA_ERR_ALIGN, LORA_ERR_HIP. */
+lora_status mxfp4_quantize(int64_t N, int64_t K, const float* W, uint8_t* Wq, uint8_t* We,
+                           void* stream);
+
+/* W~ (N x K bf16) from the codes and exponents; E is read as 2^(E - 127) for E in 1..254. */
+lora_status mxfp4_dequant(int64_t N, int64_t K, const uint8_t* Wq, const uint8_t* We, void* W_bf16,
+                          void* stream);
+
+/* Bytes of device workspace mxfp4_decode_fwd needs (0 outside its shapes); the same layout and
+ * rule as qlora_fwd's decode path: the counters must be zero before the first call that uses the
+ * workspace, and every call leaves them zero. */
+size_t mxfp4_decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
+
+/* Decode forward with the MXFP4 weight: Y = X W~^T + scale (X A^T) B^T for 1 <= M <= 8 tokens and
+ * K a multiple of 1024 (other shapes: LORA_ERR_SHAPE), in the one-kernel decode product of
+ * qlora_fwd with the E2M1 codes unpacked by the gfx950 scaled conversion.  X (M x K), A, B, Y
+ * bf16; XA (M x R fp32, unscaled) may be NULL. */
+lora_status mxfp4_decode_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                             const void* X, const uint8_t* Wq, const uint8_t* We, const void* A,
+                             const void* B, void* Y, float* XA, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* lora_status_str(lora_status s);
 

@@ -72,6 +72,93 @@ dequant_int4_kernel(const uint8_t* __restrict__ Wq, const uint16_t* __restrict__
   for (int d = 0; d < 4; ++d) st16(dst + 8 * d, dequant8_mix(w[d], sc));
 }
 
+// ---- MXFP4 (the FP4 of §二.3, read as the OCP Microscaling FP4 block format) -------------
+// 32 consecutive k share a power-of-two scale 2^(E - 127) (one byte, E8M0); each element is an
+// E2M1 code (sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0) in the same nibble
+// layout as the int4 codes.  Block exponent se = floor(log2(absmax)) - 2, clamped to [-125, 125]
+// so that every nonzero value and scale stay normal; a block of zeros takes se = 0.
+
+// quantise + pack: one thread per (row, block of 32).  x = |w| 2^-se is exact wherever it can
+// reach a rounding threshold (>= 0.25), so the code is the exact decision: nearest E2M1
+// magnitude, ties to mantissa bit 0, past 6 to 6, written as counts of thresholds passed.
+__global__ void __launch_bounds__(256)
+quantize_mxfp4_kernel(const float* __restrict__ W, uint8_t* __restrict__ Wq, uint8_t* __restrict__ We,
+                      int64_t blocks, int K) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= blocks) return;
+  const int bpr = K / 32;
+  const int64_t row = b / bpr, bi = b - row * bpr;
+  const float* src = W + row * K + bi * 32;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(src + 4 * i);
+    v[4 * i] = t[0];
+    v[4 * i + 1] = t[1];
+    v[4 * i + 2] = t[2];
+    v[4 * i + 3] = t[3];
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+  // floor(log2 a) from the exponent field (a subnormal a clamps to -125 either way)
+  const int ex = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  const int se = a == 0.f ? 0 : min(max(ex - 2, -125), 125);
+  const float inv = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, normal
+  uint32_t words[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t wv = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float w = v[8 * d + i], x = fabsf(w) * inv;
+      uint32_t c = (uint32_t)(x > 0.25f) + (uint32_t)(x >= 0.75f) + (uint32_t)(x > 1.25f) + (uint32_t)(x >= 1.75f) +
+                   (uint32_t)(x > 2.5f) + (uint32_t)(x >= 3.5f) + (uint32_t)(x > 5.f);
+      c |= w < 0.f ? 8u : 0u;
+      wv |= c << (4 * i);
+    }
+    words[d] = wv;
+  }
+  st16(Wq + row * (K / 2) + bi * 16, (u32x4){words[0], words[1], words[2], words[3]});
+  We[b] = (uint8_t)(se + 127);
+}
+
+// E2M1 pairs to bf16 with the block scale, on the gfx950 conversion instruction: byte `sel` of
+// `codes` (low nibble first) becomes the low and high bf16 of the result, value * scale (exact
+// here: at most two significant bits, normal exponents)
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t codes, float scale, int sel) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t r;
+  switch (sel) {  // the selector must be a constant
+    case 0: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0); break;
+    case 1: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1); break;
+    case 2: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2); break;
+    default: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3); break;
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+// 8 codes (one dword, k ascending from the low nibble) to 8 bf16 in k order
+__device__ __forceinline__ u32x4 dequant8_fp4(uint32_t codes, float scale) {
+  return (u32x4){fp4x2_to_bf16x2(codes, scale, 0), fp4x2_to_bf16x2(codes, scale, 1),
+                 fp4x2_to_bf16x2(codes, scale, 2), fp4x2_to_bf16x2(codes, scale, 3)};
+}
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }  // E >= 2 here
+
+// dequantise: one thread per block of 32 codes
+__global__ void __launch_bounds__(256)
+dequant_mxfp4_kernel(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ We, uint16_t* __restrict__ Wout,
+                     int64_t blocks, int K) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= blocks) return;
+  const int bpr = K / 32;
+  const int64_t row = b / bpr, bi = b - row * bpr;
+  const u32x4 w = ld16(Wq + row * (K / 2) + bi * 16);
+  const float sc = e8m0_to_f32(We[b]);
+  uint16_t* dst = Wout + row * K + bi * 32;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) st16(dst + 8 * d, dequant8_fp4(w[d], sc));
+}
+
 // ---- decode matrix-vector product, M <= 8 --------------------------------------------
 // One kernel per call, bound by the bandwidth of streaming the packed weight once.
 //
@@ -218,7 +305,9 @@ __device__ void decode_adapter(const DecodeArgs& a, int xw, float* sred, int* sf
   if (tid == 0) __hip_atomic_store(ctl + 2 * T, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int RP>
+// FP4: the weight is MXFP4 (a.Ws then holds the E8M0 bytes: 16 per row and 512-k step, the same
+// bytes per step as the int4 scales, so the staging is shared)
+template <int RP, bool FP4>
 __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint8_t sW0[4 * kDecStage];
   __shared__ __align__(16) uint8_t sW1[4 * kDecStage];
@@ -305,17 +394,32 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
   auto compute = [&](const uint8_t* sW, const uint8_t* sX, const uint32_t* sS) {
     const uint8_t* stage = sW + w * kDecStage + r16 * 256;
     const uint8_t* xl = sX + t * kDecXRow + 256 * g4;
-    const uint32_t sc = sS[w * 64 + r16 * 4 + g4];  // scales of groups 2 g4, 2 g4 + 1
-    const I4Mix m0 = i4mix(half_bits_to_f32((uint16_t)(sc & 0xffffu)));
-    const I4Mix m1 = i4mix(half_bits_to_f32((uint16_t)(sc >> 16)));
+    // int4: the fp16 scales of groups 2 g4, 2 g4 + 1; FP4: the E8M0 bytes of blocks 4 g4 .. +3,
+    // block 4 g4 + i being piece i
+    const uint32_t sc = sS[w * 64 + r16 * 4 + g4];
+    if constexpr (FP4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(stage + 16 * ((4 * g4 + i) ^ r16));
-      const I4Mix& mx = (i < 2) ? m0 : m1;
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(stage + 16 * ((4 * g4 + i) ^ r16));
+        const float bs = e8m0_to_f32((sc >> (8 * i)) & 0xffu);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 xf = *reinterpret_cast<const u32x4*>(xl + 64 * i + 16 * j);
-        acc[j & 1] = mfma16(dequant8_mix(wv[j], mx), xf, acc[j & 1]);
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 xf = *reinterpret_cast<const u32x4*>(xl + 64 * i + 16 * j);
+          acc[j & 1] = mfma16(dequant8_fp4(wv[j], bs), xf, acc[j & 1]);
+        }
+      }
+    } else {
+      const I4Mix m0 = i4mix(half_bits_to_f32((uint16_t)(sc & 0xffffu)));
+      const I4Mix m1 = i4mix(half_bits_to_f32((uint16_t)(sc >> 16)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(stage + 16 * ((4 * g4 + i) ^ r16));
+        const I4Mix& mx = (i < 2) ? m0 : m1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 xf = *reinterpret_cast<const u32x4*>(xl + 64 * i + 16 * j);
+          acc[j & 1] = mfma16(dequant8_mix(wv[j], mx), xf, acc[j & 1]);
+        }
       }
     }
   };
@@ -446,6 +550,21 @@ hipError_t launch_quantize_int4(int64_t N, int64_t K, const float* W, uint8_t* W
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_mxfp4(int64_t N, int64_t K, const float* W, uint8_t* Wq, uint8_t* We, hipStream_t s) {
+  const int64_t blocks = N * (K / 32);
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s, W, Wq, We,
+                     blocks, (int)K);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mxfp4(int64_t N, int64_t K, const uint8_t* Wq, const uint8_t* We, uint16_t* Wout,
+                                hipStream_t s) {
+  const int64_t blocks = N * (K / 32);
+  hipLaunchKernelGGL(dequant_mxfp4_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s, Wq, We, Wout,
+                     blocks, (int)K);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant_int4(int64_t N, int64_t K, const uint8_t* Wq, const uint16_t* Ws,
                                uint16_t* Wout, hipStream_t s) {
   const int64_t chunks = N * (K / 32);
@@ -484,7 +603,8 @@ static DecodeLayout decode_layout(int64_t M, int64_t N, int64_t K, int R) {
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int R) { return decode_layout(M, N, K, R).total; }
 
-hipError_t launch_gemv_int4(const FwdArgs& f, void* ws, hipStream_t s) {
+template <bool FP4>
+static hipError_t launch_gemv(const FwdArgs& f, void* ws, hipStream_t s) {
   const DecodeLayout l = decode_layout(f.M, f.N, f.K, f.R);
   char* base = static_cast<char*>(ws);
   DecodeArgs a;
@@ -510,12 +630,15 @@ hipError_t launch_gemv_int4(const FwdArgs& f, void* ws, hipStream_t s) {
   const dim3 grid((unsigned)(a.NXA + (f.N / kDecRows) * a.S));
   const int RP = decode_rp(f.R);
   if (RP == 16)
-    hipLaunchKernelGGL((decode_int4_kernel<16>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_int4_kernel<16, FP4>), grid, dim3(256), 0, s, a);
   else if (RP == 32)
-    hipLaunchKernelGGL((decode_int4_kernel<32>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_int4_kernel<32, FP4>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_int4_kernel<64>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_int4_kernel<64, FP4>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+hipError_t launch_gemv_int4(const FwdArgs& f, void* ws, hipStream_t s) { return launch_gemv<false>(f, ws, s); }
+hipError_t launch_gemv_mxfp4(const FwdArgs& f, void* ws, hipStream_t s) { return launch_gemv<true>(f, ws, s); }
 
 }  // namespace lora

@@ -112,6 +112,12 @@ hipError_t launch_dequant_int4(int64_t N, int64_t K, const uint8_t* Wq, const ui
 // decode path (M <= 8): `ws` holds gemv_workspace_bytes() bytes whose leading per-tile
 // arrival counters are zero before the call and are left zero by it
 hipError_t launch_gemv_int4(const FwdArgs& a, void* ws, hipStream_t s);
+// MXFP4 weights: codes (N x K/2 bytes, int4 nibble layout) and E8M0 block exponents (N x K/32
+// bytes); the decode product takes them in a.W and a.Ws
+hipError_t launch_quantize_mxfp4(int64_t N, int64_t K, const float* W, uint8_t* Wq, uint8_t* We, hipStream_t s);
+hipError_t launch_dequant_mxfp4(int64_t N, int64_t K, const uint8_t* Wq, const uint8_t* We, uint16_t* Wout,
+                                hipStream_t s);
+hipError_t launch_gemv_mxfp4(const FwdArgs& a, void* ws, hipStream_t s);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int R);
 
 }  // namespace lora

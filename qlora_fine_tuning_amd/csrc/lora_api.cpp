@@ -467,3 +467,48 @@ lora_status lora_rmsnorm_bwd(int64_t M, int64_t K, const void* dY, const void* X
 }
 
 }  // extern "C"
+
+// ---- MXFP4 weights and their decode product ----
+
+extern "C" {
+
+lora_status mxfp4_quantize(int64_t N, int64_t K, const float* W, uint8_t* Wq, uint8_t* We, void* stream) {
+  if (N <= 0 || K <= 0 || K % 64 != 0 || N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems)
+    return LORA_ERR_SHAPE;
+  lora_status st = check_ptrs(W, Wq, We);
+  if (st != LORA_OK) return st;
+  return from_hip(launch_quantize_mxfp4(N, K, W, Wq, We, static_cast<hipStream_t>(stream)));
+}
+
+lora_status mxfp4_dequant(int64_t N, int64_t K, const uint8_t* Wq, const uint8_t* We, void* W_bf16, void* stream) {
+  if (N <= 0 || K <= 0 || K % 64 != 0 || N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems)
+    return LORA_ERR_SHAPE;
+  lora_status st = check_ptrs(Wq, We, W_bf16);
+  if (st != LORA_OK) return st;
+  return from_hip(launch_dequant_mxfp4(N, K, Wq, We, static_cast<uint16_t*>(W_bf16),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t mxfp4_decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (check_dims(M, N, K, R) != LORA_OK || !use_gemv(M, K)) return 0;
+  return gemv_workspace_bytes(M, N, K, R);
+}
+
+lora_status mxfp4_decode_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, const void* X, const uint8_t* Wq,
+                             const uint8_t* We, const void* A, const void* B, void* Y, float* XA, void* ws,
+                             size_t ws_bytes, void* stream) {
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (M < 1 || M > 8 || K % 1024 != 0) return LORA_ERR_SHAPE;  // the decode shapes only
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(X, Wq, We, A, B, Y);
+  if (st != LORA_OK) return st;
+  if (XA != nullptr && !aligned16(XA)) return LORA_ERR_ALIGN;
+  const size_t need = mxfp4_decode_workspace_bytes(M, N, K, R);
+  if (ws == nullptr || ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  const FwdArgs a{X, Wq, We, A, B, Y, XA, M, N, K, R, scale};
+  return from_hip(launch_gemv_mxfp4(a, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -45,6 +45,10 @@ SIGNATURES = {
     "lora_rmsnorm_fwd": (_i32, [_i64, _i64, _f32, _p, _p, _p, _p, _p]),
     "lora_rmsnorm_bwd_workspace_bytes": (_sz, [_i64, _i64]),
     "lora_rmsnorm_bwd": (_i32, [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "mxfp4_quantize": (_i32, [_i64, _i64, _p, _p, _p, _p]),
+    "mxfp4_dequant": (_i32, [_i64, _i64, _p, _p, _p, _p]),
+    "mxfp4_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "mxfp4_decode_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -449,3 +453,49 @@ class RMSNormFunction(torch.autograd.Function):
         X, g, r = ctx.saved_tensors
         dX, dg = lora_rmsnorm_bwd(dY.contiguous(), X, g, r, need_dg=ctx.needs_input_grad[1])
         return dX, (dg.to(g.dtype) if dg is not None else None), None
+
+
+def mxfp4_quantize(W32, *, stream=None):
+    """MXFP4 codes and E8M0 block exponents of an fp32 weight (N x K): (Wq uint8 N x K/2,
+    We uint8 N x K/32)."""
+    lib = load()
+    _want(W32, "W", torch.float32)
+    N, K = W32.shape
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W32.device)
+    We = torch.empty((N, K // 32), dtype=torch.uint8, device=W32.device)
+    _check("mxfp4_quantize", lib.mxfp4_quantize(N, K, _ptr(W32), _ptr(Wq), _ptr(We), _stream(stream)))
+    return Wq, We
+
+
+def mxfp4_dequant(Wq, We, *, out=None, stream=None):
+    lib = load()
+    N, K = Wq.shape[0], Wq.shape[1] * 2
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=Wq.device)
+    _check("mxfp4_dequant", lib.mxfp4_dequant(N, K, _ptr(Wq), _ptr(We), _ptr(out), _stream(stream)))
+    return out
+
+
+def mxfp4_decode_workspace_bytes(M: int, N: int, K: int, R: int) -> int:
+    return int(load().mxfp4_decode_workspace_bytes(M, N, K, R))
+
+
+def mxfp4_decode_fwd(X, Wq, We, A, B, scale: float, *, Y=None, XA=None, save_xa: bool = True, ws=None,
+                     stream=None):
+    """Decode forward (1 <= M <= 8, K a multiple of 1024) with the MXFP4 weight.  Returns (Y, XA).
+    A workspace passed in must have been zeroed before its first use (every call leaves it so)."""
+    lib = load()
+    for t, n in ((X, "X"), (A, "A"), (B, "B")):
+        _want(t, n, torch.bfloat16)
+    M, K = X.shape
+    N, R = Wq.shape[0], A.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    if XA is None and save_xa:
+        XA = torch.empty((M, R), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = torch.zeros(max(mxfp4_decode_workspace_bytes(M, N, K, R), 256), dtype=torch.uint8, device=X.device)
+    st = lib.mxfp4_decode_fwd(M, N, K, R, float(scale), _ptr(X), _ptr(Wq), _ptr(We), _ptr(A), _ptr(B), _ptr(Y),
+                              _ptr(XA), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("mxfp4_decode_fwd", st)
+    return Y, XA

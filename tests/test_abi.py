@@ -26,7 +26,7 @@ def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
     keywords = {"if", "sizeof", "defined"}
-    return sorted({n for n in names if n not in keywords and (n.startswith("lora_") or n.startswith("qlora_"))})
+    return sorted({n for n in names if n not in keywords and n.startswith(("lora_", "qlora_", "mxfp4_"))})
 
 
 def test_header_declares_the_entry_points():
@@ -272,3 +272,42 @@ def test_rmsnorm_workspace_sizes(lib):
     assert lib.lora_rmsnorm_bwd_workspace_bytes(0, 4096) == 0
     assert lib.lora_rmsnorm_bwd_workspace_bytes(64, 100) == 0
     assert lora.lora_rmsnorm_bwd_workspace_bytes(8192, 4096) == (512 + 16) * 4096 * 4
+
+
+# ---- MXFP4 weights ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), 2), (dict(K=96), 2), (dict(K=0), 2),
+    (dict(W=NUL), 1), (dict(Wq=NUL), 1), (dict(We=NUL), 1), (dict(We=MIS), 4),
+])
+def test_mxfp4_quantize_and_dequant_validation(lib, kw, code):
+    p = dict(N=64, K=256, W=P, Wq=P, We=P)
+    p.update(kw)
+    assert lib.mxfp4_quantize(p["N"], p["K"], p["W"], p["Wq"], p["We"], None) == code
+    assert lib.mxfp4_dequant(p["N"], p["K"], p["Wq"], p["We"], p["W"], None) == code
+
+
+def mx_decode(lib, M=4, N=256, K=2048, R=16, scale=2.0, ws=P, ws_bytes=None, **ptrs):
+    p = dict(X=P, Wq=P, We=P, A=P, B=P, Y=P, XA=P)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.mxfp4_decode_workspace_bytes(M, N, K, R)
+    return lib.mxfp4_decode_fwd(M, N, K, R, scale, p["X"], p["Wq"], p["We"], p["A"], p["B"], p["Y"], p["XA"],
+                                ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), 2), (dict(M=9), 2), (dict(K=1536), 2), (dict(N=100), 2), (dict(R=12), 3),
+    (dict(scale=float("inf")), 8),
+    (dict(X=NUL), 1), (dict(We=NUL), 1), (dict(Y=NUL), 1), (dict(XA=MIS), 4), (dict(B=MIS), 4),
+    (dict(ws=NUL), 6), (dict(ws_bytes=64), 6), (dict(ws=MIS), 4),
+])
+def test_mxfp4_decode_validation(lib, kw, code):
+    assert mx_decode(lib, **kw) == code
+
+
+def test_mxfp4_decode_workspace_matches_qlora_decode(lib):
+    for M, N, K, R in ((1, 27648, 5120, 16), (8, 5120, 27648, 16), (4, 256, 2048, 64)):
+        assert lib.mxfp4_decode_workspace_bytes(M, N, K, R) == lib.qlora_fwd_workspace_bytes(M, N, K, R) > 0
+    assert lib.mxfp4_decode_workspace_bytes(16, 256, 2048, 16) == 0
+    assert lib.mxfp4_decode_workspace_bytes(4, 256, 1536, 16) == 0
