@@ -26,6 +26,10 @@ Sources are the web pages on Unsloth.  They are cited by page title and section:
 * RMSNorm: tutorial ch. 5 §5.4 "fused RMSNorm", ``x / sqrt(mean(x^2) + eps) * g``
   over the hidden dimension, g a learnable per-feature scale; the gradients are
   derived by hand from ``L = <dY, Y>_F``.
+* Chunked cross-entropy: tutorial ch. 5 §5.7, the LM head's logits X W^T are never
+  formed for the whole batch; chunks of tokens each compute their logits, loss and
+  gradient and drop the logits, and the chunk losses are summed.  Gradients derived by
+  hand: d loss_m / d logits_m = softmax(logits_m) - onehot(label_m).
 * FP4 weights: the same page names FP4 beside INT4 for the 4-bit weights.  Its
   format is read as the OCP Microscaling (MX) FP4: blocks of 32 consecutive k share
   a power-of-two scale 2^(E-127) (E8M0), each element an E2M1 value (sign, 2
@@ -407,3 +411,52 @@ def dequant_mxfp4(packed, E):
     codes = unpack_fp4(packed)
     se = np.asarray(E, dtype=np.int64) - 127
     return fp4_e2m1_value(codes) * np.exp2(np.repeat(se, FP4_BLOCK, axis=1))
+
+
+# ---------------------------------------------------------------------------
+# Chunked cross-entropy over an LM head (tutorial ch. 5 §5.7: chunks of tokens each compute
+# their logits, loss and gradient, the logits of the whole batch are never formed, and the
+# chunk losses are summed; gradients derived by hand)
+# ---------------------------------------------------------------------------
+
+
+def cross_entropy_rows(X, W, labels):
+    """Per-token loss of the logits X W^T: loss_m = logsumexp_v(logits[m]) - logits[m, label_m].
+
+    X: M x K, W: V x K (the LM head), labels: M ints in [0, V).  Returns (loss, lse), float64,
+    each with M entries; the log-sum-exp is taken around the row maximum.
+    """
+    X, W = _f64(X, W)
+    labels = np.asarray(labels, dtype=np.int64)
+    logits = X @ W.T
+    mx = logits.max(axis=1)
+    lse = mx + np.log(np.sum(np.exp(logits - mx[:, None]), axis=1))
+    return lse - logits[np.arange(len(labels)), labels], lse
+
+
+def cross_entropy_grad(X, W, labels, grad_scale):
+    """dX of L = grad_scale * sum_m loss_m: dlogits = grad_scale (softmax - onehot), dX = dlogits W.
+    Returns (dX, dlogits), float64."""
+    X, W = _f64(X, W)
+    labels = np.asarray(labels, dtype=np.int64)
+    logits = X @ W.T
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    p[np.arange(len(labels)), labels] -= 1.0
+    dlogits = grad_scale * p
+    return dlogits @ W, dlogits
+
+
+def cross_entropy_chunked(X, W, labels, chunk=256):
+    """The page's procedure: for each chunk of `chunk` tokens, its logits, losses and gradient
+    (for the mean loss over all M tokens), then the logits are dropped and the losses summed.
+    Returns (mean loss, dX)."""
+    X = np.asarray(X, dtype=np.float64)
+    M = X.shape[0]
+    total, dX = 0.0, np.zeros_like(X)
+    for c0 in range(0, M, chunk):
+        sl = slice(c0, min(M, c0 + chunk))
+        loss, _ = cross_entropy_rows(X[sl], W, labels[sl])
+        total += float(np.sum(loss))
+        dX[sl] = cross_entropy_grad(X[sl], W, labels[sl], 1.0 / M)[0]
+    return total / M, dX

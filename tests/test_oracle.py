@@ -657,3 +657,97 @@ def test_mxfp4_planted_mistakes_fail_the_fixture():
     assert list(away) != [6, 6, 4, 4, 2, 2, 0]
     # swapped nibbles would pack 6, 14 as 0x6E
     assert int(oracle.pack_fp4(np.array([[6, 14]], dtype=np.uint8))[0, 0]) == 0xE6
+
+
+# ---------------------------------------------------------------------------
+# Chunked cross-entropy over an LM head (tutorial ch. 5 §5.7)
+# ---------------------------------------------------------------------------
+
+
+def _term(t):
+    import math
+    if "*ln(" in t:
+        a, b = t.split("*ln(")
+        return float(Fraction(a)) * math.log(float(Fraction(b.rstrip(")"))))
+    return float(Fraction(t))
+
+
+def test_cross_entropy_hand_worked_example():
+    f = _read_fixture("cross_entropy_worked_example.txt")
+    vec = lambda k: np.array([_term(t) for t in f[k]])
+    W, X = vec("W").reshape(3, 2), vec("X").reshape(2, 2)
+    labels = np.array([int(v) for v in f["labels"]])
+    loss, lse = oracle.cross_entropy_rows(X, W, labels)
+    np.testing.assert_allclose(loss, vec("loss"), rtol=1e-14)
+    np.testing.assert_allclose(lse, vec("lse"), rtol=1e-14)
+    dX, dl = oracle.cross_entropy_grad(X, W, labels, 1.0)
+    np.testing.assert_allclose(dl, vec("dlogits").reshape(2, 3), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(dX, vec("dX").reshape(2, 2), rtol=1e-14, atol=1e-15)
+
+
+def test_cross_entropy_closed_forms_and_invariants():
+    rng = np.random.default_rng(90)
+    M, K, V = 9, 16, 50
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((V, K))
+    labels = rng.integers(0, V, M)
+    # X = 0: uniform softmax, loss = ln V, dX = mean of W's rows minus the label's row
+    loss0, _ = oracle.cross_entropy_rows(np.zeros((M, K)), W, labels)
+    np.testing.assert_allclose(loss0, np.log(V), rtol=1e-15)
+    dX0, _ = oracle.cross_entropy_grad(np.zeros((M, K)), W, labels, 1.0)
+    np.testing.assert_allclose(dX0, W.mean(axis=0)[None, :] - W[labels], rtol=1e-12, atol=1e-14)
+    # a constant added to every logit (a constant feature in X with a constant column in W)
+    # changes neither the loss nor the gradient, and the gradient's component on that feature is
+    # sum_v dlogits_v * c = 0
+    Xc, Wc = np.hstack([X, np.full((M, 1), 1.0)]), np.hstack([W, np.full((V, 1), 7.5)])
+    np.testing.assert_allclose(oracle.cross_entropy_rows(Xc, Wc, labels)[0], oracle.cross_entropy_rows(X, W, labels)[0],
+                               rtol=1e-12)
+    dXc, dl = oracle.cross_entropy_grad(Xc, Wc, labels, 1.0)
+    np.testing.assert_allclose(dXc[:, :K], oracle.cross_entropy_grad(X, W, labels, 1.0)[0], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dXc[:, K], 0.0, atol=1e-12)
+    np.testing.assert_allclose(dl.sum(axis=1), 0.0, atol=1e-13)
+    # huge logits (1e4 apart) stay finite: the log-sum-exp is taken around the maximum
+    Xb = X * 1e3
+    assert np.all(np.isfinite(oracle.cross_entropy_rows(Xb, W, labels)[0]))
+
+
+def test_cross_entropy_central_differences_and_torch():
+    rng = np.random.default_rng(91)
+    M, K, V = 5, 8, 13
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((V, K))
+    labels = rng.integers(0, V, M)
+    g = 0.37
+    L = lambda X_: g * float(np.sum(oracle.cross_entropy_rows(X_, W, labels)[0]))
+    dX, _ = oracle.cross_entropy_grad(X, W, labels, g)
+    h = 1e-5
+    num = np.zeros_like(X)
+    for idx in np.ndindex(*X.shape):
+        E = np.zeros_like(X)
+        E[idx] = h
+        num[idx] = (L(X + E) - L(X - E)) / (2 * h)
+    np.testing.assert_allclose(num, dX, rtol=1e-6, atol=1e-9)
+    tX = torch.tensor(X, requires_grad=True)
+    tl = torch.nn.functional.cross_entropy(tX @ torch.tensor(W).T, torch.tensor(labels), reduction="none")
+    (g * tl.sum()).backward()
+    np.testing.assert_allclose(oracle.cross_entropy_rows(X, W, labels)[0], tl.detach().numpy(), rtol=1e-12)
+    np.testing.assert_allclose(dX, tX.grad.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_cross_entropy_chunked_equals_whole_batch():
+    # the page's chunked procedure gives the whole batch's mean loss and gradient
+    rng = np.random.default_rng(92)
+    M, K, V = 700, 12, 40
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((V, K))
+    labels = rng.integers(0, V, M)
+    mean, dX = oracle.cross_entropy_chunked(X, W, labels, chunk=256)
+    np.testing.assert_allclose(mean, np.mean(oracle.cross_entropy_rows(X, W, labels)[0]), rtol=1e-13)
+    np.testing.assert_allclose(dX, oracle.cross_entropy_grad(X, W, labels, 1.0 / M)[0], rtol=1e-12, atol=1e-15)
+
+
+def test_cross_entropy_planted_mistake_fails():
+    # forgetting the onehot term leaves gradient rows that do not sum to zero
+    rng = np.random.default_rng(93)
+    X, W = rng.standard_normal((4, 6)), rng.standard_normal((10, 6))
+    logits = X @ W.T
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(p.sum(axis=1))) > 0.5  # the invariant pinned above would catch it
