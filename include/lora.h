@@ -265,6 +265,30 @@ lora_status mxfp4_decode_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float s
                              const void* B, void* Y, float* XA, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* ---- Cross-entropy over an LM head, in chunks of tokens ----------------------------------
+ * Tutorial ch. 5 §5.7 (chunked cross-entropy: the logits of the whole batch are never formed;
+ * each chunk of tokens computes its logits, its losses and its gradient, then drops the logits,
+ * and the losses are summed).  For hidden states X (M x K bf16), the frozen LM head W (V x K bf16)
+ * and labels (M int32 in [0, V)):
+ *   loss[m] = logsumexp_v (X W^T)[m][v] - (X W^T)[m][label[m]],
+ *   dX      = grad_scale (softmax(X W^T) - onehot(label)) W        (M x K bf16, optional),
+ * with grad_scale = 1/M for the mean loss.  Per chunk of `chunk` tokens (0: 8192) the logits
+ * are formed once on the matrix cores; the pass keeps, per row and 128 columns, the maximum and
+ * the sum of exp (fp32, from the accumulators) and the label's logit, and a fixed-order
+ * reduction gives the log-sum-exp and the loss.  With dX the same pass also stores the chunk's
+ * fp32 logits in the workspace (chunk x V x 4 bytes: sized for the accelerator's memory rather
+ * than the whole batch's), an elementwise pass turns them into the bf16 gradient of the logits,
+ * and the input-gradient kernel multiplies that by W.  V and K multiples of 64; chunk x V below 2^31.  loss (M fp32) is
+ * written; loss_sum (one fp32, the fixed-order sum of loss) and dX may be NULL.  A label outside
+ * [0, V) gives loss NaN.  Errors as for lora_fwd. */
+
+/* Bytes of device workspace lora_ce needs (grad: dX requested), no initialisation required. */
+size_t lora_ce_workspace_bytes(int64_t M, int64_t V, int64_t K, int64_t chunk, int32_t grad);
+
+lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_scale,
+                    const void* X, const void* W, const int32_t* labels, float* loss,
+                    float* loss_sum, void* dX, void* ws, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* lora_status_str(lora_status s);
 

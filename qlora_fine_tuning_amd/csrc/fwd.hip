@@ -61,15 +61,20 @@ __device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stag
 // PANEL: the panel X A^T is accumulated here from the X fragments of the main loop.  Without
 // it (rank 64, when the caller keeps XA) XA has been computed by a pass of its own and is read
 // in the epilogue: the rank-64 panel's accumulators and A fragments make the main loop spill.
-// SWIGLU (bf16 W only): N = 2 Nh stacked rows, Y = [G | U] (M x 2 Nh) and H (M x Nh) out.
-template <int RP, bool INT4, bool PANEL, bool SWIGLU>
+// EPI (bf16 W only when not kEpiLora): kEpiSwiglu, N = 2 Nh stacked rows, Y = [G | U] (M x 2 Nh)
+// and H (M x Nh) out; kEpiCeStats, the logits X W^T of an LM head (no adapter): per-row (max, sum
+// of exp) of each wave's 128 columns into `stats`, the label's logit, and the fp32 logits
+// themselves into `logits` when that is set (the gradient pass then reads them).
+template <int RP, bool INT4, bool PANEL, int EPI>
 __global__ void __launch_bounds__(kThreads)
 fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
                 const uint16_t* __restrict__ Bm, uint16_t* __restrict__ Y,
-                float* __restrict__ XA, uint16_t* __restrict__ H, int M, int N, int K, int R,
+                float* __restrict__ XA, uint16_t* __restrict__ H, CeArgs ce, int M, int N, int K, int R,
                 float scale) {
-  static_assert(!(SWIGLU && INT4), "the SwiGLU pair takes a bf16 weight");
+  constexpr bool SWIGLU = EPI == kEpiSwiglu, CE = EPI >= kEpiCeStats, LORA = !CE;
+  static_assert(EPI == kEpiLora || !INT4, "the SwiGLU pair and the LM head take a bf16 weight");
+  static_assert(!(CE && PANEL), "the LM head has no adapter");
   constexpr int TT = kTile * kStep;  // elements of one 256 x 64 operand tile
   constexpr int AROWS = RP < 32 ? 32 : RP;  // adapter rows in LDS: each wave copies 8k of them
   constexpr int AT = AROWS * kStep;
@@ -339,7 +344,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       f[i] = (n < nh && rk < R) ? ld16(Bm + row * R + rk) : zero4();
     }
   };
-  if constexpr (RP <= 32) {
+  if constexpr (RP <= 32 && LORA) {
 #pragma unroll
     for (int c = 0; c < RP / 16; ++c) load_bfrag(fbm[c], c);
   }
@@ -365,7 +370,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
         if (XA != nullptr && tn == 0 && m0 + ml < M && rk < R)
           *reinterpret_cast<f32x4*>(XA + (size_t)(m0 + ml) * R + rk) = pacc[c][j];
       }
-  } else {  // XA from its own pass (ranks >= R and tokens >= M as zeros)
+  } else if constexpr (LORA) {  // XA from its own pass (ranks >= R and tokens >= M as zeros)
     for (int e = tid; e < kTile * (RP / 4); e += kThreads) {
       const int ml = e / (RP / 4), rk = (e % (RP / 4)) * 4;
       const f32x4 v = (m0 + ml < M && rk < R) ? *reinterpret_cast<const f32x4*>(XA + (size_t)(m0 + ml) * R + rk) : fzero4();
@@ -375,7 +380,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   __syncthreads();
 
 #pragma unroll
-  for (int c = 0; c < RP / 16; ++c) {
+  for (int c = 0; c < (LORA ? RP / 16 : 0); ++c) {
     const int rk = c * 16 + (g4 & 1) * 8;
     if constexpr (RP > 32) load_bfrag(fbm[0], c);
 #pragma unroll
@@ -403,7 +408,51 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   auto buf = [&](int w) { return w == 0 ? sX0 : (w == 1 ? sX1 : (w == 2 ? sW0 : sW1)); };
   uint16_t* const stage = buf(wave);
   const int mw = m0 + wm * 128;
-  if constexpr (!SWIGLU) {
+  if constexpr (EPI == kEpiCeStats) {
+    // each lane holds rows mw + 16 j + l16 and columns nb + 16 i + 4 g4 + e of the logits
+    const int nb = n0 + wn * 128;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = mw + j * 16 + l16;
+      const int lab = m < M ? ce.labels[m] : -1;
+      float mx = -__builtin_inff(), lv = 0.f;
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = nb + i * 16 + g4 * 4 + e;
+          const float v = acc[i * 8 + j][e];
+          if (n < N) mx = fmaxf(mx, v);
+          if (n == lab) { lv = v; found = true; }
+        }
+      float sm = 0.f;
+      if (mx != -__builtin_inff())
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nb + i * 16 + g4 * 4 + e < N) sm += __expf(acc[i * 8 + j][e] - mx);
+      // the four lanes of the row (l16 + 16 g4): partners combine the same two operands
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float m2 = __shfl_xor(mx, o, 64), s2 = __shfl_xor(sm, o, 64);
+        const float mn = fmaxf(mx, m2);
+        if (mn != -__builtin_inff()) sm = sm * __expf(mx - mn) + s2 * __expf(m2 - mn);
+        mx = mn;
+      }
+      if (g4 == 0 && m < M)
+        *reinterpret_cast<float2*>(ce.stats + 2 * ((size_t)(tn * 2 + wn) * M + m)) = make_float2(mx, sm);
+      if (found) ce.lab_logit[m] = lv;  // the one lane in the grid holding the label's column
+      // the row's fp32 logits: 4 consecutive columns per lane, the row's 16 lanes adjacent
+      if (ce.logits != nullptr && m < M)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int n = nb + i * 16 + g4 * 4;
+          if (n < N) *reinterpret_cast<f32x4*>(ce.logits + (size_t)m * N + n) = acc[i * 8 + j];
+        }
+    }
+  } else if constexpr (!SWIGLU) {
     const int nw = n0 + wn * 128;
     store_block_bf16(acc, stage, Y + (size_t)mw * N + nw, (size_t)N, M - mw, N - nw, lane);
   } else {
@@ -454,16 +503,20 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   }
 }
 
-template <int RP, bool INT4, bool PANEL, bool SWIGLU = false>
+template <int RP, bool INT4, bool PANEL, int EPI = kEpiLora>
 static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
   // SwiGLU: N = 2 Nh stacked rows, one tile per 128 outputs of H: ceil(2 Nh / 256) of them
   const int tiles = (int)(((a.M + kTile - 1) / kTile) * ((a.N + kTile - 1) / kTile));
-  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, SWIGLU>), dim3(tiles), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, EPI>), dim3(tiles), dim3(kThreads), 0, s,
                      (const uint16_t*)a.X, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
-                     (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (uint16_t*)a.H, (int)a.M, (int)a.N,
+                     (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (uint16_t*)a.H, a.ce, (int)a.M, (int)a.N,
                      (int)a.K, (int)a.R, a.scale);
   return hipGetLastError();
 }
+
+// logits of an LM head (X W^T, bf16 W, no adapter) with the cross-entropy epilogue: per-row
+// statistics (a.ce.stats, a.ce.lab_logit) and, if a.ce.logits is set, the fp32 logits
+hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s) { return launch_fwd_rp<16, false, false, kEpiCeStats>(a, s); }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
@@ -475,13 +528,13 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
     const hipError_t e = launch_panel_xa(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A),
                                          a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
     if (e != hipSuccess) return e;
-    if (swiglu) return launch_fwd_rp<64, false, false, true>(a, s);
+    if (swiglu) return launch_fwd_rp<64, false, false, kEpiSwiglu>(a, s);
     return int4 ? launch_fwd_rp<64, true, false>(a, s) : launch_fwd_rp<64, false, false>(a, s);
   }
   if (swiglu) {
-    if (rp == 16) return launch_fwd_rp<16, false, true, true>(a, s);
-    if (rp == 32) return launch_fwd_rp<32, false, true, true>(a, s);
-    return launch_fwd_rp<64, false, true, true>(a, s);
+    if (rp == 16) return launch_fwd_rp<16, false, true, kEpiSwiglu>(a, s);
+    if (rp == 32) return launch_fwd_rp<32, false, true, kEpiSwiglu>(a, s);
+    return launch_fwd_rp<64, false, true, kEpiSwiglu>(a, s);
   }
   if (int4) {
     if (rp == 16) return launch_fwd_rp<16, true, true>(a, s);

@@ -11,6 +11,17 @@ namespace lora {
 constexpr int64_t kSplitRows = 256;
 constexpr int64_t kDadbCols = 256;  // columns (k or n) per workgroup of the dA / dB partial pass
 
+// epilogues of the forward GEMM
+constexpr int kEpiLora = 0, kEpiSwiglu = 1, kEpiCeStats = 2;
+
+// cross-entropy epilogues over an LM head's logits
+struct CeArgs {
+  const int32_t* labels = nullptr;  // [M] in [0, N)
+  float* stats = nullptr;           // [2 tiles_n][M] (max, sum of exp) per wave's 128 columns
+  float* lab_logit = nullptr;       // [M] the label's logit
+  float* logits = nullptr;          // [M][N] fp32, or null
+};
+
 struct FwdArgs {
   const void* X;
   const void* W;   // bf16 [N][K], fp32 [N][K], or packed int4 [N][K/2]
@@ -23,6 +34,7 @@ struct FwdArgs {
   int R;
   float scale;
   void* H = nullptr;  // SwiGLU pair (bf16 W = [Wg; Wu], N = 2 Nh): H = silu(G) U, M x Nh
+  CeArgs ce = {};
 };
 
 struct DxArgs {
@@ -58,6 +70,16 @@ struct DadbArgs {
 
 // bf16 / int4 MFMA paths
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
+hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s);
+// cross-entropy reductions (ce.hip): lse and loss per row from the stats, their fixed-order sum,
+// and a 32-bit fill
+hipError_t launch_ce_reduce(const float* stats, const float* lab_logit, float* lse, float* loss, int P, int64_t M,
+                            hipStream_t s);
+hipError_t launch_ce_sum(const float* loss, float* out, int64_t M, hipStream_t s);
+// dlogits = bf16(scale (exp(logits - lse) - onehot(label))) from the stored fp32 logits
+hipError_t launch_ce_grad(const float* logits, const float* lse, const int32_t* labels, uint16_t* dl, int64_t M,
+                          int64_t V, float scale, hipStream_t s);
+hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s);
 // ranks 33..64: G = dY B as a pass of its own (written to G), ahead of the input-gradient kernel,
 // which then reads G in its epilogue; `ws` holds panel_workspace_bytes() bytes

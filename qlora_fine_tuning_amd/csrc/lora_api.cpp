@@ -512,3 +512,118 @@ lora_status mxfp4_decode_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float s
 }
 
 }  // extern "C"
+
+// ---- Cross-entropy over an LM head, in chunks of tokens ----
+
+namespace {
+
+constexpr int64_t kCeDefaultChunk = 8192;
+constexpr int32_t kCeRank = 8;  // the input-gradient kernel runs with zero adapters of this rank
+
+int64_t ce_chunk(int64_t M, int64_t chunk) {
+  const int64_t c = chunk > 0 ? chunk : kCeDefaultChunk;
+  return M < c ? (M > 0 ? M : 1) : c;
+}
+
+lora_status check_ce(int64_t M, int64_t V, int64_t K, int64_t chunk) {
+  if (M < 0 || M >= kMaxElems || chunk < 0) return LORA_ERR_SHAPE;
+  const int64_t C = ce_chunk(M, chunk);
+  return check_dims(C, V, K, kCeRank);  // V and K multiples of 64; the chunk's C x V below 2^31
+}
+
+struct CeLayout {
+  size_t stats, lab, lse, azero, bzero, logits, dl, inner, total;
+};
+CeLayout ce_layout(int64_t M, int64_t V, int64_t K, int64_t chunk, bool grad) {
+  const int64_t C = ce_chunk(M, chunk);
+  const int64_t P = 2 * ((V + 255) / 256);  // partials per row: one per wave's 128 columns
+  CeLayout l{};
+  l.stats = 0;
+  l.lab = l.stats + align256((size_t)P * C * 8);
+  l.lse = l.lab + align256((size_t)C * 4);
+  l.total = l.lse + align256((size_t)C * 4);
+  if (grad) {
+    l.azero = l.total;
+    l.bzero = l.azero + align256((size_t)kCeRank * K * 2);
+    l.logits = l.bzero + align256((size_t)V * kCeRank * 2);
+    l.dl = l.logits + align256((size_t)C * V * 4);
+    l.inner = l.dl + align256((size_t)C * V * 2);
+    // the input-gradient workspace of a full chunk and of the last, shorter one (whose split
+    // of V may differ)
+    const int64_t tail = M % C;
+    size_t inner = bwd_layout(C, V, K, kCeRank, true).total;
+    if (tail > 0) {
+      const size_t t = bwd_layout(tail, V, K, kCeRank, true).total;
+      inner = t > inner ? t : inner;
+    }
+    l.total = l.inner + inner;
+  }
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_ce_workspace_bytes(int64_t M, int64_t V, int64_t K, int64_t chunk, int32_t grad) {
+  if (check_ce(M, V, K, chunk) != LORA_OK) return 0;
+  return ce_layout(M, V, K, chunk, grad != 0).total;
+}
+
+lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_scale, const void* X, const void* W,
+                    const int32_t* labels, float* loss, float* loss_sum, void* dX, void* ws, size_t ws_bytes,
+                    void* stream) {
+  lora_status st = check_ce(M, V, K, chunk);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(grad_scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(W);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(X, labels, loss)) != LORA_OK) return st;
+  if (dX != nullptr && !aligned16(dX)) return LORA_ERR_ALIGN;
+  if (loss_sum != nullptr && !aligned16(loss_sum)) return LORA_ERR_ALIGN;
+  const bool grad = dX != nullptr;
+  const CeLayout lay = ce_layout(M, V, K, chunk, grad);
+  if (M > 0 && (ws == nullptr || ws_bytes < lay.total)) return LORA_ERR_WORKSPACE;
+  if (ws != nullptr && !aligned16(ws)) return LORA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const int64_t C = ce_chunk(M, chunk);
+  const int P = (int)(2 * ((V + 255) / 256));
+  hipError_t e = hipSuccess;
+  if (M > 0 && grad) {
+    e = launch_fill_u32(base + lay.azero, lay.logits - lay.azero, 0u, s);  // the zero adapters
+    if (e != hipSuccess) return from_hip(e);
+  }
+  for (int64_t c0 = 0; c0 < M; c0 += C) {
+    const int64_t Mc = (M - c0 < C) ? M - c0 : C;
+    float* stats = reinterpret_cast<float*>(base + lay.stats);
+    float* lab = reinterpret_cast<float*>(base + lay.lab);
+    float* lse = reinterpret_cast<float*>(base + lay.lse);
+    // a label outside [0, V) is never found: its slot keeps NaN and so does its loss
+    e = launch_fill_u32(lab, (size_t)Mc * 4, 0x7fc00000u, s);
+    if (e != hipSuccess) return from_hip(e);
+    FwdArgs a{static_cast<const uint16_t*>(X) + c0 * K, W, nullptr, nullptr, nullptr, nullptr, nullptr, Mc, V, K,
+              kCeRank, grad_scale};
+    a.ce.labels = labels + c0;
+    a.ce.stats = stats;
+    a.ce.lab_logit = lab;
+    a.ce.logits = grad ? reinterpret_cast<float*>(base + lay.logits) : nullptr;
+    e = launch_ce_logits(a, s);
+    if (e != hipSuccess) return from_hip(e);
+    e = launch_ce_reduce(stats, lab, lse, loss + c0, P, Mc, s);
+    if (e != hipSuccess) return from_hip(e);
+    if (!grad) continue;
+    // dlogits = grad_scale (softmax - onehot) from the stored fp32 logits, then dX = dlogits W
+    e = launch_ce_grad(a.ce.logits, lse, labels + c0, reinterpret_cast<uint16_t*>(base + lay.dl), Mc, V, grad_scale,
+                       s);
+    if (e != hipSuccess) return from_hip(e);
+    st = bwd_dx_common(false, LORA_BF16, Mc, V, K, kCeRank, 0.f, base + lay.dl, W, nullptr, base + lay.azero,
+                       base + lay.bzero, static_cast<uint16_t*>(dX) + c0 * K, base + lay.inner,
+                       ws_bytes - lay.inner, stream);
+    if (st != LORA_OK) return st;
+  }
+  if (loss_sum != nullptr) return from_hip(launch_ce_sum(loss, loss_sum, M, s));
+  return LORA_OK;
+}
+
+}  // extern "C"

@@ -189,3 +189,25 @@ def make_norm_inputs(M: int, K: int, *, seed: int, eps: float = 1e-5, with_dy: b
     dY = rng.standard_normal((M, K)) if with_dy else None
     return NormInputs(M=M, K=K, eps=float(eps), seed=seed, X=_round(X, "bf16"), g=_round(g, "bf16"),
                       dY=None if dY is None else _round(dY, "bf16"))
+
+
+@dataclass
+class CeInputs:
+    """Seeded inputs of the cross-entropy over an LM head: X, W as bf16 bit patterns, labels int32."""
+    M: int
+    K: int
+    V: int
+    seed: int
+    X: np.ndarray       # M x K
+    W: np.ndarray       # V x K
+    labels: np.ndarray  # M
+
+
+def make_ce_inputs(M: int, K: int, V: int, *, seed: int, logit_std: float = 1.0) -> CeInputs:
+    """Hidden states X ~ N(0, 1), the LM head W ~ N(0, logit_std^2 / K) (logits of standard deviation
+    about logit_std), labels uniform in [0, V); drawn in that order, X and W rounded once to bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = rng.standard_normal((M, K))
+    W = rng.standard_normal((V, K)) * (logit_std / np.sqrt(K))
+    labels = rng.integers(0, V, size=M).astype(np.int32)
+    return CeInputs(M=M, K=K, V=V, seed=seed, X=_round(X, "bf16"), W=_round(W, "bf16"), labels=labels)

@@ -311,3 +311,40 @@ def test_mxfp4_decode_workspace_matches_qlora_decode(lib):
         assert lib.mxfp4_decode_workspace_bytes(M, N, K, R) == lib.qlora_fwd_workspace_bytes(M, N, K, R) > 0
     assert lib.mxfp4_decode_workspace_bytes(16, 256, 2048, 16) == 0
     assert lib.mxfp4_decode_workspace_bytes(4, 256, 1536, 16) == 0
+
+
+# ---- Cross-entropy over an LM head ------------------------------------------------------
+
+def ce_call(lib, M=64, V=1024, K=256, chunk=0, gs=1.0, ws=P, ws_bytes=None, **ptrs):
+    p = dict(X=P, W=P, labels=P, loss=P, loss_sum=P, dX=P)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.lora_ce_workspace_bytes(M, V, K, chunk, 1)
+    return lib.lora_ce(M, V, K, chunk, gs, p["X"], p["W"], p["labels"], p["loss"], p["loss_sum"], p["dX"], ws,
+                       ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(V=100), 2), (dict(K=96), 2), (dict(M=-1), 2), (dict(chunk=-1), 2),
+    (dict(gs=float("nan")), 8),
+    (dict(X=NUL), 1), (dict(W=NUL), 1), (dict(labels=NUL), 1), (dict(loss=NUL), 1),
+    (dict(dX=MIS), 4), (dict(loss_sum=MIS), 4), (dict(ws=MIS), 4),
+    (dict(ws=NUL), 6), (dict(ws_bytes=1024), 6),
+])
+def test_lora_ce_validation(lib, kw, code):
+    assert ce_call(lib, **kw) == code
+
+
+def test_lora_ce_workspace(lib):
+    # per chunk: (max, sum) per row and 128 columns, the label logits and lse; with the gradient
+    # also the zero adapters, the chunk's bf16 gradient of the logits and the input-gradient
+    # workspace of the full and the last chunk
+    M, V, K, C = 16384, 128000, 4096, 8192
+    pad = lambda b: (b + 255) // 256 * 256
+    loss_only = pad(1000 * C * 8) + pad(C * 4) + pad(C * 4)
+    assert lib.lora_ce_workspace_bytes(M, V, K, 0, 0) == loss_only
+    full = (loss_only + pad(8 * K * 2) + pad(V * 8 * 2) + pad(C * V * 4) + pad(C * V * 2)
+            + lib.lora_bwd_workspace_bytes(1, C, V, K, 8))
+    assert lib.lora_ce_workspace_bytes(M, V, K, 0, 1) == full
+    assert full < 6.5e9  # the chunk's fp32 logits and bf16 gradient: 4.2 + 2.1 GB
+    assert lib.lora_ce_workspace_bytes(M, 100, K, 0, 1) == 0

@@ -1,0 +1,89 @@
+"""GPU parity of the chunked cross-entropy over an LM head against the float64 oracle (through the
+C ABI): per-token losses, their sum and dX at shapes with ragged chunks and a partial last column
+tile, peaky logits, the Llama-3-sized head on sampled rows, an out-of-range label, determinism,
+the empty batch, and the autograd wrapper."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import assert_close, bits_to_dev, host
+from qlora_fine_tuning_amd.workloads import make_ce_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(inp):
+    return bits_to_dev(inp.X), bits_to_dev(inp.W), torch.from_numpy(inp.labels).cuda()
+
+
+def _vals(inp):
+    return oracle.bf16_bits_to_f64(inp.X), oracle.bf16_bits_to_f64(inp.W), inp.labels.astype(np.int64)
+
+
+@pytest.mark.parametrize("M,K,V,chunk,std", [(300, 256, 1024, 128, 1.0), (65, 512, 320, 0, 1.0), (1, 128, 64, 0, 1.0),
+                                             (513, 384, 2112, 200, 6.0)])
+def test_ce_shapes(gpu_lib, M, K, V, chunk, std):
+    print(f"case ce M={M} K={K} V={V} chunk={chunk} std={std}", flush=True)
+    inp = make_ce_inputs(M, K, V, seed=40 + M, logit_std=std)
+    X, W, lab = _dev(inp)
+    loss_sum, loss, dX = gpu_lib.lora_ce(X, W, lab, chunk=chunk)
+    torch.cuda.synchronize()
+    x, w, labels = _vals(inp)
+    lr, _ = oracle.cross_entropy_rows(x, w, labels)
+    dXr, _ = oracle.cross_entropy_grad(x, w, labels, 1.0 / M)
+    assert_close("loss", loss.cpu().numpy().astype(np.float64), lr)
+    assert abs(float(loss_sum[0]) - lr.sum()) <= 1e-5 * abs(lr.sum()) + 1e-5
+    assert_close("dX", host(dX), dXr)
+    # the loss alone (no gradient pass) gives the same bits
+    _, loss2, dX2 = gpu_lib.lora_ce(X, W, lab, chunk=chunk, grad=False)
+    torch.cuda.synchronize()
+    assert dX2 is None and torch.equal(loss, loss2)
+
+
+def test_ce_llama3_head_sampled(gpu_lib):
+    # the page's vocabulary (128000) over 4096 hidden features; 2048 tokens in chunks of 1024
+    M, K, V = 2048, 4096, 128000
+    print(f"case ce M={M} K={K} V={V} (sampled rows)", flush=True)
+    inp = make_ce_inputs(M, K, V, seed=5, logit_std=3.0)
+    X, W, lab = _dev(inp)
+    loss_sum, loss, dX = gpu_lib.lora_ce(X, W, lab, chunk=1024)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 255, 256, 1023, 1024, 1025, 2047} | set(np.random.default_rng(5).integers(0, M, 12))))
+    x, w, labels = _vals(inp)
+    lr, _ = oracle.cross_entropy_rows(x[rows], w, labels[rows])
+    dXr, _ = oracle.cross_entropy_grad(x[rows], w, labels[rows], 1.0 / M)
+    idx = torch.from_numpy(rows).cuda()
+    assert_close("loss", loss[idx].cpu().numpy().astype(np.float64), lr)
+    assert_close("dX", host(dX[idx]), dXr)
+    assert torch.isfinite(loss).all() and torch.isfinite(dX.float()).all()
+
+
+def test_ce_out_of_range_label_gives_nan(gpu_lib):
+    print("case ce label out of range", flush=True)
+    inp = make_ce_inputs(40, 128, 256, seed=3)
+    inp.labels[7] = 256
+    X, W, lab = _dev(inp)
+    _, loss, _ = gpu_lib.lora_ce(X, W, lab, grad=False)
+    torch.cuda.synchronize()
+    l = loss.cpu().numpy()
+    assert np.isnan(l[7]) and np.isfinite(np.delete(l, 7)).all()
+
+
+def test_ce_determinism_empty_batch_and_autograd(gpu_lib):
+    print("case ce determinism / empty / autograd", flush=True)
+    inp = make_ce_inputs(200, 256, 640, seed=4)
+    X, W, lab = _dev(inp)
+    a = gpu_lib.lora_ce(X, W, lab, chunk=64)
+    b = gpu_lib.lora_ce(X, W, lab, chunk=64)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    s0, l0, d0 = gpu_lib.lora_ce(X[:0], W, lab[:0])
+    torch.cuda.synchronize()
+    assert float(s0[0]) == 0.0 and l0.numel() == 0 and d0.shape == (0, 256)
+    Xl = X.detach().clone().requires_grad_(True)
+    mean = gpu_lib.LMHeadCrossEntropyFunction.apply(Xl, W, lab, 64)
+    mean.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(mean, a[0][0] / 200) and torch.equal(Xl.grad, a[2])
