@@ -444,13 +444,32 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       if (g4 == 0 && m < M)
         *reinterpret_cast<float2*>(ce.stats + 2 * ((size_t)(tn * 2 + wn) * M + m)) = make_float2(mx, sm);
       if (found) ce.lab_logit[m] = lv;  // the one lane in the grid holding the label's column
-      // the row's fp32 logits: 4 consecutive columns per lane, the row's 16 lanes adjacent
-      if (ce.logits != nullptr && m < M)
+    }
+    // the fp32 logits, staged through this wave's freed tile buffer in two 128 x 64 halves so that
+    // each row leaves in 256-byte segments; 16-byte chunk c of row r sits at slot c ^ (r & 15)
+    if (ce.logits != nullptr) {
+      float* const st = reinterpret_cast<float*>(stage);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int n = nb + i * 16 + g4 * 4;
-          if (n < N) *reinterpret_cast<f32x4*>(ce.logits + (size_t)m * N + n) = acc[i * 8 + j];
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = j * 16 + l16, c = i * 4 + g4;
+            *reinterpret_cast<f32x4*>(st + r * 64 + ((c ^ (r & 15)) << 2)) = acc[(4 * h + i) * 8 + j];
+          }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes have landed
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < 32; ++p) {
+          const int r = p * 4 + (lane >> 4), c = lane & 15;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(st + r * 64 + ((c ^ (r & 15)) << 2));
+          const int n = nb + h * 64 + c * 4;
+          if (mw + r < M && n < N) *reinterpret_cast<f32x4*>(ce.logits + (size_t)(mw + r) * N + n) = v;
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half is written
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   } else if constexpr (!SWIGLU) {
     const int nw = n0 + wn * 128;
