@@ -30,6 +30,9 @@ Sources are the web pages on Unsloth.  They are cited by page title and section:
   formed for the whole batch; chunks of tokens each compute their logits, loss and
   gradient and drop the logits, and the chunk losses are summed.  Gradients derived by
   hand: d loss_m / d logits_m = softmax(logits_m) - onehot(label_m).
+* RoPE: tutorial ch. 5 §5.5, each pair of coordinates of q and k rotated by an angle; the
+  pairing of the page's listing (x_j with x_{j + rot/2}, the rest passed through) and the
+  usual frequencies theta_j = pos * base^(-2j/rot); the backward is the inverse rotation.
 * FP4 weights: the same page names FP4 beside INT4 for the 4-bit weights.  Its
   format is read as the OCP Microscaling (MX) FP4: blocks of 32 consecutive k share
   a power-of-two scale 2^(E-127) (E8M0), each element an E2M1 value (sign, 2
@@ -460,3 +463,31 @@ def cross_entropy_chunked(X, W, labels, chunk=256):
         total += float(np.sum(loss))
         dX[sl] = cross_entropy_grad(X[sl], W, labels[sl], 1.0 / M)[0]
     return total / M, dX
+
+
+# ---------------------------------------------------------------------------
+# RoPE (tutorial ch. 5 §5.5: each coordinate pair of q and k multiplied by a 2 x 2 rotation; the
+# listing pairs x_j with x_{j + rot/2} for j < rot/2 and passes the remaining coordinates through)
+# ---------------------------------------------------------------------------
+
+
+def rope_angles(positions, rot, base):
+    """theta[t, j] = pos_t * base^(-2 j / rot), j < rot/2, float64."""
+    pos = np.asarray(positions, dtype=np.float64)
+    j = np.arange(rot // 2, dtype=np.float64)
+    return pos[:, None] * np.power(float(base), -2.0 * j / rot)[None, :]
+
+
+def rope_apply(x, positions, rot, base, inverse=False):
+    """Rotate x (M x H x D: tokens, heads, head dimension) by the angles of each token's position:
+    (x_j, x_{j+rot/2}) -> (x_j cos - x_{j+rot/2} sin, x_{j+rot/2} cos + x_j sin), by -theta when
+    inverse (the gradient of the rotation); coordinates rot .. D-1 unchanged.  Returns float64."""
+    x = np.asarray(x, dtype=np.float64)
+    th = rope_angles(positions, rot, base) * (-1.0 if inverse else 1.0)
+    c, s = np.cos(th)[:, None, :], np.sin(th)[:, None, :]
+    h = rot // 2
+    out = x.copy()
+    a, b = x[..., :h], x[..., h:rot]
+    out[..., :h] = a * c - b * s
+    out[..., h:rot] = b * c + a * s
+    return out

@@ -751,3 +751,71 @@ def test_cross_entropy_planted_mistake_fails():
     p = np.exp(logits - logits.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
     assert np.max(np.abs(p.sum(axis=1))) > 0.5  # the invariant pinned above would catch it
+
+
+# ---------------------------------------------------------------------------
+# RoPE (tutorial ch. 5 §5.5)
+# ---------------------------------------------------------------------------
+
+
+def _trig_expr(t):
+    import math
+    import re
+    total = 0.0
+    for sign, coef, fn, arg in re.findall(r"([+-]?)([0-9.]+)\*(cos|sin)\(([0-9.]+)\)", t):
+        v = float(coef) * (math.cos if fn == "cos" else math.sin)(float(arg))
+        total += -v if sign == "-" else v
+    return total if "(" in t else float(t)
+
+
+def test_rope_hand_worked_example():
+    f = _read_fixture("rope_worked_example.txt")
+    x = np.array([float(v) for v in f["x"]]).reshape(2, 1, 6)
+    pos = [int(v) for v in f["positions"]]
+    want = np.array([_trig_expr(t) for t in f["out"]]).reshape(2, 1, 6)
+    np.testing.assert_allclose(oracle.rope_apply(x, pos, 4, 10000.0), want, rtol=1e-14, atol=1e-15)
+
+
+def test_rope_properties():
+    rng = np.random.default_rng(95)
+    M, H, D, rot, base = 9, 3, 16, 12, 500000.0
+    pos = rng.integers(0, 8192, M)
+    x = rng.standard_normal((M, H, D))
+    y = oracle.rope_apply(x, pos, rot, base)
+    # the inverse rotation undoes it; position 0 is the identity; the pass-through part is untouched
+    np.testing.assert_allclose(oracle.rope_apply(y, pos, rot, base, inverse=True), x, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(oracle.rope_apply(x, np.zeros(M, int), rot, base), x)
+    np.testing.assert_array_equal(y[..., rot:], x[..., rot:])
+    # each pair keeps its length
+    h = rot // 2
+    np.testing.assert_allclose(y[..., :h] ** 2 + y[..., h:rot] ** 2, x[..., :h] ** 2 + x[..., h:rot] ** 2, rtol=1e-12)
+    # the defining property: <R(m) q, R(n) k> depends only on m - n
+    q, k = rng.standard_normal((1, 1, D)), rng.standard_normal((1, 1, D))
+    dot = lambda m, n: float(np.sum(oracle.rope_apply(q, [m], rot, base) * oracle.rope_apply(k, [n], rot, base)))
+    for m, n in ((5, 2), (105, 102), (3000, 2997)):
+        np.testing.assert_allclose(dot(m, n), dot(3, 0), rtol=1e-9)
+    # the gradient of L = <dY, rope(x)> is the inverse rotation of dY
+    dY = rng.standard_normal((M, H, D))
+    L = lambda x_: float(np.sum(dY * oracle.rope_apply(x_, pos, rot, base)))
+    E = np.zeros_like(x)
+    E[2, 1, 3] = 1e-6
+    np.testing.assert_allclose((L(x + E) - L(x - E)) / 2e-6, oracle.rope_apply(dY, pos, rot, base, inverse=True)[2, 1, 3],
+                               rtol=1e-7)
+
+
+def test_rope_listing_form_agrees():
+    # the page's listing: x_rot * cos + rotate_half(x_rot) * sin, rotate_half(u) = [-u2, u1], with
+    # cos, sin repeated over both halves
+    rng = np.random.default_rng(96)
+    M, H, D, rot, base = 5, 2, 8, 8, 10000.0
+    pos = rng.integers(0, 100, M)
+    x = rng.standard_normal((M, H, D))
+    th = oracle.rope_angles(pos, rot, base)
+    c = np.concatenate([np.cos(th), np.cos(th)], axis=1)[:, None, :]
+    s = np.concatenate([np.sin(th), np.sin(th)], axis=1)[:, None, :]
+    rh = np.concatenate([-x[..., rot // 2:], x[..., :rot // 2]], axis=-1)
+    np.testing.assert_allclose(oracle.rope_apply(x, pos, rot, base), x * c + rh * s, rtol=1e-13, atol=1e-14)
+    # a planted mistake (interleaved pairs) disagrees with it
+    wrong = x.copy()
+    wrong[..., 0::2] = x[..., 0::2] * np.cos(th)[:, None, :] - x[..., 1::2] * np.sin(th)[:, None, :]
+    assert not np.allclose(wrong[..., 0::2], (x * c + rh * s)[..., 0::2])
