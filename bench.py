@@ -331,6 +331,32 @@ def bench_ce(lora, torch, dev, reps):
     return out
 
 
+def bench_rope(lora, torch, dev, reps, copies=4):
+    """RoPE in place on the Llama-3-8B attention shape (8192 tokens, 32 query and 8 key heads of 128,
+    base 500000), rotating over buffer sets (> 256 MB MALL); bytes: Q and K read and written once."""
+    M, H, Hk, D = 8192, 32, 8, 128
+    Qs = [torch.randn(M, H, D, device=dev).to(torch.bfloat16) for _ in range(copies)]
+    Ks = [torch.randn(M, Hk, D, device=dev).to(torch.bfloat16) for _ in range(copies)]
+    pos = (torch.arange(M, device=dev, dtype=torch.int32) % 2048).contiguous()
+    lib, sp = lora.load(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [(M, H, Hk, D, D, 500000.0, 0, p(pos), p(Qs[i]), p(Ks[i]), sp) for i in range(copies)]
+    state = {"i": 0}
+
+    def call():
+        i = state["i"] = (state["i"] + 1) % copies
+        assert lib.lora_rope(*args[i]) == 0
+
+    for _ in range(copies):
+        call()
+    torch.cuda.synchronize()
+    ms = event_time_ms(call, reps * copies, torch.cuda.current_stream())
+    nbytes = 2 * M * (H + Hk) * D * 2 + M * 4
+    del Qs, Ks
+    return {"workload": "rope", "M": M, "H": H, "Hk": Hk, "D": D, "us_per_call": round(ms * 1e3, 2),
+            "GB/s": round(nbytes / ms / 1e6, 1), "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
 def bench_decode(lora, torch, dev, reps, copies=6):
     """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL), with
     the int4 weight (group 64, fp16 scales) and with the MXFP4 weight (blocks of 32, E8M0 scales):
@@ -483,6 +509,7 @@ def main(argv=None):
                                "decode": bench_decode(lora, torch, dev, 20),
                                "rmsnorm": bench_rmsnorm(lora, torch, dev, 20),
                                "lm_head_ce": bench_ce(lora, torch, dev, 5),
+                               "rope": bench_rope(lora, torch, dev, 20),
                                "torch_unfused": bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}
     if args.calib_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -289,6 +289,21 @@ lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_s
                     const void* X, const void* W, const int32_t* labels, float* loss,
                     float* loss_sum, void* dX, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- RoPE on the attention projections' outputs ------------------------------------------
+ * Tutorial ch. 5 §5.5 (fused RoPE: each coordinate pair of q and k multiplied by a 2 x 2 rotation,
+ * in one kernel and in place).  For token t at position positions[t] (int32; packed sequences
+ * simply restart their positions), head h and j < rot/2, with theta = pos * base^(-2j/rot):
+ *   (x_j, x_{j+rot/2}) <- (x_j cos theta - x_{j+rot/2} sin theta, x_{j+rot/2} cos theta + x_j sin theta)
+ * (the listing's pairing); coordinates rot .. D-1 are left as they are.  inverse != 0 rotates by
+ * -theta: the gradient with respect to the input, applied to dQ and dK.  Q (M x H x D) and K
+ * (M x Hk x D) bf16, rotated in place (K may be NULL when Hk = 0); D a multiple of 8 in
+ * [16, 1024]; rot a multiple of 16 in [16, D]; base finite and > 1.  Angles, sines and cosines
+ * in fp32 (the angle's rounding is below 1e-3 rad for positions up to 2^14), results rounded to
+ * bf16 once.  Errors: LORA_ERR_SHAPE, LORA_ERR_VALUE (base), LORA_ERR_NULL, LORA_ERR_ALIGN,
+ * LORA_ERR_HIP. */
+lora_status lora_rope(int64_t M, int32_t H, int32_t Hk, int32_t D, int32_t rot, float base,
+                      int32_t inverse, const int32_t* positions, void* Q, void* K, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* lora_status_str(lora_status s);
 

@@ -112,6 +112,11 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* X, const uint16_t* g, uint16_t* Y,
 hipError_t launch_rmsnorm_bwd(const uint16_t* dY, const uint16_t* X, const uint16_t* g, const float* r, uint16_t* dX,
                               float* dg, float* part, int64_t M, int64_t K, hipStream_t s);
 
+// RoPE in place on Q (M x H x D) and K (M x Hk x D), bf16; rot/2 <= kRopeMaxPairs
+constexpr int kRopeMaxPairs = 512;
+hipError_t launch_rope(uint16_t* Q, uint16_t* K, const int32_t* pos, int64_t M, int H, int Hk, int D, int rot,
+                       float base, bool inverse, hipStream_t s);
+
 // SwiGLU gate/up pair over the stacked weight [Wg; Wu]: stacked adapters, activation, upstream
 // gradient of the stacked GEMM, and the split of the stacked adapter gradients
 hipError_t launch_swiglu_stack(const uint16_t* Ag, const uint16_t* Au, const uint16_t* Bg, const uint16_t* Bu,

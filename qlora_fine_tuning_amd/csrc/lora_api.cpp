@@ -627,3 +627,24 @@ lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_s
 }
 
 }  // extern "C"
+
+// ---- RoPE ----
+
+extern "C" {
+
+lora_status lora_rope(int64_t M, int32_t H, int32_t Hk, int32_t D, int32_t rot, float base, int32_t inverse,
+                      const int32_t* positions, void* Q, void* K, void* stream) {
+  if (M < 0 || M >= kMaxElems || H < 1 || Hk < 0 || D < 16 || D % 8 != 0 || D > 2 * kRopeMaxPairs) return LORA_ERR_SHAPE;
+  if (rot < 16 || rot % 16 != 0 || rot > D) return LORA_ERR_SHAPE;
+  if (M * (int64_t)(H + Hk) * D >= kMaxElems) return LORA_ERR_SHAPE;
+  if (!std::isfinite(base) || base <= 1.f) return LORA_ERR_VALUE;
+  if (M == 0) return LORA_OK;  // empty batch: every pointer may be NULL
+  lora_status st = check_ptrs(Q);
+  if (st != LORA_OK) return st;
+  if (positions == nullptr) return LORA_ERR_NULL;
+  if (Hk > 0 && (st = check_ptrs(K)) != LORA_OK) return st;
+  return from_hip(launch_rope(static_cast<uint16_t*>(Q), static_cast<uint16_t*>(K), positions, M, H, Hk, D, rot,
+                              base, inverse != 0, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -51,6 +51,7 @@ SIGNATURES = {
     "mxfp4_decode_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "lora_ce_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "lora_ce": (_i32, [_i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "lora_rope": (_i32, [_i64, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -554,3 +555,41 @@ class LMHeadCrossEntropyFunction(torch.autograd.Function):
         if not torch.equal(g, torch.ones_like(g)):
             dX = (dX.float() * g).to(dX.dtype)
         return dX, None, None, None
+
+
+def lora_rope(Q, K, positions, base: float, *, rot: Optional[int] = None, inverse: bool = False, stream=None):
+    """Rotate Q (M x H x D) and K (M x Hk x D, or None) in place by the positions' angles (inverse:
+    by the negated angles, the backward).  Returns (Q, K)."""
+    lib = load()
+    _want(Q, "Q", torch.bfloat16)
+    _want(positions, "positions", torch.int32)
+    M, H, D = Q.shape
+    Hk = 0
+    if K is not None:
+        _want(K, "K", torch.bfloat16)
+        Hk = K.shape[1]
+    rot = D if rot is None else rot
+    st = lib.lora_rope(M, H, Hk, D, rot, float(base), int(inverse), _ptr(positions), _ptr(Q), _ptr(K),
+                       _stream(stream))
+    _check("lora_rope", st)
+    return Q, K
+
+
+class RoPEFunction(torch.autograd.Function):
+    """Autograd wrapper: rotates copies of Q and K (the inputs stay as they are); the backward
+    rotates the incoming gradients back in place."""
+
+    @staticmethod
+    def forward(ctx, Q, K, positions, base, rot=None):
+        Qr, Kr = Q.clone(), K.clone()
+        lora_rope(Qr, Kr, positions, base, rot=rot)
+        ctx.save_for_backward(positions)
+        ctx.base, ctx.rot = base, rot
+        return Qr, Kr
+
+    @staticmethod
+    def backward(ctx, dQ, dK):
+        (positions,) = ctx.saved_tensors
+        dQ, dK = dQ.contiguous().clone(), dK.contiguous().clone()
+        lora_rope(dQ, dK, positions, ctx.base, rot=ctx.rot, inverse=True)
+        return dQ, dK, None, None, None

@@ -348,3 +348,21 @@ def test_lora_ce_workspace(lib):
     assert lib.lora_ce_workspace_bytes(M, V, K, 0, 1) == full
     assert full < 6.5e9  # the chunk's fp32 logits and bf16 gradient: 4.2 + 2.1 GB
     assert lib.lora_ce_workspace_bytes(M, 100, K, 0, 1) == 0
+
+
+# ---- RoPE ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 2), (dict(H=0), 2), (dict(D=12), 2), (dict(D=2048, rot=64), 2), (dict(rot=24), 2),
+    (dict(rot=160), 2), (dict(base=1.0), 8), (dict(base=float("nan")), 8),
+    (dict(Q=NUL), 1), (dict(pos=NUL), 1), (dict(K=NUL), 1), (dict(Q=MIS), 4), (dict(K=MIS), 4),
+])
+def test_lora_rope_validation(lib, kw, code):
+    p = dict(M=64, H=4, Hk=2, D=128, rot=128, base=10000.0, inv=0, pos=P, Q=P, K=P)
+    p.update(kw)
+    assert lib.lora_rope(p["M"], p["H"], p["Hk"], p["D"], p["rot"], p["base"], p["inv"], p["pos"], p["Q"], p["K"],
+                         None) == code
+
+
+def test_lora_rope_empty_batch_needs_no_pointers(lib):
+    assert lib.lora_rope(0, 4, 2, 128, 128, 10000.0, 0, None, None, None, None) == 0
