@@ -143,12 +143,13 @@ def bench_torch_unfused(torch, X, W, A, B, dY, scale, reps):
             "note": "bf16 torch.matmul / addmm, one GEMM per product, fp32 accumulation inside each"}
 
 
-def bench_qlora_ffn(lora, torch, dev, reps):
+def bench_qlora_ffn(lora, torch, dev, reps, group=64):
+    """QLoRA fwd+bwd on the FFN shape; group 64: int4 weights with fp16 scales, group 32: MXFP4."""
     from qlora_fine_tuning_amd.workloads import workload_inputs
 
     inp = workload_inputs("qlora_ffn")
     M, N, K, R = inp.M, inp.N, inp.K, inp.R
-    Wq, Ws = lora.qlora_quantize(torch.from_numpy(inp.W).to(dev))
+    Wq, Ws = lora.qlora_quantize(torch.from_numpy(inp.W).to(dev), group=group)
     X, A, B, dY = (dev_bits(getattr(inp, n), dev) for n in ("X", "A", "B", "dY"))
     Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     XA = torch.empty(M, R, dtype=torch.float32, device=dev)
@@ -167,7 +168,8 @@ def bench_qlora_ffn(lora, torch, dev, reps):
     torch.cuda.synchronize()
     ms = event_time_ms(step, reps, stream)
     fl = lora_flops(M, N, K, R)
-    return {"workload": "qlora_ffn", "M": M, "N": N, "K": K, "r": R, "ms_per_step": round(ms, 4),
+    return {"workload": "qlora_ffn", "weights": "int4" if group == 64 else "mxfp4", "M": M, "N": N, "K": K,
+            "r": R, "ms_per_step": round(ms, 4),
             "TFLOP/s": round(fl / ms / 1e9, 2), "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
 
@@ -506,6 +508,7 @@ def main(argv=None):
         result["secondary"] = {"mlp": bench_mlp(lora, torch, dev, 20),
                                "mlp_swiglu": bench_swiglu(lora, torch, dev, 20),
                                "qlora": bench_qlora_ffn(lora, torch, dev, 20),
+                               "qlora_mxfp4": bench_qlora_ffn(lora, torch, dev, 20, group=32),
                                "decode": bench_decode(lora, torch, dev, 20),
                                "rmsnorm": bench_rmsnorm(lora, torch, dev, 20),
                                "lm_head_ce": bench_ce(lora, torch, dev, 5),

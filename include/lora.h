@@ -60,7 +60,7 @@ typedef enum lora_status {
   LORA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
   LORA_ERR_DTYPE = 5,     /* unknown element type */
   LORA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the matching *_workspace_bytes() */
-  LORA_ERR_GROUP = 7,     /* int4 group size other than 64 */
+  LORA_ERR_GROUP = 7,     /* 4-bit group other than 64 (int4) or 32 (MXFP4) */
   LORA_ERR_VALUE = 8,     /* scale not finite, or eps not finite and >= 0 */
   LORA_ERR_HIP = 9        /* a HIP launch failed; lora_last_hip_error() names it */
 } lora_status;
@@ -118,7 +118,11 @@ lora_status lora_bwd_dadb(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_
  * scaling coefficient; the exact format is given at the top of this header).
  *   W  [N][K] fp32                        (input)
  *   Wq [N][K/2] bytes, Ws [N][K/group] fp16 (outputs)
- * group must be 64.  Codes are decided exactly (ties to even on the exact quotient). */
+ * group must be 64.  Codes are decided exactly (ties to even on the exact quotient).
+ * group = 32 selects the MXFP4 format instead (see mxfp4_quantize: E2M1 codes in the same nibble
+ * layout, Ws = N x K/32 E8M0 exponent bytes) in qlora_quantize, qlora_dequant, qlora_fwd,
+ * qlora_bwd and qlora_bwd_dx: QLoRA training and inference with FP4 weights, unpacked in
+ * registers by the gfx950 scaled FP4 conversion. */
 lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W,
                            uint8_t* Wq, void* Ws, void* stream);
 
@@ -296,7 +300,8 @@ lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_s
  *   (x_j, x_{j+rot/2}) <- (x_j cos theta - x_{j+rot/2} sin theta, x_{j+rot/2} cos theta + x_j sin theta)
  * (the listing's pairing); coordinates rot .. D-1 are left as they are.  inverse != 0 rotates by
  * -theta: the gradient with respect to the input, applied to dQ and dK.  Q (M x H x D) and K
- * (M x Hk x D) bf16, rotated in place (K may be NULL when Hk = 0); D a multiple of 8 in
+ * (M x Hk x D) bf16, rotated in place (K may be NULL when Hk = 0; Q and K must not overlap,
+ * since an overlapped element would be rotated twice); D a multiple of 8 in
  * [16, 1024]; rot a multiple of 16 in [16, D]; base finite and > 1.  Angles, sines and cosines
  * in fp32 (the angle's rounding is below 1e-3 rad for positions up to 2^14), results rounded to
  * bf16 once.  Errors: LORA_ERR_SHAPE, LORA_ERR_VALUE (base), LORA_ERR_NULL, LORA_ERR_ALIGN,

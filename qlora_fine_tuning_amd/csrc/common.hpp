@@ -206,6 +206,29 @@ __device__ __forceinline__ void store_block_bf16(const f32x4* acc, uint16_t* sta
   }
 }
 
+// ---- MXFP4: E2M1 codes in the int4 nibble layout, one E8M0 exponent per 32 k ----
+// E2M1 pairs to bf16 with the block scale, on the gfx950 conversion instruction: byte `sel` of
+// `codes` (low nibble first) becomes the low and high bf16 of the result, value * scale (exact
+// here: at most two significant bits, normal exponents)
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t codes, float scale, int sel) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t r;
+  switch (sel) {  // the selector must be a constant
+    case 0: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0); break;
+    case 1: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1); break;
+    case 2: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2); break;
+    default: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3); break;
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+// 8 codes (one dword, k ascending from the low nibble) to 8 bf16 in k order
+__device__ __forceinline__ u32x4 dequant8_fp4(uint32_t codes, float scale) {
+  return (u32x4){fp4x2_to_bf16x2(codes, scale, 0), fp4x2_to_bf16x2(codes, scale, 1),
+                 fp4x2_to_bf16x2(codes, scale, 2), fp4x2_to_bf16x2(codes, scale, 3)};
+}
+// E8M0 exponent byte -> 2^(E - 127) (E in 1..254; the quantiser writes 2..252)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+
 // Workgroup id -> logical tile id such that each of the 8 XCDs (which receive workgroups
 // round-robin by id) owns one contiguous range of logical tiles; a bijection for any total.
 __device__ __forceinline__ int xcd_remap(int bid, int total) {

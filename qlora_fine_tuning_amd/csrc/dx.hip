@@ -48,7 +48,9 @@ __device__ __forceinline__ f32x4 ld_part(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCpolSc1);
 }
 
-template <int RP, bool INT4>
+// FP4 (with INT4): the 4-bit weight is MXFP4 (E2M1 codes, one E8M0 byte per 32 k; a thread's 64
+// codes are two blocks, whose two bytes sit where the int4 fp16 scale would).
+template <int RP, bool INT4, bool FP4 = false>
 __global__ void __launch_bounds__(kThreads)
 dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
                const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
@@ -144,7 +146,10 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
   auto store_w4_part = [&](const W4& v, uint16_t* w, int d) {  // packed dword d of the 64 codes
     uint16_t* row = w + qblk * 4096 + qrow * 64;
-    st16(row + ((d ^ wsw(qrow)) << 3), dequant8_mix(v.q[d >> 2][d & 3], i4mix(half_bits_to_f32((uint16_t)v.s))));
+    if constexpr (FP4)  // dwords 0-3 are block 0, 4-7 block 1
+      st16(row + ((d ^ wsw(qrow)) << 3), dequant8_fp4(v.q[d >> 2][d & 3], e8m0_to_f32((v.s >> (8 * (d >> 2))) & 0xffu)));
+    else
+      st16(row + ((d ^ wsw(qrow)) << 3), dequant8_mix(v.q[d >> 2][d & 3], i4mix(half_bits_to_f32((uint16_t)v.s))));
   };
   auto store_w4 = [&](const W4& v, uint16_t* w) {
 #pragma unroll
@@ -508,7 +513,7 @@ __global__ void zero_u32_kernel(uint32_t* p, int n) {  // the split arrival coun
   if (i < n) p[i] = 0u;
 }
 
-template <int RP, bool INT4>
+template <int RP, bool INT4, bool FP4 = false>
 static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
   const int tiles = dx_tiles(a.M, a.K);
   const int splits = dx_splits(a.M, a.N, a.K, a.R);
@@ -517,7 +522,7 @@ static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4>), dim3(tiles * splits), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4, FP4>), dim3(tiles * splits), dim3(kThreads), 0, s,
                      (const uint16_t*)a.dY, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.dX, a.G, (int)a.M, (int)a.N, (int)a.K,
                      (int)a.R, a.scale, splits, a.part, a.ctr);
@@ -526,6 +531,11 @@ static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
 
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
+  if (int4 && a.fp4) {
+    if (rp == 16) return launch_dx_rp<16, true, true>(a, s);
+    if (rp == 32) return launch_dx_rp<32, true, true>(a, s);
+    return launch_dx_rp<64, true, true>(a, s);
+  }
   if (int4) {
     if (rp == 16) return launch_dx_rp<16, true>(a, s);
     if (rp == 32) return launch_dx_rp<32, true>(a, s);

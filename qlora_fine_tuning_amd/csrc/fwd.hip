@@ -65,7 +65,9 @@ __device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stag
 // and H (M x Nh) out; kEpiCeStats, the logits X W^T of an LM head (no adapter): per-row (max, sum
 // of exp) of each wave's 128 columns into `stats`, the label's logit, and the fp32 logits
 // themselves into `logits` when that is set (the gradient pass then reads them).
-template <int RP, bool INT4, bool PANEL, int EPI>
+// FP4 (with INT4): the 4-bit weight is MXFP4, E2M1 codes in the same nibble layout and one E8M0
+// exponent byte per 32 k (the two bytes of a 64-k step sit where the int4 fp16 scale would).
+template <int RP, bool INT4, bool PANEL, int EPI, bool FP4 = false>
 __global__ void __launch_bounds__(kThreads)
 fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
@@ -172,8 +174,12 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   auto store_w4_part = [&](const W4& v, uint16_t* w, int p) {
     const int q = p >> 2, d = p & 3;
     const int r = q * 128 + (tid >> 1);
-    st16(w + lds_offf(r, (tid & 1) * 4 + d),
-         dequant8_mix(v.q[q][d], i4mix(half_bits_to_f32((uint16_t)v.s[q]))));
+    if constexpr (FP4)  // this thread's 32 codes are one block: its exponent byte is (tid & 1)
+      st16(w + lds_offf(r, (tid & 1) * 4 + d),
+           dequant8_fp4(v.q[q][d], e8m0_to_f32((v.s[q] >> (8 * (tid & 1))) & 0xffu)));
+    else
+      st16(w + lds_offf(r, (tid & 1) * 4 + d),
+           dequant8_mix(v.q[q][d], i4mix(half_bits_to_f32((uint16_t)v.s[q]))));
   };
   auto store_w4 = [&](const W4& v, uint16_t* w) {
 #pragma unroll
@@ -522,11 +528,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   }
 }
 
-template <int RP, bool INT4, bool PANEL, int EPI = kEpiLora>
+template <int RP, bool INT4, bool PANEL, int EPI = kEpiLora, bool FP4 = false>
 static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
   // SwiGLU: N = 2 Nh stacked rows, one tile per 128 outputs of H: ceil(2 Nh / 256) of them
   const int tiles = (int)(((a.M + kTile - 1) / kTile) * ((a.N + kTile - 1) / kTile));
-  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, EPI>), dim3(tiles), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, EPI, FP4>), dim3(tiles), dim3(kThreads), 0, s,
                      (const uint16_t*)a.X, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (uint16_t*)a.H, a.ce, (int)a.M, (int)a.N,
                      (int)a.K, (int)a.R, a.scale);
@@ -548,12 +554,18 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
                                          a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
     if (e != hipSuccess) return e;
     if (swiglu) return launch_fwd_rp<64, false, false, kEpiSwiglu>(a, s);
+    if (int4 && a.fp4) return launch_fwd_rp<64, true, false, kEpiLora, true>(a, s);
     return int4 ? launch_fwd_rp<64, true, false>(a, s) : launch_fwd_rp<64, false, false>(a, s);
   }
   if (swiglu) {
     if (rp == 16) return launch_fwd_rp<16, false, true, kEpiSwiglu>(a, s);
     if (rp == 32) return launch_fwd_rp<32, false, true, kEpiSwiglu>(a, s);
     return launch_fwd_rp<64, false, true, kEpiSwiglu>(a, s);
+  }
+  if (int4 && a.fp4) {
+    if (rp == 16) return launch_fwd_rp<16, true, true, kEpiLora, true>(a, s);
+    if (rp == 32) return launch_fwd_rp<32, true, true, kEpiLora, true>(a, s);
+    return launch_fwd_rp<64, true, true, kEpiLora, true>(a, s);
   }
   if (int4) {
     if (rp == 16) return launch_fwd_rp<16, true, true>(a, s);

@@ -123,27 +123,6 @@ quantize_mxfp4_kernel(const float* __restrict__ W, uint8_t* __restrict__ Wq, uin
   We[b] = (uint8_t)(se + 127);
 }
 
-// E2M1 pairs to bf16 with the block scale, on the gfx950 conversion instruction: byte `sel` of
-// `codes` (low nibble first) becomes the low and high bf16 of the result, value * scale (exact
-// here: at most two significant bits, normal exponents)
-__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t codes, float scale, int sel) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t r;
-  switch (sel) {  // the selector must be a constant
-    case 0: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0); break;
-    case 1: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1); break;
-    case 2: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2); break;
-    default: r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3); break;
-  }
-  return __builtin_bit_cast(uint32_t, r);
-}
-// 8 codes (one dword, k ascending from the low nibble) to 8 bf16 in k order
-__device__ __forceinline__ u32x4 dequant8_fp4(uint32_t codes, float scale) {
-  return (u32x4){fp4x2_to_bf16x2(codes, scale, 0), fp4x2_to_bf16x2(codes, scale, 1),
-                 fp4x2_to_bf16x2(codes, scale, 2), fp4x2_to_bf16x2(codes, scale, 3)};
-}
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }  // E >= 2 here
-
 // dequantise: one thread per block of 32 codes
 __global__ void __launch_bounds__(256)
 dequant_mxfp4_kernel(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ We, uint16_t* __restrict__ Wout,

@@ -35,6 +35,7 @@ struct FwdArgs {
   float scale;
   void* H = nullptr;  // SwiGLU pair (bf16 W = [Wg; Wu], N = 2 Nh): H = silu(G) U, M x Nh
   CeArgs ce = {};
+  bool fp4 = false;   // 4-bit W is MXFP4 (E8M0 exponents in Ws) rather than int4 with fp16 scales
 };
 
 struct DxArgs {
@@ -50,6 +51,7 @@ struct DxArgs {
   float scale;
   uint32_t* ctr;   // split-N path (bf16 / int4): dx_tiles() arrival counters,
   float* part;     // and dx_part_bytes() bytes of split partials
+  bool fp4 = false;  // 4-bit W is MXFP4 rather than int4
 };
 
 struct DadbArgs {

@@ -92,7 +92,7 @@ bool use_gemv(int64_t M, int64_t K) { return M >= 1 && M <= 8 && K % 1024 == 0; 
 // The two halves of the backward; sizes and pointers validated by the callers.
 lora_status bwd_dx_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R,
                           float scale, const void* dY, const void* W, const void* Ws, const void* A,
-                          const void* B, void* dX, void* ws, size_t ws_bytes, void* stream) {
+                          const void* B, void* dX, void* ws, size_t ws_bytes, void* stream, bool fp4 = false) {
   const BwdLayout lay = bwd_layout(M, N, K, R, dt != LORA_F32);
   if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
   if (!aligned16(ws)) return LORA_ERR_ALIGN;
@@ -101,6 +101,7 @@ lora_status bwd_dx_common(bool int4, lora_dtype dt, int64_t M, int64_t N, int64_
   float* G = reinterpret_cast<float*>(base + lay.g);
   DxArgs a{dY, W, Ws, A, B, dX, G, M, N, K, R, scale, reinterpret_cast<uint32_t*>(base + lay.ctr),
            reinterpret_cast<float*>(base + lay.dxp)};
+  a.fp4 = fp4;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == LORA_F32) return from_hip(launch_dx_f32(a, s));
   if (R > 32) {  // the rank-64 input-gradient kernel reads G from this pass
@@ -247,22 +248,27 @@ lora_status lora_bwd_dadb(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_
 
 lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W, uint8_t* Wq,
                            void* Ws, void* stream) {
-  if (group != 64) return LORA_ERR_GROUP;
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
   if (N <= 0 || K <= 0 || K % 64 != 0 || N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems)
     return LORA_ERR_SHAPE;
   lora_status st = check_ptrs(W, Wq, Ws);
   if (st != LORA_OK) return st;
+  if (group == 32)
+    return from_hip(launch_quantize_mxfp4(N, K, W, Wq, static_cast<uint8_t*>(Ws), static_cast<hipStream_t>(stream)));
   return from_hip(launch_quantize_int4(N, K, W, Wq, static_cast<uint16_t*>(Ws),
                                        static_cast<hipStream_t>(stream)));
 }
 
 lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq, const void* Ws,
                           void* W_bf16, void* stream) {
-  if (group != 64) return LORA_ERR_GROUP;
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
   if (N <= 0 || K <= 0 || K % 64 != 0 || N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems)
     return LORA_ERR_SHAPE;
   lora_status st = check_ptrs(Wq, Ws, W_bf16);
   if (st != LORA_OK) return st;
+  if (group == 32)
+    return from_hip(launch_dequant_mxfp4(N, K, Wq, static_cast<const uint8_t*>(Ws), static_cast<uint16_t*>(W_bf16),
+                                         static_cast<hipStream_t>(stream)));
   return from_hip(launch_dequant_int4(N, K, Wq, static_cast<const uint16_t*>(Ws),
                                       static_cast<uint16_t*>(W_bf16), static_cast<hipStream_t>(stream)));
 }
@@ -276,7 +282,7 @@ size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
 lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
                       const void* X, const uint8_t* Wq, const void* Ws, const void* A, const void* B,
                       void* Y, float* XA, void* ws, size_t ws_bytes, void* stream) {
-  if (group != 64) return LORA_ERR_GROUP;
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
   lora_status st = check_dims(M, N, K, R);
   if (st != LORA_OK) return st;
   if (!std::isfinite(scale)) return LORA_ERR_VALUE;
@@ -290,8 +296,9 @@ lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return LORA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return LORA_ERR_ALIGN;
   FwdArgs a{X, Wq, Ws, A, B, Y, XA, M, N, K, R, scale};
+  a.fp4 = group == 32;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (use_gemv(M, K)) return from_hip(launch_gemv_int4(a, ws, s));
+  if (use_gemv(M, K)) return from_hip(a.fp4 ? launch_gemv_mxfp4(a, ws, s) : launch_gemv_int4(a, ws, s));
   return from_hip(launch_fwd_mfma(a, true, s));
 }
 
@@ -304,14 +311,14 @@ lora_status qlora_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
                       const void* dY, const void* X, const uint8_t* Wq, const void* Ws, const void* A,
                       const void* B, const float* XA, void* dX, float* dA, float* dB, void* ws,
                       size_t ws_bytes, void* stream) {
-  if (group != 64) return LORA_ERR_GROUP;
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
   lora_status st = check_dims(M, N, K, R);
   if (st != LORA_OK) return st;
   if (!std::isfinite(scale)) return LORA_ERR_VALUE;
   st = check_ptrs(Wq, Ws, A, B, dA, dB);
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, X, XA, dX)) != LORA_OK) return st;
-  st = bwd_dx_common(true, LORA_BF16, M, N, K, R, scale, dY, Wq, Ws, A, B, dX, ws, ws_bytes, stream);
+  st = bwd_dx_common(true, LORA_BF16, M, N, K, R, scale, dY, Wq, Ws, A, B, dX, ws, ws_bytes, stream, group == 32);
   if (st != LORA_OK) return st;
   return bwd_dadb_common(LORA_BF16, M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
 }
@@ -319,14 +326,14 @@ lora_status qlora_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
 lora_status qlora_bwd_dx(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
                          const void* dY, const uint8_t* Wq, const void* Ws, const void* A,
                          const void* B, void* dX, void* ws, size_t ws_bytes, void* stream) {
-  if (group != 64) return LORA_ERR_GROUP;
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
   lora_status st = check_dims(M, N, K, R);
   if (st != LORA_OK) return st;
   if (!std::isfinite(scale)) return LORA_ERR_VALUE;
   st = check_ptrs(Wq, Ws, A, B);
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, dX)) != LORA_OK) return st;
-  return bwd_dx_common(true, LORA_BF16, M, N, K, R, scale, dY, Wq, Ws, A, B, dX, ws, ws_bytes, stream);
+  return bwd_dx_common(true, LORA_BF16, M, N, K, R, scale, dY, Wq, Ws, A, B, dX, ws, ws_bytes, stream, group == 32);
 }
 
 size_t lora_swiglu_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {

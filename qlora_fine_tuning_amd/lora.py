@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "liblora_mi355x.so")
 
 LORA_F32, LORA_BF16 = 0, 1
 GROUP = 64
+MXFP4_GROUP = 32  # the group argument that selects MXFP4 weights
 STATUS = {
     0: "LORA_OK", 1: "LORA_ERR_NULL", 2: "LORA_ERR_SHAPE", 3: "LORA_ERR_RANK", 4: "LORA_ERR_ALIGN",
     5: "LORA_ERR_DTYPE", 6: "LORA_ERR_WORKSPACE", 7: "LORA_ERR_GROUP", 8: "LORA_ERR_VALUE",
@@ -210,20 +211,27 @@ def qlora_bwd_dx(dY, Wq, Ws, A, B, scale: float, *, ws, dX=None, stream=None):
     if dX is None:
         dX = torch.empty((M, K), dtype=torch.bfloat16, device=dY.device)
     ws, wsb = _ws_for(lib, LORA_BF16, M, N, K, R, ws, dY.device)
-    st = lib.qlora_bwd_dx(M, N, K, R, float(scale), GROUP, _ptr(dY), _ptr(Wq), _ptr(Ws), _ptr(A), _ptr(B),
+    st = lib.qlora_bwd_dx(M, N, K, R, float(scale), _group_of(Ws), _ptr(dY), _ptr(Wq), _ptr(Ws), _ptr(A), _ptr(B),
                           _ptr(dX), _ptr(ws), wsb, _stream(stream))
     _check("qlora_bwd_dx", st)
     return dX
 
 
-def qlora_quantize(W32, *, stream=None):
-    """fp32 W (N x K) -> (Wq uint8 N x K/2, Ws fp16 N x K/64)."""
+def _group_of(Ws) -> int:
+    """The 4-bit format from its scales: fp16 per 64 k (int4) or E8M0 bytes per 32 k (MXFP4)."""
+    return MXFP4_GROUP if Ws.dtype == torch.uint8 else GROUP
+
+
+def qlora_quantize(W32, *, group: int = GROUP, stream=None):
+    """fp32 W (N x K) -> (Wq uint8 N x K/2, Ws): group 64, int4 codes with fp16 scales (N x K/64);
+    group 32, MXFP4 (E2M1 codes, E8M0 exponent bytes N x K/32)."""
     lib = load()
     _want(W32, "W", torch.float32)
     N, K = W32.shape
     Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W32.device)
-    Ws = torch.empty((N, max(K // GROUP, 1)), dtype=torch.float16, device=W32.device)
-    st = lib.qlora_quantize(N, K, GROUP, _ptr(W32), _ptr(Wq), _ptr(Ws), _stream(stream))
+    sdt = torch.uint8 if group == MXFP4_GROUP else torch.float16
+    Ws = torch.empty((N, max(K // group, 1)), dtype=sdt, device=W32.device)
+    st = lib.qlora_quantize(N, K, group, _ptr(W32), _ptr(Wq), _ptr(Ws), _stream(stream))
     _check("qlora_quantize", st)
     return Wq, Ws
 
@@ -234,7 +242,7 @@ def qlora_dequant(Wq, Ws, *, out=None, stream=None):
     N, K = Wq.shape[0], Wq.shape[1] * 2
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=Wq.device)
-    st = lib.qlora_dequant(N, K, GROUP, _ptr(Wq), _ptr(Ws), _ptr(out), _stream(stream))
+    st = lib.qlora_dequant(N, K, _group_of(Ws), _ptr(Wq), _ptr(Ws), _ptr(out), _stream(stream))
     _check("qlora_dequant", st)
     return out
 
@@ -258,7 +266,7 @@ def qlora_fwd(X, Wq, Ws, A, B, scale: float, *, Y=None, XA=None, save_xa: bool =
         # the decode path's arrival counters must start at zero (each call leaves them zero)
         ws = torch.zeros(int(need), dtype=torch.uint8, device=dev)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    st = lib.qlora_fwd(M, N, K, R, float(scale), GROUP, _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A), _ptr(B),
+    st = lib.qlora_fwd(M, N, K, R, float(scale), _group_of(Ws), _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A), _ptr(B),
                        _ptr(Y), _ptr(XA), _ptr(ws), wsb, _stream(stream))
     _check("qlora_fwd", st)
     return Y, XA
@@ -283,7 +291,7 @@ def qlora_bwd(dY, X, Wq, Ws, A, B, XA, scale: float, *, dX=None, dA=None, dB=Non
     need = lib.qlora_bwd_workspace_bytes(M, N, K, R)
     if ws is None:
         ws = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
-    st = lib.qlora_bwd(M, N, K, R, float(scale), GROUP, _ptr(dY), _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A),
+    st = lib.qlora_bwd(M, N, K, R, float(scale), _group_of(Ws), _ptr(dY), _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A),
                        _ptr(B), _ptr(XA), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                        ws.numel() * ws.element_size(), _stream(stream))
     _check("qlora_bwd", st)

@@ -135,11 +135,16 @@ def test_split_backward_validation(lib):
     assert lib.lora_bwd_dadb(1, 64, 256, 256, 16, 2.0, P, P, NUL, P, P, P, need, None) == 1
     assert lib.lora_bwd_dadb(1, 64, 256, 200, 16, 2.0, P, P, P, P, P, P, need, None) == 2
     assert lib.qlora_bwd_dx(64, 256, 256, 16, 2.0, 64, P, P, P, P, P, P, NUL, 0, None) == 6
-    assert lib.qlora_bwd_dx(64, 256, 256, 16, 2.0, 32, P, P, P, P, P, P, P, need, None) == 7
+    assert lib.qlora_bwd_dx(64, 256, 256, 16, 2.0, 16, P, P, P, P, P, P, P, need, None) == 7
 
 
 def test_qlora_validation(lib):
-    assert lib.qlora_quantize(64, 128, 32, P, P, P, None) == 7
+    assert lib.qlora_quantize(64, 128, 16, P, P, P, None) == 7
+    # group 32 is the MXFP4 format: validated like group 64 (every call here fails before a launch)
+    assert lib.qlora_quantize(64, 100, 32, P, P, P, None) == 2
+    assert lib.qlora_dequant(64, 128, 32, P, MIS, P, None) == 4
+    assert lib.qlora_fwd(4, 256, 1024, 16, 2.0, 32, P, P, P, P, P, P, P, NUL, 0, None) == 6
+    assert lib.qlora_bwd(64, 256, 256, 16, 2.0, 32, P, P, P, P, P, P, P, P, P, P, P, 0, None) == 6
     assert lib.qlora_quantize(64, 100, 64, P, P, P, None) == 2
     assert lib.qlora_quantize(64, 128, 64, NUL, P, P, None) == 1
     assert lib.qlora_dequant(64, 128, 64, P, MIS, P, None) == 4

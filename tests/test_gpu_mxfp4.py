@@ -100,3 +100,54 @@ def test_mxfp4_decode_workspace_reuse_and_determinism(gpu_lib):
             else:
                 assert torch.equal(Y, first[M][0]) and torch.equal(XA, first[M][1])
     assert not ws[: 4 * (N // 64)].any(), "arrival counters not left at zero"
+
+
+# ---- QLoRA training and prefill with MXFP4 weights (qlora_* with group 32) ----------------
+
+def _check_qlora_mx(lib, inp, sampled):
+    from parity_util import sample_rows
+    Wq, We, wt = _quant_check(lib, inp.W)  # codes and exponents bit for bit first
+    X, A, B = (to_dev(inp, n) for n in ("X", "A", "B"))
+    Y, XA = lib.qlora_fwd(X, Wq, We, A, B, inp.scale)
+    x, a, b = (values(inp, n) for n in ("X", "A", "B"))
+    rows = sample_rows(inp.M) if sampled else np.arange(inp.M)
+    idx = torch.from_numpy(rows).cuda()
+    Yr, XAr = oracle.lora_forward_rows(x, wt, a, b, inp.scale, rows)
+    torch.cuda.synchronize()
+    assert_close("Y", host(Y[idx]), Yr)
+    assert_close("XA", host(XA[idx]), XAr)
+    dY = to_dev(inp, "dY")
+    dX, dA, dB = lib.qlora_bwd(dY, X, Wq, We, A, B, XA, inp.scale)
+    torch.cuda.synchronize()
+    dy = values(inp, "dY")
+    assert_close("dX", host(dX[idx]), oracle.lora_backward_dx_rows(dy, wt, a, b, inp.scale, rows))
+    assert_close("dA", host(dA), inp.scale * ((dy @ b).T @ x))
+    assert_close("dB", host(dB), inp.scale * (dy.T @ (x @ a.T)))
+
+
+@pytest.mark.parametrize("M,N,K,R", [(300, 576, 512, 16), (257, 256, 1024, 8), (9, 320, 768, 32),
+                                     (130, 320, 256, 64), (65, 448, 2048, 24)])
+def test_mxfp4_qlora_small_shapes(gpu_lib, M, N, K, R):
+    print(f"case mxfp4 qlora M={M} N={N} K={K} R={R}", flush=True)
+    _check_qlora_mx(gpu_lib, make_inputs(M, N, K, R, seed=700 + M, int4=True), sampled=False)
+
+
+def test_mxfp4_qlora_ffn_sampled(gpu_lib):
+    # the QLoRA FFN shape (M=4096, K=5120 -> N=27648, r=16): the input gradient splits N
+    print("case mxfp4 qlora_ffn (sampled rows)", flush=True)
+    _check_qlora_mx(gpu_lib, workload_inputs("qlora_ffn"), sampled=True)
+
+
+def test_mxfp4_qlora_autograd(gpu_lib):
+    print("case mxfp4 qlora autograd", flush=True)
+    inp = make_inputs(200, 320, 512, 16, seed=11, int4=True)
+    Wq, We = gpu_lib.qlora_quantize(torch.from_numpy(inp.W).cuda(), group=32)
+    X, A, B, dY = (to_dev(inp, n) for n in ("X", "A", "B", "dY"))
+    leaves = [t.detach().clone().requires_grad_(True) for t in (X, A, B)]
+    Y = gpu_lib.QLoRALinearFunction.apply(leaves[0], Wq, We, leaves[1], leaves[2], inp.scale)
+    Y.backward(dY)
+    Yd, XA = gpu_lib.qlora_fwd(X, Wq, We, A, B, inp.scale)
+    dX, dA, dB = gpu_lib.qlora_bwd(dY, X, Wq, We, A, B, XA, inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Yd) and torch.equal(leaves[0].grad, dX)
+    assert torch.equal(leaves[1].grad, dA.to(A.dtype)) and torch.equal(leaves[2].grad, dB.to(B.dtype))
