@@ -206,6 +206,22 @@ lora_status lora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float sc
                             const float* XA, void* dX, float* dAg, float* dAu, float* dBg,
                             float* dBu, void* ws, size_t ws_bytes, void* stream);
 
+/* The SwiGLU pair with the frozen stacked weight [Wg; Wu] in 4 bits (QLoRA): group 64, int4 codes
+ * with fp16 scales (Wgus: 2N x K/64); group 32, MXFP4 codes with E8M0 bytes (Wgus: 2N x K/32);
+ * Wguq: 2N x K/2 bytes, as qlora_quantize writes for the 2N x K fp32 stacked weight.  Otherwise
+ * as lora_swiglu_fwd / lora_swiglu_bwd, with the same workspace sizes; the codes are unpacked in
+ * registers on their way to the matrix cores.  Errors: also LORA_ERR_GROUP. */
+lora_status qlora_swiglu_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                             int32_t group, const void* X, const uint8_t* Wguq, const void* Wgus,
+                             const void* Ag, const void* Au, const void* Bg, const void* Bu, void* H,
+                             void* GU, float* XA, void* ws, size_t ws_bytes, void* stream);
+lora_status qlora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+                             int32_t group, const void* dH, const void* X, const uint8_t* Wguq,
+                             const void* Wgus, const void* Ag, const void* Au, const void* Bg,
+                             const void* Bu, const void* GU, const float* XA, void* dX, float* dAg,
+                             float* dAu, float* dBg, float* dBu, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* ---- RMSNorm ahead of a projection ------------------------------------------------------
  * Tutorial ch. 5 §5.4 (fused RMSNorm: the mean square of each row, eps, the root and the
  * per-feature scale g in one kernel that reads and writes the hidden state once):

@@ -75,7 +75,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 float* __restrict__ XA, uint16_t* __restrict__ H, CeArgs ce, int M, int N, int K, int R,
                 float scale) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu, CE = EPI >= kEpiCeStats, LORA = !CE;
-  static_assert(EPI == kEpiLora || !INT4, "the SwiGLU pair and the LM head take a bf16 weight");
+  static_assert(!(CE && INT4), "the LM head takes a bf16 weight");
   static_assert(!(CE && PANEL), "the LM head has no adapter");
   constexpr int TT = kTile * kStep;  // elements of one 256 x 64 operand tile
   constexpr int AROWS = RP < 32 ? 32 : RP;  // adapter rows in LDS: each wave copies 8k of them
@@ -103,7 +103,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   // rows 128-255 the up rows (rWu, Nh rows further on)
   const int nh = SWIGLU ? N / 2 : N, ng = SWIGLU ? tn * (kTile / 2) : n0;
   rsrc_t rW, rWu;
-  if constexpr (SWIGLU) {
+  if constexpr (SWIGLU && !INT4) {
     const uint32_t bytes = (uint32_t)min(nh - ng, kTile / 2) * rowb;
     rW = make_rsrc(static_cast<const uint16_t*>(Wp) + (size_t)ng * K, bytes);
     rWu = make_rsrc(static_cast<const uint16_t*>(Wp) + (size_t)(nh + ng) * K, bytes);
@@ -155,19 +155,32 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   // fallback for callers that do not keep XA) uses one set loaded one step ahead (its two-set
   // form crashes the compiler).
   constexpr bool AHEAD = INT4 && (RP <= 32 || !PANEL);
-  rsrc_t rWq, rWs;
+  // 4-bit W: codes and scales (fp16 per 64 k, or E8M0 bytes per 32 k: the same bytes per row);
+  // SwiGLU takes tile rows 0-127 from the gate rows (rWq, rWs) and 128-255 from the up rows
+  rsrc_t rWq, rWs, rWqU, rWsU;
   if constexpr (INT4) {
-    const int nrows = min(N - n0, kTile);
-    rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + (size_t)n0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2));
-    rWs = make_rsrc(Wscale + (size_t)n0 * (K / 64), (uint32_t)nrows * (uint32_t)(K / 64) * 2u);
+    const uint8_t* W8 = static_cast<const uint8_t*>(Wp);
+    if constexpr (SWIGLU) {
+      const uint32_t nrows = (uint32_t)min(nh - ng, kTile / 2);
+      rWq = make_rsrc(W8 + (size_t)ng * (K / 2), nrows * (uint32_t)(K / 2));
+      rWqU = make_rsrc(W8 + (size_t)(nh + ng) * (K / 2), nrows * (uint32_t)(K / 2));
+      rWs = make_rsrc(Wscale + (size_t)ng * (K / 64), nrows * (uint32_t)(K / 64) * 2u);
+      rWsU = make_rsrc(Wscale + (size_t)(nh + ng) * (K / 64), nrows * (uint32_t)(K / 64) * 2u);
+    } else {
+      const int nrows = min(N - n0, kTile);
+      rWq = make_rsrc(W8 + (size_t)n0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2));
+      rWs = make_rsrc(Wscale + (size_t)n0 * (K / 64), (uint32_t)nrows * (uint32_t)(K / 64) * 2u);
+    }
   }
   auto load_w4 = [&](W4& v, int kn) {
     const uint32_t k0 = (uint32_t)min(kn, nk - 1) * kStep;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t r = (uint32_t)(q * 128 + (tid >> 1));
-      v.q[q] = bload16(rWq, r * (uint32_t)(K / 2) + (uint32_t)(tid & 1) * 16u, k0 / 2u);
-      v.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rWs, (int)(r * (uint32_t)(K / 64) * 2u), (int)(k0 / 32u), 0);
+      const uint32_t r = (uint32_t)((SWIGLU ? 0 : q * 128) + (tid >> 1));
+      const rsrc_t& cq = (SWIGLU && q == 1) ? rWqU : rWq;
+      const rsrc_t& cs = (SWIGLU && q == 1) ? rWsU : rWs;
+      v.q[q] = bload16(cq, r * (uint32_t)(K / 2) + (uint32_t)(tid & 1) * 16u, k0 / 2u);
+      v.s[q] = __builtin_amdgcn_raw_buffer_load_b16(cs, (int)(r * (uint32_t)(K / 64) * 2u), (int)(k0 / 32u), 0);
     }
   };
   // part p = 4 q + d: packed dword d (codes k = 8d .. 8d+7 of this half) of row q * 128 + ...
@@ -546,7 +559,23 @@ hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s) { return launch_fwd
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
   const bool swiglu = a.H != nullptr;
-  if (swiglu && int4) return hipErrorInvalidValue;
+  if (swiglu && int4) {  // the SwiGLU pair over a stacked 4-bit weight
+    if (rp == 64 && a.XA != nullptr) {
+      const hipError_t e = launch_panel_xa(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A),
+                                           a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
+      if (e != hipSuccess) return e;
+      return a.fp4 ? launch_fwd_rp<64, true, false, kEpiSwiglu, true>(a, s)
+                   : launch_fwd_rp<64, true, false, kEpiSwiglu, false>(a, s);
+    }
+    if (a.fp4) {
+      if (rp == 16) return launch_fwd_rp<16, true, true, kEpiSwiglu, true>(a, s);
+      if (rp == 32) return launch_fwd_rp<32, true, true, kEpiSwiglu, true>(a, s);
+      return launch_fwd_rp<64, true, true, kEpiSwiglu, true>(a, s);
+    }
+    if (rp == 16) return launch_fwd_rp<16, true, true, kEpiSwiglu>(a, s);
+    if (rp == 32) return launch_fwd_rp<32, true, true, kEpiSwiglu>(a, s);
+    return launch_fwd_rp<64, true, true, kEpiSwiglu>(a, s);
+  }
   if (rp == 64 && a.XA != nullptr) {
     // the panel as a pass of its own into XA (its partials in Y, which the kernel then
     // overwrites), then the kernel without the panel

@@ -158,6 +158,74 @@ SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t K, int32_t R, bool bwd)
   return l;
 }
 
+// fmt: 0 bf16 weight; 64 int4 codes + fp16 scales (Ws); 32 MXFP4 codes + E8M0 bytes (Ws)
+lora_status swiglu_fwd_impl(int fmt, int64_t M, int64_t N, int64_t K, int32_t R, float scale, const void* X,
+                            const void* Wgu, const void* Ws, const void* Ag, const void* Au, const void* Bg, const void* Bu,
+                            void* H, void* GU, float* XA, void* ws, size_t ws_bytes, void* stream) {
+  lora_status st = check_swiglu(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(Wgu, Ag, Au, Bg, Bu);
+  if (st != LORA_OK) return st;
+  if (M == 0) return LORA_OK;  // empty batch: X, H, GU and XA may be NULL
+  st = check_ptrs(X, H, GU);
+  if (st != LORA_OK) return st;
+  if (XA != nullptr && !aligned16(XA)) return LORA_ERR_ALIGN;
+  const SwigluLayout lay = swiglu_layout(M, N, K, R, false);
+  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  char* base = static_cast<char*>(ws);
+  uint16_t* As = reinterpret_cast<uint16_t*>(base + lay.as);
+  uint16_t* Bs = reinterpret_cast<uint16_t*>(base + lay.bs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_swiglu_stack(static_cast<const uint16_t*>(Ag), static_cast<const uint16_t*>(Au),
+                                     static_cast<const uint16_t*>(Bg), static_cast<const uint16_t*>(Bu), As, Bs,
+                                     N, K, R, s);
+  if (e != hipSuccess) return from_hip(e);
+  // [G | U] = X [Wg; Wu]^T + scale (X [Ag; Au]^T) [Bg 0; 0 Bu]^T: one GEMM over both
+  // projections, whose epilogue also forms H = silu(G) U from the fp32 accumulators
+  FwdArgs a{X, Wgu, Ws, As, Bs, GU, XA, M, 2 * N, K, 2 * R, scale, H};
+  a.fp4 = fmt == 32;
+  return from_hip(launch_fwd_mfma(a, fmt != 0, s));
+}
+
+lora_status swiglu_bwd_impl(int fmt, int64_t M, int64_t N, int64_t K, int32_t R, float scale, const void* dH,
+                            const void* X, const void* Wgu, const void* Ws, const void* Ag, const void* Au, const void* Bg,
+                            const void* Bu, const void* GU, const float* XA, void* dX, float* dAg, float* dAu,
+                            float* dBg, float* dBu, void* ws, size_t ws_bytes, void* stream) {
+  lora_status st = check_swiglu(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(Wgu, Ag, Au, Bg, Bu, dAg, dAu, dBg, dBu);
+  if (st != LORA_OK) return st;
+  if (M > 0 && (st = check_ptrs(dH, X, GU, XA, dX)) != LORA_OK) return st;
+  const SwigluLayout lay = swiglu_layout(M, N, K, R, true);
+  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  char* base = static_cast<char*>(ws);
+  uint16_t* As = reinterpret_cast<uint16_t*>(base + lay.as);
+  uint16_t* Bs = reinterpret_cast<uint16_t*>(base + lay.bs);
+  uint16_t* dGU = reinterpret_cast<uint16_t*>(base + lay.dgu);
+  float* dAs = reinterpret_cast<float*>(base + lay.das);
+  float* dBs = reinterpret_cast<float*>(base + lay.dbs);
+  void* inner = base + lay.inner;
+  const size_t inner_bytes = ws_bytes - lay.inner;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_swiglu_stack(static_cast<const uint16_t*>(Ag), static_cast<const uint16_t*>(Au),
+                                     static_cast<const uint16_t*>(Bg), static_cast<const uint16_t*>(Bu), As, Bs,
+                                     N, K, R, s);
+  if (e != hipSuccess) return from_hip(e);
+  e = launch_swiglu_bwd(static_cast<const uint16_t*>(dH), static_cast<const uint16_t*>(GU), dGU, M, N, s);
+  if (e != hipSuccess) return from_hip(e);
+  // the LoRA backward of the stacked GEMM with [dG | dU] as its upstream gradient
+  st = bwd_dx_common(fmt != 0, LORA_BF16, M, 2 * N, K, 2 * R, scale, dGU, Wgu, Ws, As, Bs, dX, inner,
+                     inner_bytes, stream, fmt == 32);
+  if (st != LORA_OK) return st;
+  st = bwd_dadb_common(LORA_BF16, M, 2 * N, K, 2 * R, scale, dGU, X, XA, dAs, dBs, inner, inner_bytes, stream);
+  if (st != LORA_OK) return st;
+  return from_hip(launch_swiglu_unstack(dAs, dBs, dAg, dAu, dBg, dBu, N, K, R, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -344,30 +412,15 @@ size_t lora_swiglu_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t 
 lora_status lora_swiglu_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, const void* X,
                             const void* Wgu, const void* Ag, const void* Au, const void* Bg, const void* Bu,
                             void* H, void* GU, float* XA, void* ws, size_t ws_bytes, void* stream) {
-  lora_status st = check_swiglu(M, N, K, R);
-  if (st != LORA_OK) return st;
-  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
-  st = check_ptrs(Wgu, Ag, Au, Bg, Bu);
-  if (st != LORA_OK) return st;
-  if (M == 0) return LORA_OK;  // empty batch: X, H, GU and XA may be NULL
-  st = check_ptrs(X, H, GU);
-  if (st != LORA_OK) return st;
-  if (XA != nullptr && !aligned16(XA)) return LORA_ERR_ALIGN;
-  const SwigluLayout lay = swiglu_layout(M, N, K, R, false);
-  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
-  if (!aligned16(ws)) return LORA_ERR_ALIGN;
-  char* base = static_cast<char*>(ws);
-  uint16_t* As = reinterpret_cast<uint16_t*>(base + lay.as);
-  uint16_t* Bs = reinterpret_cast<uint16_t*>(base + lay.bs);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_swiglu_stack(static_cast<const uint16_t*>(Ag), static_cast<const uint16_t*>(Au),
-                                     static_cast<const uint16_t*>(Bg), static_cast<const uint16_t*>(Bu), As, Bs,
-                                     N, K, R, s);
-  if (e != hipSuccess) return from_hip(e);
-  // [G | U] = X [Wg; Wu]^T + scale (X [Ag; Au]^T) [Bg 0; 0 Bu]^T: one GEMM over both
-  // projections, whose epilogue also forms H = silu(G) U from the fp32 accumulators
-  const FwdArgs a{X, Wgu, nullptr, As, Bs, GU, XA, M, 2 * N, K, 2 * R, scale, H};
-  return from_hip(launch_fwd_mfma(a, false, s));
+  return swiglu_fwd_impl(0, M, N, K, R, scale, X, Wgu, nullptr, Ag, Au, Bg, Bu, H, GU, XA, ws, ws_bytes, stream);
+}
+
+lora_status qlora_swiglu_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group, const void* X,
+                             const uint8_t* Wguq, const void* Wgus, const void* Ag, const void* Au, const void* Bg,
+                             const void* Bu, void* H, void* GU, float* XA, void* ws, size_t ws_bytes, void* stream) {
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
+  if (Wgus == nullptr) return LORA_ERR_NULL;
+  return swiglu_fwd_impl(group, M, N, K, R, scale, X, Wguq, Wgus, Ag, Au, Bg, Bu, H, GU, XA, ws, ws_bytes, stream);
 }
 
 size_t lora_swiglu_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) {
@@ -379,37 +432,18 @@ lora_status lora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float sc
                             const void* X, const void* Wgu, const void* Ag, const void* Au, const void* Bg,
                             const void* Bu, const void* GU, const float* XA, void* dX, float* dAg, float* dAu,
                             float* dBg, float* dBu, void* ws, size_t ws_bytes, void* stream) {
-  lora_status st = check_swiglu(M, N, K, R);
-  if (st != LORA_OK) return st;
-  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
-  st = check_ptrs(Wgu, Ag, Au, Bg, Bu, dAg, dAu, dBg, dBu);
-  if (st != LORA_OK) return st;
-  if (M > 0 && (st = check_ptrs(dH, X, GU, XA, dX)) != LORA_OK) return st;
-  const SwigluLayout lay = swiglu_layout(M, N, K, R, true);
-  if (ws == nullptr || ws_bytes < lay.total) return LORA_ERR_WORKSPACE;
-  if (!aligned16(ws)) return LORA_ERR_ALIGN;
-  char* base = static_cast<char*>(ws);
-  uint16_t* As = reinterpret_cast<uint16_t*>(base + lay.as);
-  uint16_t* Bs = reinterpret_cast<uint16_t*>(base + lay.bs);
-  uint16_t* dGU = reinterpret_cast<uint16_t*>(base + lay.dgu);
-  float* dAs = reinterpret_cast<float*>(base + lay.das);
-  float* dBs = reinterpret_cast<float*>(base + lay.dbs);
-  void* inner = base + lay.inner;
-  const size_t inner_bytes = ws_bytes - lay.inner;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_swiglu_stack(static_cast<const uint16_t*>(Ag), static_cast<const uint16_t*>(Au),
-                                     static_cast<const uint16_t*>(Bg), static_cast<const uint16_t*>(Bu), As, Bs,
-                                     N, K, R, s);
-  if (e != hipSuccess) return from_hip(e);
-  e = launch_swiglu_bwd(static_cast<const uint16_t*>(dH), static_cast<const uint16_t*>(GU), dGU, M, N, s);
-  if (e != hipSuccess) return from_hip(e);
-  // the LoRA backward of the stacked GEMM with [dG | dU] as its upstream gradient
-  st = bwd_dx_common(false, LORA_BF16, M, 2 * N, K, 2 * R, scale, dGU, Wgu, nullptr, As, Bs, dX, inner,
-                     inner_bytes, stream);
-  if (st != LORA_OK) return st;
-  st = bwd_dadb_common(LORA_BF16, M, 2 * N, K, 2 * R, scale, dGU, X, XA, dAs, dBs, inner, inner_bytes, stream);
-  if (st != LORA_OK) return st;
-  return from_hip(launch_swiglu_unstack(dAs, dBs, dAg, dAu, dBg, dBu, N, K, R, s));
+  return swiglu_bwd_impl(0, M, N, K, R, scale, dH, X, Wgu, nullptr, Ag, Au, Bg, Bu, GU, XA, dX, dAg, dAu, dBg, dBu,
+                         ws, ws_bytes, stream);
+}
+
+lora_status qlora_swiglu_bwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group, const void* dH,
+                             const void* X, const uint8_t* Wguq, const void* Wgus, const void* Ag, const void* Au,
+                             const void* Bg, const void* Bu, const void* GU, const float* XA, void* dX, float* dAg,
+                             float* dAu, float* dBg, float* dBu, void* ws, size_t ws_bytes, void* stream) {
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
+  if (Wgus == nullptr) return LORA_ERR_NULL;
+  return swiglu_bwd_impl(group, M, N, K, R, scale, dH, X, Wguq, Wgus, Ag, Au, Bg, Bu, GU, XA, dX, dAg, dAu, dBg, dBu,
+                         ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -53,6 +53,8 @@ SIGNATURES = {
     "lora_ce_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "lora_ce": (_i32, [_i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "lora_rope": (_i32, [_i64, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
+    "qlora_swiglu_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 11 + [_sz, _p]),
+    "qlora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 16 + [_sz, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -601,3 +603,45 @@ class RoPEFunction(torch.autograd.Function):
         dQ, dK = dQ.contiguous().clone(), dK.contiguous().clone()
         lora_rope(dQ, dK, positions, ctx.base, rot=ctx.rot, inverse=True)
         return dQ, dK, None, None, None
+
+
+def qlora_swiglu_fwd(X, Wguq, Wgus, Ag, Au, Bg, Bu, scale: float, *, H=None, GU=None, XA=None,
+                     save_xa: bool = True, ws=None, stream=None):
+    """The SwiGLU pair over the stacked 4-bit weight (Wguq, Wgus from qlora_quantize of [Wg; Wu]; the
+    format follows Wgus: fp16 scales int4, uint8 exponents MXFP4).  Returns (H, GU, XA)."""
+    lib = load()
+    for t, n in ((X, "X"), (Ag, "Ag"), (Au, "Au"), (Bg, "Bg"), (Bu, "Bu")):
+        _want(t, n, torch.bfloat16)
+    M, K = X.shape
+    N, R = Wguq.shape[0] // 2, Ag.shape[0]
+    dev = X.device
+    H = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if H is None else H
+    GU = torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev) if GU is None else GU
+    if XA is None and save_xa:
+        XA = torch.empty((M, 2 * R), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(lora_swiglu_fwd_workspace_bytes(M, N, K, R), 1), dtype=torch.uint8, device=dev)
+    st = lib.qlora_swiglu_fwd(M, N, K, R, float(scale), _group_of(Wgus), _ptr(X), _ptr(Wguq), _ptr(Wgus), _ptr(Ag),
+                              _ptr(Au), _ptr(Bg), _ptr(Bu), _ptr(H), _ptr(GU), _ptr(XA), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream))
+    _check("qlora_swiglu_fwd", st)
+    return H, GU, XA
+
+
+def qlora_swiglu_bwd(dH, X, Wguq, Wgus, Ag, Au, Bg, Bu, GU, XA, scale: float, *, ws=None, stream=None):
+    """Returns (dX, dAg, dAu, dBg, dBu) for the 4-bit stacked weight."""
+    lib = load()
+    M, K = X.shape
+    N, R = Wguq.shape[0] // 2, Ag.shape[0]
+    dev = X.device
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dAg, dAu = (torch.empty((R, K), dtype=torch.float32, device=dev) for _ in range(2))
+    dBg, dBu = (torch.empty((N, R), dtype=torch.float32, device=dev) for _ in range(2))
+    if ws is None:
+        ws = torch.empty(max(lora_swiglu_bwd_workspace_bytes(M, N, K, R), 1), dtype=torch.uint8, device=dev)
+    st = lib.qlora_swiglu_bwd(M, N, K, R, float(scale), _group_of(Wgus), _ptr(dH), _ptr(X), _ptr(Wguq), _ptr(Wgus),
+                              _ptr(Ag), _ptr(Au), _ptr(Bg), _ptr(Bu), _ptr(GU), _ptr(XA), _ptr(dX), _ptr(dAg),
+                              _ptr(dAu), _ptr(dBg), _ptr(dBu), _ptr(ws), ws.numel() * ws.element_size(),
+                              _stream(stream))
+    _check("qlora_swiglu_bwd", st)
+    return dX, dAg, dAu, dBg, dBu

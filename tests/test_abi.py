@@ -371,3 +371,26 @@ def test_lora_rope_validation(lib, kw, code):
 
 def test_lora_rope_empty_batch_needs_no_pointers(lib):
     assert lib.lora_rope(0, 4, 2, 128, 128, 10000.0, 0, None, None, None, None) == 0
+
+
+def test_qlora_swiglu_validation(lib):
+    # the 4-bit SwiGLU pair: the group selects the format; every call here fails before a launch
+    args = lambda group, ws_bytes: (64, 256, 256, 16, 2.0, group, P, P, P, P, P, P, P, P, P, P, P, ws_bytes, None)
+    need = lib.lora_swiglu_fwd_workspace_bytes(64, 256, 256, 16)
+    assert lib.qlora_swiglu_fwd(*args(16, need)) == 7
+    assert lib.qlora_swiglu_fwd(*args(64, 16)) == 6
+    assert lib.qlora_swiglu_fwd(*args(32, 16)) == 6
+    b = (64, 256, 256, 16, 2.0, 64) + (P,) * 16 + (16, None)  # 16 pointers, then the workspace size
+    assert lib.qlora_swiglu_bwd(*b) == 6
+    assert lib.qlora_swiglu_bwd(*((64, 256, 256, 16, 2.0, 48) + (P,) * 16 + (1 << 30, None))) == 7
+
+
+def test_binding_argument_counts_match_the_header():
+    # every binding signature has as many arguments as the header declares (a wrong count would
+    # shift every later argument of the call)
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, (_, args) in lora.SIGNATURES.items():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), f"{name}: header {len(params)} parameters, binding {len(args)}"

@@ -117,3 +117,43 @@ def test_swiglu_empty_batch(gpu_lib):
     assert H.shape == (0, 128) and dX.shape == (0, 256)
     for t in (dAg, dAu, dBg, dBu):
         assert torch.count_nonzero(t) == 0
+
+
+def _quantized_stack(lib, inp, group):
+    """[Wg; Wu] (the inputs' bf16 values, exact in fp32) quantised on the GPU, the codes checked bit
+    for bit against the oracle's; returns the device codes and scales and the exact W~g, W~u."""
+    w = np.vstack([oracle.bf16_bits_to_f64(inp.Wg), oracle.bf16_bits_to_f64(inp.Wu)]).astype(np.float32)
+    Wq, Ws = lib.qlora_quantize(torch.from_numpy(w).cuda(), group=group)
+    torch.cuda.synchronize()
+    if group == 64:
+        q, s = oracle.quantize_int4(w)
+        packed = oracle.pack_int4(q)
+        np.testing.assert_array_equal(Ws.view(torch.int16).cpu().numpy().view(np.uint16), s.view(np.uint16))
+        wt = oracle.dequant_int4(packed, s)
+    else:
+        codes, E = oracle.quantize_mxfp4(w)
+        packed = oracle.pack_fp4(codes)
+        np.testing.assert_array_equal(Ws.cpu().numpy(), E)
+        wt = oracle.dequant_mxfp4(packed, E)
+    np.testing.assert_array_equal(Wq.cpu().numpy(), packed)
+    return Wq, Ws, wt[:inp.N], wt[inp.N:]
+
+
+@pytest.mark.parametrize("group", [64, 32])
+@pytest.mark.parametrize("M,N,K,R", [(300, 256, 320, 16), (130, 320, 256, 32), (65, 128, 512, 8)])
+def test_qlora_swiglu_4bit_weights(gpu_lib, group, M, N, K, R):
+    print(f"case qlora swiglu group={group} M={M} N={N} K={K} R={R}", flush=True)
+    inp = make_swiglu_inputs(M, N, K, R, seed=2000 + M + group)
+    Wq, Ws, wg, wu = _quantized_stack(gpu_lib, inp, group)
+    X, _, Ag, Au, Bg, Bu = _dev(inp)
+    H, GU, XA = gpu_lib.qlora_swiglu_fwd(X, Wq, Ws, Ag, Au, Bg, Bu, inp.scale)
+    grads = gpu_lib.qlora_swiglu_bwd(bits_to_dev(inp.dH), X, Wq, Ws, Ag, Au, Bg, Bu, GU, XA, inp.scale)
+    torch.cuda.synchronize()
+    x, ag, au, bg, bu, dh = _vals(inp, "X", "Ag", "Au", "Bg", "Bu", "dH")
+    Hr, Gr, Ur, _, _ = oracle.swiglu_lora_forward(x, wg, wu, ag, au, bg, bu, inp.scale)
+    assert_close("H", host(H), Hr)
+    assert_close("G", host(GU[:, :N]), Gr)
+    assert_close("U", host(GU[:, N:]), Ur)
+    ref = oracle.swiglu_lora_backward(dh, x, wg, wu, ag, au, bg, bu, inp.scale)
+    for name, got, r in zip(("dX", "dAg", "dAu", "dBg", "dBu"), grads, ref):
+        assert_close(name, host(got), r)
