@@ -44,7 +44,7 @@ Sources are the web pages on Unsloth.  They are cited by page title and section:
   int4 in -7..7, two per byte, groups of 64 along K, fp16 scale = absmax/7) is
   this repository's workload definition; the pages fix none of its details.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   row-major tokens, W is (N x K) = (out x in), A is (R x K), B is (N x R);
   scale = alpha / r passed as a number; no dropout; dW is not computed;
   XA = X A^T is the unscaled fp32 panel saved for backward; gradients overwrite;
