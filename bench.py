@@ -423,7 +423,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's data-parallel sharding (token slices per GPU, "
-              "one all-reduce of dA and dB per layer) is not part of this build. Run with --gpus 1.",
+              "one all-reduce of dA and dB per layer) is not implemented here. Run with --gpus 1.",
               file=sys.stderr)
         return 2
 
