@@ -41,11 +41,13 @@ def test_ce_shapes(gpu_lib, M, K, V, chunk, std):
     assert dX2 is None and torch.equal(loss, loss2)
 
 
-def test_ce_llama3_head_sampled(gpu_lib):
-    # the page's vocabulary (128000) over 4096 hidden features; 2048 tokens in chunks of 1024
-    M, K, V = 2048, 4096, 128000
+@pytest.mark.parametrize("V,K", [(128000, 4096), (152064, 5120)])
+def test_ce_lm_heads_sampled(gpu_lib, V, K):
+    # the pages' vocabularies: 128000 (the chunked cross-entropy section) over 4096 hidden features,
+    # and 152064 (the decode page's model table) over 5120; 2048 tokens in chunks of 1024
+    M = 2048
     print(f"case ce M={M} K={K} V={V} (sampled rows)", flush=True)
-    inp = make_ce_inputs(M, K, V, seed=5, logit_std=3.0)
+    inp = make_ce_inputs(M, K, V, seed=5 + V % 7, logit_std=3.0)
     X, W, lab = _dev(inp)
     loss_sum, loss, dX = gpu_lib.lora_ce(X, W, lab, chunk=1024)
     torch.cuda.synchronize()
