@@ -44,7 +44,8 @@ def test_ce_shapes(gpu_lib, M, K, V, chunk, std):
 @pytest.mark.parametrize("V,K", [(128000, 4096), (152064, 5120)])
 def test_ce_lm_heads_sampled(gpu_lib, V, K):
     # the pages' vocabularies: 128000 (the chunked cross-entropy section) over 4096 hidden features,
-    # and 152064 (the decode page's model table) over 5120; 2048 tokens in chunks of 1024
+    # and 152064 (the architecture table of the Qwen 27B inference post, section three) over 5120;
+    # 2048 tokens in chunks of 1024
     M = 2048
     print(f"case ce M={M} K={K} V={V} (sampled rows)", flush=True)
     inp = make_ce_inputs(M, K, V, seed=5 + V % 7, logit_std=3.0)
