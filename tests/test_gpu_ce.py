@@ -1,7 +1,7 @@
 """GPU parity of the chunked cross-entropy over an LM head against the float64 oracle (through the
 C ABI): per-token losses, their sum and dX at shapes with ragged chunks and a partial last column
-tile, peaky logits, the Llama-3-sized head on sampled rows, an out-of-range label, determinism,
-the empty batch, and the autograd wrapper."""
+tile, peaky logits, the pages' two LM heads on sampled rows (one at the default chunk, whose fp32
+logits pass 4 GiB), an out-of-range label, determinism, the empty batch, and the autograd wrapper."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +53,25 @@ def test_ce_lm_heads_sampled(gpu_lib, V, K):
     loss_sum, loss, dX = gpu_lib.lora_ce(X, W, lab, chunk=1024)
     torch.cuda.synchronize()
     rows = np.array(sorted({0, 1, 255, 256, 1023, 1024, 1025, 2047} | set(np.random.default_rng(5).integers(0, M, 12))))
+    x, w, labels = _vals(inp)
+    lr, _ = oracle.cross_entropy_rows(x[rows], w, labels[rows])
+    dXr, _ = oracle.cross_entropy_grad(x[rows], w, labels[rows], 1.0 / M)
+    idx = torch.from_numpy(rows).cuda()
+    assert_close("loss", loss[idx].cpu().numpy().astype(np.float64), lr)
+    assert_close("dX", host(dX[idx]), dXr)
+    assert torch.isfinite(loss).all() and torch.isfinite(dX.float()).all()
+
+
+def test_ce_default_chunk_logits_past_4gib(gpu_lib):
+    # 8200 tokens at the 152064-word head over 5120 features: one default 8192-token chunk, whose
+    # fp32 logits (4.98 GB) pass 2^32 bytes inside row 7061, then an 8-token tail chunk
+    M, K, V = 8200, 5120, 152064
+    print(f"case ce M={M} K={K} V={V} default chunk (sampled rows)", flush=True)
+    inp = make_ce_inputs(M, K, V, seed=17, logit_std=3.0)
+    X, W, lab = _dev(inp)
+    loss_sum, loss, dX = gpu_lib.lora_ce(X, W, lab)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 7060, 7061, 7062, 7063, 8191, 8192, 8199} | set(np.random.default_rng(6).integers(0, M, 8))))
     x, w, labels = _vals(inp)
     lr, _ = oracle.cross_entropy_rows(x[rows], w, labels[rows])
     dXr, _ = oracle.cross_entropy_grad(x[rows], w, labels[rows], 1.0 / M)
