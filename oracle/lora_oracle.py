@@ -13,8 +13,9 @@ Sources are the web pages on Unsloth.  They are cited by page title and section:
   LoRA equation ``y = W x + (alpha/r) B A x`` with ``A`` (r x d), ``B`` (d x r);
   the same equation appears in tutorial ch. 1 "项目背景与定位", §1.2, as
   ``Delta W = (alpha/r) B A``.
-* Term order: §5.3's listing of the unfused PEFT forward (base layer, lora_A,
-  lora_B, multiply by alpha/r, add).  The oracle follows that order.
+* Row form of the equation: a batch of row vectors X (M x K) gives
+  ``Y = X W^T + (alpha/r) (X A^T) B^T``; the rank-r product X A^T is formed first and
+  ``B A`` is never materialised (it is only the brute-force check in the tests).
 * Backward: §5.3's paragraph on the fused backward (gradients for X, A, B; W only
   "if trained", and here W is frozen) and the hand-derived-backward section of
   the wisestudy.cn Unsloth essay.  The gradients below are derived by hand from
@@ -185,16 +186,22 @@ def _f64(*xs):
 
 
 def lora_forward(X, W, A, B, scale):
-    """Y = X W^T + scale * (X A^T) B^T, in the order of §5.3's unfused PEFT listing.
+    """The §5.3 LoRA equation y = W x + (alpha/r) B (A x), applied to each row x of X.
 
-    X: M x K, W: N x K, A: R x K, B: N x R.  Returns (Y: M x N, XA: M x R), float64.
+    X: M x K, W: N x K, A: R x K, B: N x R, scale = alpha / r.
+    Returns (Y, P) in float64: Y (M x N) the layer output and P = X A^T (M x R), the
+    unscaled rank-R projection of every token (the state the backward reuses).
     """
     X, W, A, B = _f64(X, W, A, B)
-    main = X @ W.T                 # base layer
-    xa = X @ A.T                   # lora_A
-    lora = xa @ B.T                # lora_B
-    lora = lora * float(scale)     # multiply by alpha / r
-    return main + lora, xa
+    P = lora_projection(X, A)
+    Y = X @ W.T + float(scale) * (P @ B.T)
+    return Y, P
+
+
+def lora_projection(X, A):
+    """P = X A^T (M x R): the rank-R projection A x of every token row x, float64."""
+    X, A = _f64(X, A)
+    return X @ A.T
 
 
 def lora_backward(dY, X, W, A, B, scale, XA=None):
@@ -215,13 +222,24 @@ def lora_backward(dY, X, W, A, B, scale, XA=None):
     return dX, dA, dB
 
 
+def lora_backward_adapters(dY, X, A, B, scale, XA=None):
+    """The adapter gradients of ``lora_backward`` alone (no dX, so W is not needed):
+
+    dA = scale * (dY B)^T X   (R x K),   dB = scale * dY^T (X A^T)   (N x R).
+
+    Returns (dA, dB), float64.  XA, when given, is the saved X A^T.
+    """
+    dY, X, A, B = _f64(dY, X, A, B)
+    s = float(scale)
+    xa = X @ A.T if XA is None else np.asarray(XA, dtype=np.float64)
+    G = dY @ B
+    return s * (G.T @ X), s * (dY.T @ xa)
+
+
 def lora_forward_rows(X, W, A, B, scale, rows):
     """Rows ``rows`` of (Y, XA), computed one row set at a time (for full-size sampling)."""
     rows = np.asarray(rows)
-    Xr, W, A, B = _f64(np.asarray(X)[rows], W, A, B)
-    main = Xr @ W.T
-    xa = Xr @ A.T
-    return main + (xa @ B.T) * float(scale), xa
+    return lora_forward(np.asarray(X)[rows], W, A, B, scale)
 
 
 def lora_backward_dx_rows(dY, W, A, B, scale, rows):
@@ -284,6 +302,20 @@ def swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, scale):
     dXg, dAg, dBg = lora_backward(dG, X, Wg, Ag, Bg, scale)
     dXu, dAu, dBu = lora_backward(dU, X, Wu, Au, Bu, scale)
     return dXg + dXu, dAg, dAu, dBg, dBu
+
+
+def swiglu_lora_backward_adapters(dH, X, Wg, Wu, Ag, Au, Bg, Bu, scale):
+    """The four adapter gradients of ``swiglu_lora_backward`` without dX: the same dG and dU
+    from the forward's G and U, then ``lora_backward_adapters`` of each projection.
+    Returns (dAg, dAu, dBg, dBu), float64."""
+    dH = np.asarray(dH, dtype=np.float64)
+    G, xag = lora_forward(X, Wg, Ag, Bg, scale)
+    U, xau = lora_forward(X, Wu, Au, Bu, scale)
+    dU = dH * silu(G)
+    dG = dH * U * silu_grad(G)
+    dAg, dBg = lora_backward_adapters(dG, X, Ag, Bg, scale, XA=xag)
+    dAu, dBu = lora_backward_adapters(dU, X, Au, Bu, scale, XA=xau)
+    return dAg, dAu, dBg, dBu
 
 
 def swiglu_lora_rows(X, Wg, Wu, Ag, Au, Bg, Bu, scale, rows):

@@ -248,6 +248,55 @@ def test_backward_dx_rows_matches_full():
                                rtol=1e-13, atol=1e-13)
 
 
+def test_backward_adapters_hand_worked_example():
+    # the adapter gradients alone reproduce the hand-worked fixture's dA and dB exactly, with and
+    # without the saved panel
+    f = _fixture_lora()
+    dA, dB = oracle.lora_backward_adapters(f["dY"], f["X"], f["A"], f["B"], f["s"])
+    np.testing.assert_array_equal(dA, f["dA"])
+    np.testing.assert_array_equal(dB, f["dB"])
+    dA2, dB2 = oracle.lora_backward_adapters(f["dY"], f["X"], f["A"], f["B"], f["s"], XA=f["XA"])
+    np.testing.assert_array_equal(dA2, f["dA"])
+    np.testing.assert_array_equal(dB2, f["dB"])
+
+
+@pytest.mark.parametrize("M,K,N,R", [(3, 5, 4, 2), (6, 4, 7, 3)])
+def test_backward_adapters_central_differences(M, K, N, R):
+    # L = <dY, Y> is linear in A and in B separately: unit-step central differences are exact
+    rng = np.random.default_rng(40 + M)
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((N, K))
+    A, B = rng.standard_normal((R, K)), rng.standard_normal((N, R))
+    dY, s = rng.standard_normal((M, N)), 1.25
+    dA, dB = oracle.lora_backward_adapters(dY, X, A, B, s)
+    for name, got in (("A", dA), ("B", dB)):
+        want = np.zeros(got.shape)
+        for idx in np.ndindex(*got.shape):
+            p, m = {"A": A.copy(), "B": B.copy()}, {"A": A.copy(), "B": B.copy()}
+            p[name][idx] += 1.0
+            m[name][idx] -= 1.0
+            want[idx] = (_loss(dY, X, W, p["A"], p["B"], s) - _loss(dY, X, W, m["A"], m["B"], s)) / 2.0
+        np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-9)
+
+
+def test_backward_adapters_invariants_and_full_backward():
+    # <dA, A> = <dB, B> = s <dY, (X A^T) B^T>, and the same values as the full backward
+    rng = np.random.default_rng(41)
+    M, K, N, R, s = 64, 48, 40, 8, 2.0
+    X, W = rng.standard_normal((M, K)), rng.standard_normal((N, K)) / np.sqrt(K)
+    A, B = rng.uniform(-0.1, 0.1, (R, K)), rng.standard_normal((N, R)) * 0.14
+    dY = rng.standard_normal((M, N))
+    dA, dB = oracle.lora_backward_adapters(dY, X, A, B, s)
+    Lr = s * np.sum(dY * np.matmul(np.matmul(X, A.T), B.T))
+    assert abs(np.sum(dA * A) - Lr) <= 1e-10 * max(1.0, abs(Lr))
+    assert abs(np.sum(dB * B) - Lr) <= 1e-10 * max(1.0, abs(Lr))
+    _, dA2, dB2 = oracle.lora_backward(dY, X, W, A, B, s)
+    np.testing.assert_array_equal(dA, dA2)
+    np.testing.assert_array_equal(dB, dB2)
+    # a planted mistake (dB from the scaled panel s X A^T) breaks the invariant
+    bad = s * (dY.T @ (s * (X @ A.T)))
+    assert abs(np.sum(bad * B) - Lr) > 1e-3 * abs(Lr)
+
+
 # ---------------------------------------------------------------------------
 # int4 format
 # ---------------------------------------------------------------------------
@@ -432,6 +481,10 @@ def test_swiglu_against_torch_autograd_float64():
     np.testing.assert_allclose(Go, G.detach().numpy(), rtol=1e-12, atol=1e-12)
     got = oracle.swiglu_lora_backward(dH, X, Wg, Wu, Ag, Au, Bg, Bu, s)
     for g, ref in zip(got, (tX, tAg, tAu, tBg, tBu)):
+        np.testing.assert_allclose(g, ref.grad.numpy(), rtol=1e-11, atol=1e-12)
+    # the adapter-only form against the same autograd witness
+    ad = oracle.swiglu_lora_backward_adapters(dH, X, Wg, Wu, Ag, Au, Bg, Bu, s)
+    for g, ref in zip(ad, (tAg, tAu, tBg, tBu)):
         np.testing.assert_allclose(g, ref.grad.numpy(), rtol=1e-11, atol=1e-12)
 
 
@@ -803,19 +856,27 @@ def test_rope_properties():
                                rtol=1e-7)
 
 
-def test_rope_listing_form_agrees():
-    # the page's listing: x_rot * cos + rotate_half(x_rot) * sin, rotate_half(u) = [-u2, u1], with
-    # cos, sin repeated over both halves
+def test_rope_rotation_matrix_form_agrees():
+    # §5.5's formula: each coordinate pair multiplied by the 2 x 2 rotation [[cos, -sin], [sin, cos]].
+    # Written here as one explicit D x D matrix per token, acting on the half-split pairs
+    # (j, j + rot/2) and the identity on the pass-through coordinates, applied by a matrix product
     rng = np.random.default_rng(96)
-    M, H, D, rot, base = 5, 2, 8, 8, 10000.0
+    M, H, D, rot, base = 5, 2, 10, 8, 10000.0
     pos = rng.integers(0, 100, M)
     x = rng.standard_normal((M, H, D))
     th = oracle.rope_angles(pos, rot, base)
-    c = np.concatenate([np.cos(th), np.cos(th)], axis=1)[:, None, :]
-    s = np.concatenate([np.sin(th), np.sin(th)], axis=1)[:, None, :]
-    rh = np.concatenate([-x[..., rot // 2:], x[..., :rot // 2]], axis=-1)
-    np.testing.assert_allclose(oracle.rope_apply(x, pos, rot, base), x * c + rh * s, rtol=1e-13, atol=1e-14)
-    # a planted mistake (interleaved pairs) disagrees with it
+    h = rot // 2
+    want = np.empty_like(x)
+    for t in range(M):
+        Rm = np.eye(D)
+        for j in range(h):
+            c, s_ = np.cos(th[t, j]), np.sin(th[t, j])
+            Rm[j, j], Rm[j, j + h] = c, -s_
+            Rm[j + h, j], Rm[j + h, j + h] = s_, c
+        want[t] = x[t] @ Rm.T
+    np.testing.assert_allclose(oracle.rope_apply(x, pos, rot, base), want, rtol=1e-13, atol=1e-14)
+    # a planted mistake (pairs (2i, 2i+1) instead of the half split) disagrees with it
     wrong = x.copy()
-    wrong[..., 0::2] = x[..., 0::2] * np.cos(th)[:, None, :] - x[..., 1::2] * np.sin(th)[:, None, :]
-    assert not np.allclose(wrong[..., 0::2], (x * c + rh * s)[..., 0::2])
+    wrong[..., 0:rot:2] = x[..., 0:rot:2] * np.cos(th)[:, None, :] - x[..., 1:rot:2] * np.sin(th)[:, None, :]
+    wrong[..., 1:rot:2] = x[..., 1:rot:2] * np.cos(th)[:, None, :] + x[..., 0:rot:2] * np.sin(th)[:, None, :]
+    assert not np.allclose(wrong, want)
