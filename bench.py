@@ -97,24 +97,23 @@ def event_time_ms(fn, reps, stream):
 
 
 def cpu_baseline(inp, min_seconds):
-    """The float64 oracle, as it stands, on the whole workload, repeated for >= min_seconds."""
+    """The float64 oracle, as it stands, on the whole workload, repeated for >= min_seconds, with
+    the BLAS thread pool pinned to the cores this process may run on."""
     import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    cores = len(os.sched_getaffinity(0))
     x, dy, w, a, b = (oracle.bf16_bits_to_f64(getattr(inp, n)) for n in ("X", "dY", "W", "A", "B"))
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        Y, XA = oracle.lora_forward(x, w, a, b, inp.scale)
-        oracle.lora_backward(dy, x, w, a, b, inp.scale, XA=XA)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or reps >= 200:
-            break
+    with threadpool_limits(limits=cores):
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            Y, XA = oracle.lora_forward(x, w, a, b, inp.scale)
+            oracle.lora_backward(dy, x, w, a, b, inp.scale, XA=XA)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds or reps >= 200:
+                break
     fl = lora_flops(inp.M, inp.N, inp.K, inp.R) * reps
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 fwd+bwd of the whole workload ({inp.M} tokens), {reps} repetitions "
@@ -454,44 +453,57 @@ def main(argv=None):
     def fwd():
         lora.lora_fwd(X, W, A, B, inp.scale, Y=Y, XA=XA, stream=stream)
 
-    def bwd():
-        lora.lora_bwd(dY, X, W, A, B, XA, inp.scale, dX=dX, dA=dA, dB=dB, ws=ws, stream=stream)
-
-    def step():
-        fwd()
-        bwd()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
-    fl = lora_flops(M, N, K, R)
-    value = fl / ms / 1e9
-
-    # dominant kernel: the fused input gradient (the one kernel of lora_bwd_dx), timed live
+    # lora_bwd as its two halves (bit for bit the same calls): the input gradient, whose kernel is
+    # the dominant one and is timed on its own inside the timed region, then the adapter gradients
     def bwd_dx():
         lora.lora_bwd_dx(dY, W, A, B, inp.scale, ws=ws, dX=dX, stream=stream)
 
+    def bwd_dadb():
+        lora.lora_bwd_dadb(dY, X, XA, inp.scale, R, ws=ws, dA=dA, dB=dB, stream=stream)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd_dx()
+        bwd_dadb()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    t_step = [ev() for _ in range(args.steps + 1)]   # step boundaries
+    t_dx = [(ev(), ev()) for _ in range(args.steps)]  # around each input-gradient kernel
+    t0 = time.perf_counter()
+    t_step[0].record(stream)
+    for i in range(args.steps):
+        fwd()
+        t_dx[i][0].record(stream)
+        bwd_dx()
+        t_dx[i][1].record(stream)
+        bwd_dadb()
+        t_step[i + 1].record(stream)
+    clk = lora.lora_probe_sclk(2000, stream=stream)  # right after the last step: 20 us spin
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = t_step[0].elapsed_time(t_step[-1]) / args.steps
+    steps_ms = np.array([t_step[i].elapsed_time(t_step[i + 1]) for i in range(args.steps)])
+    dx_each = np.array([a.elapsed_time(b) for a, b in t_dx])
+    cyc, ticks = (int(v) for v in clk.cpu().tolist())
+    fl = lora_flops(M, N, K, R)
+    value = fl / ms / 1e9
+
+    dx_ms = float(dx_each.mean())
     reps = max(args.steps, 10)
-    dx_ms = event_time_ms(bwd_dx, reps, stream)
     fwd_ms = event_time_ms(fwd, reps, stream)
-    bwd_ms = event_time_ms(bwd, reps, stream)
     ach = dx_flops(M, N, K, R) / dx_ms / 1e9
     kernel = "dx_mfma_kernel<16,false>"
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(kernel, DX_SOURCES),
-                "traffic_unit": "HBM bytes per launch", "kernel": kernel, "kernel_ms": round(dx_ms, 4),
-                "fwd_ms": round(fwd_ms, 4), "fwd_frac": round(fwd_flops(M, N, K, R) / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                "bwd_ms": round(bwd_ms, 4)}
+                "traffic_unit": "HBM bytes per launch", "kernel": kernel,
+                "kernel_ms": round(dx_ms, 4), "kernel_ms_source": "HIP events around each timed step's lora_bwd_dx",
+                "fwd_ms": round(fwd_ms, 4), "fwd_frac": round(fwd_flops(M, N, K, R) / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    step_stats = {"median": round(float(np.median(steps_ms)), 4), "p10": round(float(np.percentile(steps_ms, 10)), 4),
+                  "p90": round(float(np.percentile(steps_ms, 90)), 4), "min": round(float(steps_ms.min()), 4),
+                  "max": round(float(steps_ms.max()), 4)}
+    sclk = {"mhz_after_timed_steps": round(100.0 * cyc / ticks, 1) if ticks else None,
+            "how": "shader-cycle counter against the 100 MHz real-time counter over a 20 us spin enqueued "
+                   "right after the last timed step"}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -502,6 +514,8 @@ def main(argv=None):
                    "global_batch": 4, "seq_len": 2048, "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
+        "step_ms": step_stats,
+        "sclk": sclk,
         "roofline": roofline,
     }
     if not args.no_secondary:

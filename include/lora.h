@@ -325,6 +325,15 @@ lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_s
 lora_status lora_rope(int64_t M, int32_t H, int32_t Hk, int32_t D, int32_t rot, float base,
                       int32_t inverse, const int32_t* positions, void* Q, void* K, void* stream);
 
+/* ---- Diagnostics -----------------------------------------------------------------------
+ * The shader clock as a kernel sees it (measurement support, not part of the layer): one wave
+ * reads the shader-cycle counter and the 100 MHz real-time counter, spins until `ticks`
+ * real-time ticks (10 ns each, 1..10^8) have passed, and writes the two deltas to out[0]
+ * (shader cycles) and out[1] (real-time ticks); out[0] / out[1] * 100 is the average shader
+ * clock in MHz over the spin.  out: device memory of two uint64, 8-byte aligned.  Errors:
+ * LORA_ERR_NULL, LORA_ERR_ALIGN, LORA_ERR_VALUE (ticks), LORA_ERR_HIP. */
+lora_status lora_probe_sclk(uint64_t* out, uint32_t ticks, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* lora_status_str(lora_status s);
 

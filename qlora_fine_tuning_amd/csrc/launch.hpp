@@ -70,6 +70,9 @@ struct DadbArgs {
   int split_rows;  // tokens per split (the last split may be shorter)
 };
 
+// shader-clock probe (diag.hip)
+hipError_t launch_sclk_probe(unsigned long long* out, unsigned int ticks, hipStream_t s);
+
 // bf16 / int4 MFMA paths
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
 hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s);

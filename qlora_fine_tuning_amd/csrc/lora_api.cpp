@@ -689,3 +689,17 @@ lora_status lora_rope(int64_t M, int32_t H, int32_t Hk, int32_t D, int32_t rot, 
 }
 
 }  // extern "C"
+
+// ---- Diagnostics ----
+
+extern "C" {
+
+lora_status lora_probe_sclk(uint64_t* out, uint32_t ticks, void* stream) {
+  if (out == nullptr) return LORA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0) return LORA_ERR_ALIGN;
+  if (ticks < 1 || ticks > 100000000u) return LORA_ERR_VALUE;
+  return from_hip(launch_sclk_probe(reinterpret_cast<unsigned long long*>(out), ticks,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -55,6 +55,7 @@ SIGNATURES = {
     "lora_rope": (_i32, [_i64, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
     "qlora_swiglu_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 11 + [_sz, _p]),
     "qlora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 16 + [_sz, _p]),
+    "lora_probe_sclk": (_i32, [_p, ctypes.c_uint32, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -645,3 +646,13 @@ def qlora_swiglu_bwd(dH, X, Wguq, Wgus, Ag, Au, Bg, Bu, GU, XA, scale: float, *,
                               _stream(stream))
     _check("qlora_swiglu_bwd", st)
     return dX, dAg, dAu, dBg, dBu
+
+
+def lora_probe_sclk(ticks: int = 2000, *, out=None, stream=None) -> torch.Tensor:
+    """Enqueue the shader-clock probe; returns the device tensor [shader cycles, 100 MHz ticks]
+    (int64), to be read after the stream has run it."""
+    lib = load()
+    if out is None:
+        out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _check("lora_probe_sclk", lib.lora_probe_sclk(_ptr(out), int(ticks), _stream(stream)))
+    return out

@@ -394,3 +394,10 @@ def test_binding_argument_counts_match_the_header():
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(args), f"{name}: header {len(params)} parameters, binding {len(args)}"
+
+
+def test_probe_sclk_validation(lib):
+    assert lib.lora_probe_sclk(None, 2000, None) == 1
+    assert lib.lora_probe_sclk(ctypes.c_void_p(0x10004), 2000, None) == 4
+    assert lib.lora_probe_sclk(P, 0, None) == 8
+    assert lib.lora_probe_sclk(P, 100000001, None) == 8
