@@ -361,10 +361,13 @@ def bench_rope(lora, torch, dev, reps, copies=4):
 def bench_decode(lora, torch, dev, reps, copies=6):
     """Decode matrix-vector rate, rotating over `copies` distinct weight copies (> 256 MB MALL), with
     the int4 weight (group 64, fp16 scales) and with the MXFP4 weight (blocks of 32, E8M0 scales):
-    both move 0.5 + 1/32 bytes per weight."""
+    both move 0.5 + 1/32 bytes per weight.  The C entry points are called with their arguments
+    marshalled once (a call is ~15 us: Python must not set the pace)."""
     from qlora_fine_tuning_amd.workloads import workload_inputs
 
     out = []
+    lib = lora.load()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
     for fmt in ("int4", "mxfp4"):
         for name in ("decode_up", "decode_down"):
             inp = workload_inputs(name, M=8)
@@ -377,25 +380,32 @@ def bench_decode(lora, torch, dev, reps, copies=6):
             A, B = dev_bits(inp.A, dev), dev_bits(inp.B, dev)
             Xall = dev_bits(inp.X, dev)
             stream = torch.cuda.current_stream()
+            sp = ctypes.c_void_p(stream.cuda_stream)
             for M in (1, 4, 8):
                 X = Xall[:M].contiguous()
                 Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-                ws = torch.zeros(max(lora.qlora_fwd_workspace_bytes(M, N, K, R), 256), dtype=torch.uint8,
-                                 device=dev)
+                need = lora.qlora_fwd_workspace_bytes(M, N, K, R)
+                ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+                if fmt == "int4":
+                    args = [(M, N, K, R, inp.scale, 64, p(X), p(Wqs[i]), p(Wss[i]), p(A), p(B), p(Y), None,
+                             p(ws), need, sp) for i in range(copies)]
+                    fn = lib.qlora_fwd
+                else:
+                    args = [(M, N, K, R, inp.scale, p(X), p(Wqs[i]), p(Wss[i]), p(A), p(B), p(Y), None, p(ws), need,
+                             sp) for i in range(copies)]
+                    fn = lib.mxfp4_decode_fwd
                 state = {"i": 0}
 
                 def call():
                     i = state["i"]
                     state["i"] = (i + 1) % copies
-                    if fmt == "int4":
-                        lora.qlora_fwd(X, Wqs[i], Wss[i], A, B, inp.scale, Y=Y, save_xa=False, ws=ws)
-                    else:
-                        lora.mxfp4_decode_fwd(X, Wqs[i], Wss[i], A, B, inp.scale, Y=Y, save_xa=False, ws=ws)
+                    assert fn(*args[i]) == 0
 
                 for _ in range(copies):
                     call()
                 torch.cuda.synchronize()
                 ms = event_time_ms(call, reps * copies, stream)
+                assert lora.qlora_decode_status(ws) == 0
                 wbytes = N * K // 2 + (N * (K // 64) * 2 if fmt == "int4" else N * (K // 32))
                 nbytes = wbytes + R * K * 2 + N * R * 2 + M * K * 2 + M * N * 2
                 out.append({"workload": name, "weights": fmt, "M": M, "N": N, "K": K,
@@ -414,6 +424,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the QLoRA and decode lines")
+    ap.add_argument("--only", default=None, help="comma-separated secondary lines to run (e.g. decode)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline (whole workload, repeated)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -519,15 +530,17 @@ def main(argv=None):
         "roofline": roofline,
     }
     if not args.no_secondary:
-        result["secondary"] = {"mlp": bench_mlp(lora, torch, dev, 20),
-                               "mlp_swiglu": bench_swiglu(lora, torch, dev, 20),
-                               "qlora": bench_qlora_ffn(lora, torch, dev, 20),
-                               "qlora_mxfp4": bench_qlora_ffn(lora, torch, dev, 20, group=32),
-                               "decode": bench_decode(lora, torch, dev, 20),
-                               "rmsnorm": bench_rmsnorm(lora, torch, dev, 20),
-                               "lm_head_ce": bench_ce(lora, torch, dev, 5),
-                               "rope": bench_rope(lora, torch, dev, 20),
-                               "torch_unfused": bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}
+        lines = {"mlp": lambda: bench_mlp(lora, torch, dev, 20),
+                 "mlp_swiglu": lambda: bench_swiglu(lora, torch, dev, 20),
+                 "qlora": lambda: bench_qlora_ffn(lora, torch, dev, 20),
+                 "qlora_mxfp4": lambda: bench_qlora_ffn(lora, torch, dev, 20, group=32),
+                 "decode": lambda: bench_decode(lora, torch, dev, 20),
+                 "rmsnorm": lambda: bench_rmsnorm(lora, torch, dev, 20),
+                 "lm_head_ce": lambda: bench_ce(lora, torch, dev, 5),
+                 "rope": lambda: bench_rope(lora, torch, dev, 20),
+                 "torch_unfused": lambda: bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}
+        only = set(args.only.split(",")) if args.only else None
+        result["secondary"] = {k: f() for k, f in lines.items() if only is None or k in only}
     if args.calib_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -130,17 +130,23 @@ lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W,
 lora_status qlora_dequant(int64_t N, int64_t K, int32_t group, const uint8_t* Wq, const void* Ws,
                           void* W_bf16, void* stream);
 
-/* Bytes of device workspace qlora_fwd needs: 0 unless M <= 8 and K % 1024 == 0; for that (decode) path, per-
- * tile arrival counters followed by per-split partial sums.  The counters must be zero before
- * the first call that uses the workspace (e.g. hipMemset once after allocating it); every
- * call leaves them zero again, so a workspace can be reused by later calls without clearing.
- * Two calls that overlap in time must not share a workspace. */
+/* Bytes of device workspace qlora_fwd needs: 0 unless 1 <= M <= 8 and K % 1024 == 0.  For that
+ * (decode) path: a 16-byte header (a status word and a test hold word), the per-tile arrival
+ * counters and ready tokens and an adapter counter (u32, 2 N/64 + 1 of them), then the fp32 partial
+ * sums.  The header and the counters must be zero before the first call that uses the workspace
+ * (allocate it zeroed, or clear it with qlora_decode_status); every call that completes normally
+ * leaves them zero, so a workspace serves later calls of any M without clearing.  Two calls that
+ * overlap in time must not share a workspace. */
 size_t qlora_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
 
 /* QLoRA forward: Y = X W~^T + scale (X A^T) B^T with W~ unpacked in registers.  For M <= 8
- * and K a multiple of 1024 it runs as one HBM-bandwidth-bound matrix-vector kernel (per generated token every weight
- * byte is streamed once: "探微索隐 ...", §一, the memory wall of decoding); its K splits are
- * added in a fixed order, so results do not depend on timing.
+ * and K a multiple of 1024 it runs as one HBM-bandwidth-bound matrix-vector kernel (per generated
+ * token every weight byte is streamed once: "探微索隐 ...", §一, the memory wall of decoding): its
+ * first workgroups compute X A^T and announce it to the tile workgroups, which wait for it a bounded
+ * time (about a second); partial sums are added in a fixed order, so results do not depend on
+ * timing.  If a wait gives up (e.g. when other work keeps the announcing workgroups off the
+ * device), the tile's Y is written as NaN and the workspace's status word is set; from then on every
+ * call on that workspace writes NaN until qlora_decode_status clears it.
  *   X [M][K], A [R][K], B [N][R] bf16; Wq [N][K/2]; Ws [N][K/64] fp16   (inputs)
  *   Y [M][N] bf16; XA [M][R] fp32 or NULL                               (outputs)
  *   ws: at least qlora_fwd_workspace_bytes() bytes (may be NULL when that is 0). */
@@ -148,6 +154,19 @@ lora_status qlora_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, i
                       const void* X, const uint8_t* Wq, const void* Ws,
                       const void* A, const void* B, void* Y, float* XA,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* Status of a decode workspace (the M <= 8 path of qlora_fwd and mxfp4_decode_fwd): waits for the
+ * stream, writes the status word to *status (0: every call completed normally; 1: a bounded wait
+ * gave up, and that call's outputs and those of every later call were written as NaN) and, with
+ * clear != 0, zeroes the whole workspace (ws_bytes) so it can be used again.  Synchronises
+ * `stream`; not for use inside graph capture.  Errors: LORA_ERR_NULL, LORA_ERR_ALIGN,
+ * LORA_ERR_WORKSPACE (fewer than 16 bytes), LORA_ERR_HIP. */
+lora_status qlora_decode_status(void* ws, size_t ws_bytes, uint32_t* status, int32_t clear, void* stream);
+
+/* Test hook for the decode path's failure handling: with hold != 0, calls on this workspace do not
+ * announce X A^T to the tile workgroups, so their bounded waits give up (after about a second) and
+ * the call reports it as above.  Synchronises `stream`. */
+lora_status qlora_decode_set_hold(void* ws, size_t ws_bytes, int32_t hold, void* stream);
 
 /* Bytes of device workspace qlora_bwd needs. */
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
@@ -272,8 +291,8 @@ lora_status mxfp4_dequant(int64_t N, int64_t K, const uint8_t* Wq, const uint8_t
                           void* stream);
 
 /* Bytes of device workspace mxfp4_decode_fwd needs (0 outside its shapes); the same layout and
- * rule as qlora_fwd's decode path: the counters must be zero before the first call that uses the
- * workspace, and every call leaves them zero. */
+ * rules as qlora_fwd's decode path (control block zero before the first call, left zero by every
+ * call that completes normally, status and clearing through qlora_decode_status). */
 size_t mxfp4_decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
 
 /* Decode forward with the MXFP4 weight: Y = X W~^T + scale (X A^T) B^T for 1 <= M <= 8 tokens and

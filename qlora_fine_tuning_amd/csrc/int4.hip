@@ -160,8 +160,11 @@ dequant_mxfp4_kernel(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__
 //    (normally seen during the loop), writes Y, and clears the token and the counter.
 // Every control word is thus cleared by the one workgroup that used it last, and no word is
 // shared by more than one tile.  Tile workgroups wait only for the adapter workgroups, which
-// come first in the grid (dispatched first) and wait for nothing, and the wait is bounded:
-// if the token never arrives the tile's Y is written as NaN instead of hanging the device.
+// come first in the grid (dispatched first) and wait for nothing, and the wait is bounded.  If
+// the token never arrives, the tile writes NaN and sets the sticky status word at the head of
+// the workspace (a token set later would otherwise pass a stale X A^T to the next call); while
+// the status word is set, every call on the workspace writes NaN at once, until the caller reads
+// and clears it (qlora_decode_status).
 // Cross-workgroup data (partials, XA_f, counters) crosses XCDs, whose L2 caches are not
 // coherent with each other; it is written and read with device-scope relaxed atomic
 // accesses, and every writer waits for its stores (vmcnt) before moving a counter.
@@ -205,6 +208,7 @@ struct DecodeArgs {
   const uint16_t* B;
   uint16_t* Y;
   float* XA;
+  uint32_t* hdr;   // [0] status (nonzero: a wait gave up), [1] hold (test hook: no tokens published)
   uint32_t* ctl;   // [T] split arrival counters, [T] ready tokens, adapter arrival counter
   float* part;     // [S][T][M][64] tile partials
   float* pxa;      // [NXA][M][RP] adapter partials
@@ -230,6 +234,7 @@ __device__ void decode_adapter(const DecodeArgs& a, int xw, float* sred, int* sf
   const int M = a.M, K = a.K;
   const int t = min(r16, M - 1);
   const int kw = xw * kDecXK + 256 * w;
+  const uint32_t hold = __hip_atomic_load(a.hdr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   f32x4 acc[NA];
 #pragma unroll
   for (int ib = 0; ib < NA; ++ib) acc[ib] = fzero4();
@@ -280,7 +285,8 @@ __device__ void decode_adapter(const DecodeArgs& a, int xw, float* sred, int* sf
   }
   wait_stores();
   __syncthreads();
-  for (int t = tid; t < T; t += 256) __hip_atomic_store(ctl + T + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (hold == 0u)
+    for (int t = tid; t < T; t += 256) __hip_atomic_store(ctl + T + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (tid == 0) __hip_atomic_store(ctl + 2 * T, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -368,6 +374,8 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
   };
 
   const int t = min(r16, M - 1);
+  // the status word, read now and used at the end: a workspace whose status is set gives NaN
+  const uint32_t status0 = tid == 0 ? __hip_atomic_load(a.hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
   f32x4 acc[2] = {fzero4(), fzero4()};
   // one step: MFMA (piece i, dword j) covers k = 512 st + 32 (4 g4 + i) + 8 j .. +7
   auto compute = [&](const uint8_t* sW, const uint8_t* sX, const uint32_t* sS) {
@@ -477,13 +485,15 @@ __global__ void __launch_bounds__(256) decode_int4_kernel(DecodeArgs a) {
   // ---- this workgroup finishes the tile: wait for X A^T, add the low-rank term, write Y ----
   __syncthreads();
   if (tid == 0) {
+    const bool poisoned = status0 != 0u;
     uint32_t n = 0;
-    if (!seen)
+    if (!seen && !poisoned)
       while (__hip_atomic_load(ctl + T + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u && n < kDecSpin) {
         __builtin_amdgcn_s_sleep(8);
         ++n;
       }
-    sflag = n < kDecSpin;
+    if (n >= kDecSpin) __hip_atomic_fetch_or(a.hdr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sflag = (n < kDecSpin) && !poisoned;
   }
   __syncthreads();
   const bool ready = sflag;
@@ -566,14 +576,15 @@ static int decode_splits(int64_t N, int64_t K) {
 }
 
 struct DecodeLayout {
-  size_t ctl, part, pxa, xaf, total;
+  size_t hdr, ctl, part, pxa, xaf, total;
 };
 static DecodeLayout decode_layout(int64_t M, int64_t N, int64_t K, int R) {
   const size_t T = (size_t)(N / kDecRows), S = (size_t)decode_splits(N, K), RP = (size_t)decode_rp(R);
   const size_t NXA = (size_t)(K / kDecXK);
   DecodeLayout l;
-  l.ctl = 0;
-  l.part = a256((2 * T + 1) * 4);
+  l.hdr = 0;
+  l.ctl = 16;
+  l.part = a256(16 + (2 * T + 1) * 4);
   l.pxa = l.part + a256(S * T * (size_t)M * kDecRows * 4);
   l.xaf = l.pxa + a256(NXA * (size_t)M * RP * 4);
   l.total = l.xaf + a256((size_t)M * RP * 4);
@@ -594,6 +605,7 @@ static hipError_t launch_gemv(const FwdArgs& f, void* ws, hipStream_t s) {
   a.B = static_cast<const uint16_t*>(f.B);
   a.Y = static_cast<uint16_t*>(f.Y);
   a.XA = f.XA;
+  a.hdr = reinterpret_cast<uint32_t*>(base + l.hdr);
   a.ctl = reinterpret_cast<uint32_t*>(base + l.ctl);
   a.part = reinterpret_cast<float*>(base + l.part);
   a.pxa = reinterpret_cast<float*>(base + l.pxa);

@@ -141,9 +141,12 @@ hipError_t launch_quantize_int4(int64_t N, int64_t K, const float* W, uint8_t* W
                                 hipStream_t s);
 hipError_t launch_dequant_int4(int64_t N, int64_t K, const uint8_t* Wq, const uint16_t* Ws,
                                uint16_t* Wout, hipStream_t s);
-// decode path (M <= 8): `ws` holds gemv_workspace_bytes() bytes whose leading per-tile
-// arrival counters are zero before the call and are left zero by it
+// decode path (M <= 8): `ws` holds gemv_workspace_bytes() bytes: a 16-byte header (status word,
+// hold word) and then the per-tile arrival counters, ready tokens and the adapter counter, all zero
+// before the first call and left zero by every call that completes normally
 hipError_t launch_gemv_int4(const FwdArgs& a, void* ws, hipStream_t s);
+constexpr int kDecodeStatusWord = 0, kDecodeHoldWord = 1;
+constexpr size_t kDecodeHeaderBytes = 16;
 // MXFP4 weights: codes (N x K/2 bytes, int4 nibble layout) and E8M0 block exponents (N x K/32
 // bytes); the decode product takes them in a.W and a.Ws
 hipError_t launch_quantize_mxfp4(int64_t N, int64_t K, const float* W, uint8_t* Wq, uint8_t* We, hipStream_t s);

@@ -535,6 +535,29 @@ size_t mxfp4_decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R) 
   return gemv_workspace_bytes(M, N, K, R);
 }
 
+lora_status qlora_decode_status(void* ws, size_t ws_bytes, uint32_t* status, int32_t clear, void* stream) {
+  if (ws == nullptr || status == nullptr) return LORA_ERR_NULL;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  if (ws_bytes < kDecodeHeaderBytes) return LORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* ctl = static_cast<uint32_t*>(ws);
+  hipError_t e = hipMemcpyAsync(status, ctl + kDecodeStatusWord, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && clear) e = hipMemsetAsync(ws, 0, ws_bytes, s);  // the whole workspace
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return from_hip(e);
+}
+
+lora_status qlora_decode_set_hold(void* ws, size_t ws_bytes, int32_t hold, void* stream) {
+  if (ws == nullptr) return LORA_ERR_NULL;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  if (ws_bytes < kDecodeHeaderBytes) return LORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t v = hold != 0 ? 1u : 0u;
+  hipError_t e = hipMemcpyAsync(static_cast<uint32_t*>(ws) + kDecodeHoldWord, &v, 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return from_hip(e);
+}
+
 lora_status mxfp4_decode_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float scale, const void* X, const uint8_t* Wq,
                              const uint8_t* We, const void* A, const void* B, void* Y, float* XA, void* ws,
                              size_t ws_bytes, void* stream) {

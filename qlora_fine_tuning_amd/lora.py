@@ -56,6 +56,8 @@ SIGNATURES = {
     "qlora_swiglu_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 11 + [_sz, _p]),
     "qlora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 16 + [_sz, _p]),
     "lora_probe_sclk": (_i32, [_p, ctypes.c_uint32, _p]),
+    "qlora_decode_status": (_i32, [_p, _sz, _p, _i32, _p]),
+    "qlora_decode_set_hold": (_i32, [_p, _sz, _i32, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -656,3 +658,20 @@ def lora_probe_sclk(ticks: int = 2000, *, out=None, stream=None) -> torch.Tensor
         out = torch.zeros(2, dtype=torch.int64, device="cuda")
     _check("lora_probe_sclk", lib.lora_probe_sclk(_ptr(out), int(ticks), _stream(stream)))
     return out
+
+
+def qlora_decode_status(ws: torch.Tensor, *, clear: bool = False, stream=None) -> int:
+    """Status word of a decode workspace (0: normal; 1: a bounded wait gave up); waits for the stream.
+    With clear, the control block is zeroed so the workspace can be used again."""
+    lib = load()
+    out = ctypes.c_uint32(0)
+    _check("qlora_decode_status", lib.qlora_decode_status(_ptr(ws), ws.numel() * ws.element_size(),
+                                                          ctypes.byref(out), int(clear), _stream(stream)))
+    return int(out.value)
+
+
+def qlora_decode_set_hold(ws: torch.Tensor, hold: bool, *, stream=None) -> None:
+    """Test hook: with hold, decode calls on `ws` withhold their X A^T partials, so their bounded waits give up."""
+    lib = load()
+    _check("qlora_decode_set_hold", lib.qlora_decode_set_hold(_ptr(ws), ws.numel() * ws.element_size(), int(hold),
+                                                              _stream(stream)))

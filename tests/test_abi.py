@@ -401,3 +401,14 @@ def test_probe_sclk_validation(lib):
     assert lib.lora_probe_sclk(ctypes.c_void_p(0x10004), 2000, None) == 4
     assert lib.lora_probe_sclk(P, 0, None) == 8
     assert lib.lora_probe_sclk(P, 100000001, None) == 8
+
+
+def test_decode_status_validation(lib):
+    st = ctypes.c_uint32(0)
+    assert lib.qlora_decode_status(None, 256, ctypes.byref(st), 0, None) == 1
+    assert lib.qlora_decode_status(P, 256, None, 0, None) == 1
+    assert lib.qlora_decode_status(MIS, 256, ctypes.byref(st), 0, None) == 4
+    assert lib.qlora_decode_status(P, 15, ctypes.byref(st), 0, None) == 6
+    assert lib.qlora_decode_set_hold(None, 256, 1, None) == 1
+    assert lib.qlora_decode_set_hold(MIS, 256, 1, None) == 4
+    assert lib.qlora_decode_set_hold(P, 8, 1, None) == 6

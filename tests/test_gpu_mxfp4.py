@@ -99,7 +99,7 @@ def test_mxfp4_decode_workspace_reuse_and_determinism(gpu_lib):
                 first[M] = (Y.clone(), XA.clone())
             else:
                 assert torch.equal(Y, first[M][0]) and torch.equal(XA, first[M][1])
-    assert not ws[: 4 * (N // 64)].any(), "arrival counters not left at zero"
+    assert not ws[: 16 + 4 * (2 * (N // 64) + 1)].any(), "control words not left at zero"
 
 
 # ---- QLoRA training and prefill with MXFP4 weights (qlora_* with group 32) ----------------

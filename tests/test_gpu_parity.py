@@ -379,12 +379,40 @@ def test_decode_workspace_reuse(gpu_lib):
                 first[M] = (Y.clone(), XA.clone())
             else:
                 assert torch.equal(Y, first[M][0]) and torch.equal(XA, first[M][1])
-    T = N // 64
-    assert not ws[: 4 * T].any(), "arrival counters not left at zero"
+    ctl = 16 + 4 * (2 * (N // 64) + 1)  # header, per-tile counters and tokens, adapter counter
+    assert not ws[:ctl].any(), "control words not left at zero"
+    assert gpu_lib.qlora_decode_status(ws) == 0
     # and a call on a fresh workspace gives the same bits
     Y, XA = lora.qlora_fwd(X8[:5].contiguous(), Wq, Ws, A, B, inp.scale)
     torch.cuda.synchronize()
     assert torch.equal(Y, first[5][0]) and torch.equal(XA, first[5][1])
+
+
+def test_decode_bounded_wait_reports_and_recovers(gpu_lib):
+    # the host withholds the X A^T announcements (test hook), so every workgroup's bounded wait
+    # gives up: the call writes NaN and sets the status word; the next call on the same workspace
+    # writes NaN at once; after the status is read and cleared, calls are correct again
+    _say("case decode bounded wait (announcements withheld)")
+    lora = gpu_lib
+    inp = make_inputs(4, 1024, 2048, 16, seed=31, dtype="bf16", int4=True, with_dy=False)
+    Wq, Ws, packed, sref = quantize_both(lora, inp)
+    X, A, B = (to_dev(inp, n) for n in ("X", "A", "B"))
+    ws = torch.zeros(lora.qlora_fwd_workspace_bytes(4, 1024, 2048, 16), dtype=torch.uint8, device=X.device)
+    lora.qlora_decode_set_hold(ws, True)
+    Y1, XA1 = lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale, ws=ws)
+    assert lora.qlora_decode_status(ws) == 1
+    assert torch.isnan(Y1.float()).all()
+    Y2, _ = lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale, ws=ws)
+    assert lora.qlora_decode_status(ws, clear=True) == 1
+    assert torch.isnan(Y2.float()).all()
+    assert not ws.any()
+    Y3, XA3 = lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale, ws=ws)
+    assert lora.qlora_decode_status(ws) == 0
+    x, a, b = (values(inp, n) for n in ("X", "A", "B"))
+    Yr, XAr = oracle.lora_forward(x, oracle.dequant_int4(packed, sref), a, b, inp.scale)
+    assert_close("Y", host(Y3), Yr)
+    assert_close("XA", host(XA3), XAr)
+    assert not ws[: 16 + 4 * (2 * (1024 // 64) + 1)].any()
 
 
 # ---------------------------------------------------------------------------
