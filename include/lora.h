@@ -168,6 +168,20 @@ lora_status qlora_decode_status(void* ws, size_t ws_bytes, uint32_t* status, int
  * the call reports it as above.  Synchronises `stream`. */
 lora_status qlora_decode_set_hold(void* ws, size_t ws_bytes, int32_t hold, void* stream);
 
+/* The decode path of qlora_fwd (1 <= M <= 8, K a multiple of 1024; group 64: int4, group 32:
+ * MXFP4) for callers that cannot allocate: code under graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It takes no workspace: its scratch is a static device array
+ * of 2 MiB per device (kept until the process ends), which the call clears (control words only, by
+ * a small kernel) before the decode kernel runs; it calls no allocating routine.  Same arguments
+ * and results as qlora_fwd otherwise (Y bitwise equal to qlora_fwd's for the same inputs).  Shapes
+ * whose decode workspace (qlora_fwd_workspace_bytes) exceeds 2 MiB return LORA_ERR_WORKSPACE (at
+ * M = 8 and rank 64 that is N above about 63000); non-decode shapes return LORA_ERR_SHAPE.  Calls on one device
+ * share the array: two calls that overlap in time (e.g. on two streams) race.  A call whose bounded
+ * wait gave up writes NaN (no status word is kept here; the next call starts clean). */
+lora_status qlora_decode_fwd_noalloc(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                                     const void* X, const uint8_t* Wq, const void* Ws, const void* A,
+                                     const void* B, void* Y, float* XA, void* stream);
+
 /* Bytes of device workspace qlora_bwd needs. */
 size_t qlora_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t R);
 

@@ -592,6 +592,7 @@ static DecodeLayout decode_layout(int64_t M, int64_t N, int64_t K, int R) {
 }
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int R) { return decode_layout(M, N, K, R).total; }
+size_t gemv_control_bytes(int64_t N) { return a256(16 + (2 * (size_t)(N / kDecRows) + 1) * 4); }
 
 template <bool FP4>
 static hipError_t launch_gemv(const FwdArgs& f, void* ws, hipStream_t s) {

@@ -154,5 +154,7 @@ hipError_t launch_dequant_mxfp4(int64_t N, int64_t K, const uint8_t* Wq, const u
                                 hipStream_t s);
 hipError_t launch_gemv_mxfp4(const FwdArgs& a, void* ws, hipStream_t s);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int R);
+// leading bytes of that workspace holding the header and control words (zero between calls)
+size_t gemv_control_bytes(int64_t N);
 
 }  // namespace lora

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -723,6 +724,76 @@ lora_status lora_probe_sclk(uint64_t* out, uint32_t ticks, void* stream) {
   if (ticks < 1 || ticks > 100000000u) return LORA_ERR_VALUE;
   return from_hip(launch_sclk_probe(reinterpret_cast<unsigned long long*>(out), ticks,
                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---- The decode product without a caller workspace ----
+//
+// For callers that cannot allocate (code under graph capture, tight serving loops): the decode
+// path's workspace lives in a file-scope device array, one copy per device, whose address is
+// taken once per device with hipGetSymbolAddress (in host code the array's name is only a
+// stand-in).  Every call clears the array's control words with a small fill kernel before the
+// decode kernel, so nothing a previous call left there (even one whose bounded wait gave up) is
+// read.  Calls that overlap in time on one device share the array and race.
+
+namespace {
+
+constexpr size_t kDecodeScratchBytes = (size_t)2 << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+__device__ __align__(256) uint8_t lora_decode_scratch[kDecodeScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// this device's copy of the array (resolved on the first call on the device, that device current)
+lora_status decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return LORA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(lora_decode_scratch));
+    if (e != hipSuccess) return from_hip(e);
+    if (p == nullptr) return LORA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status qlora_decode_fwd_noalloc(int64_t M, int64_t N, int64_t K, int32_t R, float scale, int32_t group,
+                                     const void* X, const uint8_t* Wq, const void* Ws, const void* A,
+                                     const void* B, void* Y, float* XA, void* stream) {
+  if (group != 64 && group != 32) return LORA_ERR_GROUP;
+  lora_status st = check_dims(M, N, K, R);
+  if (st != LORA_OK) return st;
+  if (!use_gemv(M, K)) return LORA_ERR_SHAPE;  // the decode shapes only
+  if (!std::isfinite(scale)) return LORA_ERR_VALUE;
+  st = check_ptrs(X, Wq, Ws, A, B, Y);
+  if (st != LORA_OK) return st;
+  if (XA != nullptr && !aligned16(XA)) return LORA_ERR_ALIGN;
+  if (gemv_workspace_bytes(M, N, K, R) > kDecodeScratchBytes) return LORA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = decode_scratch(&ws);
+  if (st != LORA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_fill_u32(ws, gemv_control_bytes(N), 0u, s);
+  if (e != hipSuccess) return from_hip(e);
+  FwdArgs a{X, Wq, Ws, A, B, Y, XA, M, N, K, R, scale};
+  a.fp4 = group == 32;
+  return from_hip(a.fp4 ? launch_gemv_mxfp4(a, ws, s) : launch_gemv_int4(a, ws, s));
 }
 
 }  // extern "C"

@@ -57,6 +57,7 @@ SIGNATURES = {
     "qlora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 16 + [_sz, _p]),
     "lora_probe_sclk": (_i32, [_p, ctypes.c_uint32, _p]),
     "qlora_decode_status": (_i32, [_p, _sz, _p, _i32, _p]),
+    "qlora_decode_fwd_noalloc": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]),
     "qlora_decode_set_hold": (_i32, [_p, _sz, _i32, _p]),
     "lora_status_str": (ctypes.c_char_p, [_i32]),
     "lora_last_hip_error": (ctypes.c_char_p, []),
@@ -675,3 +676,13 @@ def qlora_decode_set_hold(ws: torch.Tensor, hold: bool, *, stream=None) -> None:
     lib = load()
     _check("qlora_decode_set_hold", lib.qlora_decode_set_hold(_ptr(ws), ws.numel() * ws.element_size(), int(hold),
                                                               _stream(stream)))
+
+
+def qlora_decode_fwd_noalloc(X, Wq, Ws, A, B, scale: float, *, Y, XA=None, stream=None) -> None:
+    """The decode product with the library's static scratch (no workspace; the caller passes Y)."""
+    lib = load()
+    M, K = X.shape
+    N, R = Wq.shape[0], A.shape[0]
+    st = lib.qlora_decode_fwd_noalloc(M, N, K, R, float(scale), _group_of(Ws), _ptr(X), _ptr(Wq), _ptr(Ws), _ptr(A),
+                                      _ptr(B), _ptr(Y), _ptr(XA), _stream(stream))
+    _check("qlora_decode_fwd_noalloc", st)

@@ -412,3 +412,19 @@ def test_decode_status_validation(lib):
     assert lib.qlora_decode_set_hold(None, 256, 1, None) == 1
     assert lib.qlora_decode_set_hold(MIS, 256, 1, None) == 4
     assert lib.qlora_decode_set_hold(P, 8, 1, None) == 6
+
+
+def test_decode_noalloc_validation(lib):
+    # rejected before any HIP call: group, shape, the decode shapes only, scale, pointers, and a
+    # decode workspace beyond the static scratch's 2 MiB
+    args = lambda M=4, N=256, K=1024, R=16, scale=2.0, group=64, X=P, Wq=P, Ws=P, A=P, B=P, Y=P, XA=None: (
+        M, N, K, R, scale, group, X, Wq, Ws, A, B, Y, XA, None)
+    f = lib.qlora_decode_fwd_noalloc
+    assert f(*args(group=16)) == 7
+    assert f(*args(N=100)) == 2
+    assert f(*args(M=9)) == 2 and f(*args(M=0)) == 2 and f(*args(K=512)) == 2
+    assert f(*args(R=12)) == 3
+    assert f(*args(scale=float("nan"))) == 8
+    assert f(*args(X=None)) == 1 and f(*args(Y=None)) == 1 and f(*args(Ws=None)) == 1
+    assert f(*args(XA=MIS)) == 4
+    assert f(*args(M=8, N=1 << 20)) == 6
