@@ -308,27 +308,32 @@ def bench_rmsnorm(lora, torch, dev, reps):
 
 def bench_ce(lora, torch, dev, reps):
     """Chunked cross-entropy over an LM head at the page's workload (batch 8 x 2048 tokens, vocabulary
-    128000, hidden 4096): loss and dX per call, TFLOP/s counting 4 M V K (the logits and the dX
-    products; each is formed once)."""
+    128000, hidden 4096): loss and dX per call at the library's default chunk (its fp32 logits within
+    512 MiB) and at the page's 256-token chunk, TFLOP/s counting 4 M V K (the logits and the dX
+    products; each is formed once), with the workspace each needs."""
     from qlora_fine_tuning_amd.workloads import make_ce_inputs
 
     M, K, V = 16384, 4096, 128000
     inp = make_ce_inputs(M, K, V, seed=8, logit_std=3.0)
     X, W = dev_bits(inp.X, dev), dev_bits(inp.W, dev)
     lab = torch.from_numpy(inp.labels).to(dev)
-    ws = torch.empty(lora.lora_ce_workspace_bytes(M, V, K, 0, True), dtype=torch.uint8, device=dev)
     loss = torch.empty(M, dtype=torch.float32, device=dev)
     dX = torch.empty_like(X)
-    call = lambda: lora.lora_ce(X, W, lab, loss=loss, dX=dX, ws=ws)
-    for _ in range(2):
-        call()
-    torch.cuda.synchronize()
-    ms = event_time_ms(call, reps, torch.cuda.current_stream())
-    out = {"workload": "lm_head_ce", "M": M, "K": K, "V": V, "chunk": 8192, "ms_per_call": round(ms, 3),
-           "TFLOP/s": round(4 * M * V * K / ms / 1e9, 1),
-           "frac_bf16_peak": round(4 * M * V * K / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-           "workspace_GB": round(ws.numel() / 1e9, 3), "full_fp32_logits_GB": round(M * V * 4 / 1e9, 2)}
-    del X, W, ws, dX
+    out = []
+    for chunk in (0, 256):
+        ws = torch.empty(lora.lora_ce_workspace_bytes(M, V, K, chunk, True), dtype=torch.uint8, device=dev)
+        call = lambda: lora.lora_ce(X, W, lab, loss=loss, dX=dX, ws=ws, chunk=chunk)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        ms = event_time_ms(call, reps, torch.cuda.current_stream())
+        out.append({"workload": "lm_head_ce", "M": M, "K": K, "V": V,
+                    "chunk": chunk or lora.lora_ce_default_chunk(V), "default_chunk": chunk == 0,
+                    "ms_per_call": round(ms, 3), "TFLOP/s": round(4 * M * V * K / ms / 1e9, 1),
+                    "frac_bf16_peak": round(4 * M * V * K / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                    "workspace_GB": round(ws.numel() / 1e9, 3), "full_fp32_logits_GB": round(M * V * 4 / 1e9, 2)})
+        del ws
+    del X, W, dX
     return out
 
 

@@ -323,24 +323,38 @@ lora_status mxfp4_decode_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float s
  * each chunk of tokens computes its logits, its losses and its gradient, then drops the logits,
  * and the losses are summed).  For hidden states X (M x K bf16), the frozen LM head W (V x K bf16)
  * and labels (M int32 in [0, V)):
- *   loss[m] = logsumexp_v (X W^T)[m][v] - (X W^T)[m][label[m]],
- *   dX      = grad_scale (softmax(X W^T) - onehot(label)) W        (M x K bf16, optional),
- * with grad_scale = 1/M for the mean loss.  Per chunk of `chunk` tokens (0: 8192) the logits
- * are formed once on the matrix cores; the pass keeps, per row and 128 columns, the maximum and
- * the sum of exp (fp32, from the accumulators) and the label's logit, and a fixed-order
+ *   loss[m]    = logsumexp_v (X W^T)[m][v] - (X W^T)[m][label[m]],
+ *   loss_total = grad_scale * sum_m loss[m]                          (the objective),
+ *   dX         = grad_scale (softmax(X W^T) - onehot(label)) W      (its gradient, M x K bf16),
+ * so grad_scale = 1/M gives the mean loss and its gradient.  Per chunk of `chunk` tokens the
+ * logits are formed once on the matrix cores; the pass keeps, per row and 128 columns, the maximum
+ * and the sum of exp (fp32, from the accumulators) and the label's logit, and a fixed-order
  * reduction gives the log-sum-exp and the loss.  With dX the same pass also stores the chunk's
- * fp32 logits in the workspace (chunk x V x 4 bytes: sized for the accelerator's memory rather
- * than the whole batch's), an elementwise pass turns them into the bf16 gradient of the logits,
- * and the input-gradient kernel multiplies that by W.  V and K multiples of 64; chunk x V below 2^31.  loss (M fp32) is
- * written; loss_sum (one fp32, the fixed-order sum of loss) and dX may be NULL.  A label outside
- * [0, V) gives loss NaN.  Errors as for lora_fwd. */
+ * fp32 logits in the workspace (as a high and a low 16-bit plane, chunk x V x 4 bytes in all), an
+ * elementwise pass writes the bf16 gradient of the logits over the high plane, and the
+ * input-gradient kernel multiplies that by W.  chunk = 0 takes lora_ce_default_chunk(V): the
+ * largest multiple of 256 tokens whose fp32 logits fit in 512 MiB (at least 256; 1024 at
+ * V = 128000), so the workspace stays near that bound whatever M is.  V and K multiples of 64;
+ * chunk x V below 2^31.  loss (M fp32) is written; loss_total (one fp32, the fixed-order sum of
+ * loss times grad_scale) and dX may be NULL.  A label outside [0, V) gives loss NaN.  Errors as
+ * for lora_fwd. */
+
+/* The chunk lora_ce takes when its `chunk` is 0. */
+int64_t lora_ce_default_chunk(int64_t V);
 
 /* Bytes of device workspace lora_ce needs (grad: dX requested), no initialisation required. */
 size_t lora_ce_workspace_bytes(int64_t M, int64_t V, int64_t K, int64_t chunk, int32_t grad);
 
 lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_scale,
                     const void* X, const void* W, const int32_t* labels, float* loss,
-                    float* loss_sum, void* dX, void* ws, size_t ws_bytes, void* stream);
+                    float* loss_total, void* dX, void* ws, size_t ws_bytes, void* stream);
+
+/* The chain rule's last step for lora_ce's dX when the objective arrives with an upstream
+ * gradient g (one fp32 in device memory, read by the kernel, so the host never waits for it):
+ * out = bf16(dX * g[0]) over M x K bf16 values (out may equal dX).  K a multiple of 8; dX and out
+ * 16-byte aligned, g 4-byte aligned.  Errors: LORA_ERR_SHAPE, LORA_ERR_NULL, LORA_ERR_ALIGN,
+ * LORA_ERR_HIP. */
+lora_status lora_ce_scale_grad(int64_t M, int64_t K, const float* g, const void* dX, void* out, void* stream);
 
 /* ---- RoPE on the attention projections' outputs ------------------------------------------
  * Tutorial ch. 5 §5.5 (fused RoPE: each coordinate pair of q and k multiplied by a 2 x 2 rotation,

@@ -9,17 +9,19 @@ namespace lora {
 
 int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile)); }
 
-// Number of N ranges per output tile (1..8, at least 8 steps of 64 each), minimising an
+// Number of N ranges per output tile (1..32, at least 8 steps of 64 each), minimising an
 // estimate in tile-steps (x 256): rounds of 256 resident workgroups x steps per unit, plus the
 // units' partials, each a 256 KB fp32 store that the tile's last unit reads back, at about 40
 // tile-steps per unit on each CU (measured on the QLoRA FFN input gradient, 320 tiles x 432
-// steps: S = 2, 3, 4, 8 took 1.13, 1.09, 1.15, 1.73 ms; a flat 4 steps per unit chose 4).
+// steps: S = 2, 3, 4, 8 took 1.13, 1.09, 1.15, 1.73 ms; a flat 4 steps per unit chose 4).  More
+// than 8 ranges only pay for a handful of tiles over a long N (a 256-token chunk of an LM head's
+// gradient: 16 tiles, 2000 steps, S = 16).
 int dx_splits(int64_t M, int64_t N, int64_t K, int R) {
   const int64_t tiles = dx_tiles(M, K), steps = N / kStep;
   int best = 1;
   (void)R;
   int64_t best_cost = ((tiles + 255) / 256) * steps * 256;
-  for (int64_t s = 2; s <= 8 && steps / s >= 8; ++s) {
+  for (int64_t s = 2; s <= 32 && steps / s >= 8; ++s) {
     const int64_t cost = ((tiles * s + 255) / 256) * ((steps + s - 1) / s) * 256 + 40 * tiles * s;
     if (cost < best_cost) best = (int)s, best_cost = cost;
   }

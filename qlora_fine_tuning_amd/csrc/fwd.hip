@@ -64,7 +64,8 @@ __device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stag
 // EPI (bf16 W only when not kEpiLora): kEpiSwiglu, N = 2 Nh stacked rows, Y = [G | U] (M x 2 Nh)
 // and H (M x Nh) out; kEpiCeStats, the logits X W^T of an LM head (no adapter): per-row (max, sum
 // of exp) of each wave's 128 columns into `stats`, the label's logit, and the fp32 logits
-// themselves into `logits` when that is set (the gradient pass then reads them).
+// themselves, split into high and low 16-bit planes, when `hi` is set (the gradient pass then
+// reads them).
 // FP4 (with INT4): the 4-bit weight is MXFP4, E2M1 codes in the same nibble layout and one E8M0
 // exponent byte per 32 k (the two bytes of a 64-k step sit where the int4 fp16 scale would).
 template <int RP, bool INT4, bool PANEL, int EPI, bool FP4 = false>
@@ -461,12 +462,15 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
         mx = mn;
       }
       if (g4 == 0 && m < M)
-        *reinterpret_cast<float2*>(ce.stats + 2 * ((size_t)(tn * 2 + wn) * M + m)) = make_float2(mx, sm);
+        *reinterpret_cast<float2*>(ce.stats + 2 * ((size_t)m * (2 * tiles_n) + tn * 2 + wn)) = make_float2(mx, sm);
       if (found) ce.lab_logit[m] = lv;  // the one lane in the grid holding the label's column
     }
     // the fp32 logits, staged through this wave's freed tile buffer in two 128 x 64 halves so that
-    // each row leaves in 256-byte segments; 16-byte chunk c of row r sits at slot c ^ (r & 15)
-    if (ce.logits != nullptr) {
+    // each row leaves in whole segments; 16-byte chunk c of row r sits at slot c ^ (r & 15).  A
+    // logit's 32 bits leave as two 16-bit halves, the high half into one plane and the low half
+    // into another (128-byte row segments each): the gradient pass then writes the bf16 gradient
+    // over the high plane in place, a dense M x N matrix, and no third buffer is needed.
+    if (ce.hi != nullptr) {
       float* const st = reinterpret_cast<float*>(stage);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -484,7 +488,16 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
           const int r = p * 4 + (lane >> 4), c = lane & 15;
           const f32x4 v = *reinterpret_cast<const f32x4*>(st + r * 64 + ((c ^ (r & 15)) << 2));
           const int n = nb + h * 64 + c * 4;
-          if (mw + r < M && n < N) *reinterpret_cast<f32x4*>(ce.logits + (size_t)(mw + r) * N + n) = v;
+          if (mw + r < M && n < N) {
+            const size_t o = (size_t)(mw + r) * N + n;
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = __float_as_uint(v[e]);
+            *reinterpret_cast<uint2*>(ce.hi + o) =
+                make_uint2((b[0] >> 16) | (b[1] & 0xffff0000u), (b[2] >> 16) | (b[3] & 0xffff0000u));
+            *reinterpret_cast<uint2*>(ce.lo + o) =
+                make_uint2((b[0] & 0xffffu) | (b[1] << 16), (b[2] & 0xffffu) | (b[3] << 16));
+          }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the next half is written
         __builtin_amdgcn_wave_barrier();
@@ -553,7 +566,7 @@ static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
 }
 
 // logits of an LM head (X W^T, bf16 W, no adapter) with the cross-entropy epilogue: per-row
-// statistics (a.ce.stats, a.ce.lab_logit) and, if a.ce.logits is set, the fp32 logits
+// statistics (a.ce.stats, a.ce.lab_logit) and, if a.ce.hi is set, the fp32 logits as 16-bit planes
 hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s) { return launch_fwd_rp<16, false, false, kEpiCeStats>(a, s); }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {

@@ -17,9 +17,10 @@ constexpr int kEpiLora = 0, kEpiSwiglu = 1, kEpiCeStats = 2;
 // cross-entropy epilogues over an LM head's logits
 struct CeArgs {
   const int32_t* labels = nullptr;  // [M] in [0, N)
-  float* stats = nullptr;           // [2 tiles_n][M] (max, sum of exp) per wave's 128 columns
+  float* stats = nullptr;           // [M][2 tiles_n] (max, sum of exp) per wave's 128 columns
   float* lab_logit = nullptr;       // [M] the label's logit
-  float* logits = nullptr;          // [M][N] fp32, or null
+  uint16_t* hi = nullptr;           // [M][N] high 16 bits of the fp32 logits, or null
+  uint16_t* lo = nullptr;           // [M][N] their low 16 bits
 };
 
 struct FwdArgs {
@@ -78,12 +79,17 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
 hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s);
 // cross-entropy reductions (ce.hip): lse and loss per row from the stats, their fixed-order sum,
 // and a 32-bit fill
-hipError_t launch_ce_reduce(const float* stats, const float* lab_logit, float* lse, float* loss, int P, int64_t M,
+// (the reduction also sets the label-logit slots back to NaN for the next chunk)
+hipError_t launch_ce_reduce(const float* stats, float* lab_logit, float* lse, float* loss, int P, int64_t M,
                             hipStream_t s);
-hipError_t launch_ce_sum(const float* loss, float* out, int64_t M, hipStream_t s);
-// dlogits = bf16(scale (exp(logits - lse) - onehot(label))) from the stored fp32 logits
-hipError_t launch_ce_grad(const float* logits, const float* lse, const int32_t* labels, uint16_t* dl, int64_t M,
+// out[0] = scale x the fixed-order sum of loss
+hipError_t launch_ce_sum(const float* loss, float* out, int64_t M, float scale, hipStream_t s);
+// dlogits = bf16(scale (exp(logits - lse) - onehot(label))) from the stored fp32 logits (16-bit
+// planes hi and lo), written over hi
+hipError_t launch_ce_grad(uint16_t* hi, const uint16_t* lo, const float* lse, const int32_t* labels, int64_t M,
                           int64_t V, float scale, hipStream_t s);
+// out = bf16(in x g[0]) over n bf16 values (g: one fp32 in device memory)
+hipError_t launch_scale_bf16(const uint16_t* in, uint16_t* out, int64_t n, const float* g, hipStream_t s);
 hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s);
 // ranks 33..64: G = dY B as a pass of its own (written to G), ahead of the input-gradient kernel,

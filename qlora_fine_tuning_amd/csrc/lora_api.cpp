@@ -582,25 +582,37 @@ lora_status mxfp4_decode_fwd(int64_t M, int64_t N, int64_t K, int32_t R, float s
 
 namespace {
 
-constexpr int64_t kCeDefaultChunk = 8192;
+// The default chunk keeps its fp32 logits (4 bytes per token and vocabulary word) within this
+// budget, in whole multiples of 256 tokens and never fewer than 256.
+constexpr size_t kCeLogitsBudget = (size_t)512 << 20;
+constexpr int64_t kCeChunkUnit = 256;
 constexpr int32_t kCeRank = 8;  // the input-gradient kernel runs with zero adapters of this rank
 
-int64_t ce_chunk(int64_t M, int64_t chunk) {
-  const int64_t c = chunk > 0 ? chunk : kCeDefaultChunk;
+int64_t ce_default_chunk(int64_t V) {
+  if (V <= 0) return kCeChunkUnit;
+  const int64_t c = (int64_t)(kCeLogitsBudget / ((size_t)V * 4)) / kCeChunkUnit * kCeChunkUnit;
+  return c < kCeChunkUnit ? kCeChunkUnit : c;
+}
+
+int64_t ce_chunk(int64_t M, int64_t V, int64_t chunk) {
+  const int64_t c = chunk > 0 ? chunk : ce_default_chunk(V);
   return M < c ? (M > 0 ? M : 1) : c;
 }
 
 lora_status check_ce(int64_t M, int64_t V, int64_t K, int64_t chunk) {
   if (M < 0 || M >= kMaxElems || chunk < 0) return LORA_ERR_SHAPE;
-  const int64_t C = ce_chunk(M, chunk);
+  const int64_t C = ce_chunk(M, V, chunk);
   return check_dims(C, V, K, kCeRank);  // V and K multiples of 64; the chunk's C x V below 2^31
 }
 
+// Per chunk: the (max, sum of exp) pairs, label logits and lse of its rows; with the gradient also
+// the zero adapters, the chunk's fp32 logits as a high and a low 16-bit plane (the gradient of the
+// logits is written over the high plane), and the input-gradient kernel's workspace.
 struct CeLayout {
-  size_t stats, lab, lse, azero, bzero, logits, dl, inner, total;
+  size_t stats, lab, lse, azero, bzero, hi, lo, inner, total;
 };
 CeLayout ce_layout(int64_t M, int64_t V, int64_t K, int64_t chunk, bool grad) {
-  const int64_t C = ce_chunk(M, chunk);
+  const int64_t C = ce_chunk(M, V, chunk);
   const int64_t P = 2 * ((V + 255) / 256);  // partials per row: one per wave's 128 columns
   CeLayout l{};
   l.stats = 0;
@@ -610,9 +622,9 @@ CeLayout ce_layout(int64_t M, int64_t V, int64_t K, int64_t chunk, bool grad) {
   if (grad) {
     l.azero = l.total;
     l.bzero = l.azero + align256((size_t)kCeRank * K * 2);
-    l.logits = l.bzero + align256((size_t)V * kCeRank * 2);
-    l.dl = l.logits + align256((size_t)C * V * 4);
-    l.inner = l.dl + align256((size_t)C * V * 2);
+    l.hi = l.bzero + align256((size_t)V * kCeRank * 2);
+    l.lo = l.hi + align256((size_t)C * V * 2);
+    l.inner = l.lo + align256((size_t)C * V * 2);
     // the input-gradient workspace of a full chunk and of the last, shorter one (whose split
     // of V may differ)
     const int64_t tail = M % C;
@@ -630,13 +642,15 @@ CeLayout ce_layout(int64_t M, int64_t V, int64_t K, int64_t chunk, bool grad) {
 
 extern "C" {
 
+int64_t lora_ce_default_chunk(int64_t V) { return ce_default_chunk(V); }
+
 size_t lora_ce_workspace_bytes(int64_t M, int64_t V, int64_t K, int64_t chunk, int32_t grad) {
   if (check_ce(M, V, K, chunk) != LORA_OK) return 0;
   return ce_layout(M, V, K, chunk, grad != 0).total;
 }
 
 lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_scale, const void* X, const void* W,
-                    const int32_t* labels, float* loss, float* loss_sum, void* dX, void* ws, size_t ws_bytes,
+                    const int32_t* labels, float* loss, float* loss_total, void* dX, void* ws, size_t ws_bytes,
                     void* stream) {
   lora_status st = check_ce(M, V, K, chunk);
   if (st != LORA_OK) return st;
@@ -645,50 +659,65 @@ lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_s
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(X, labels, loss)) != LORA_OK) return st;
   if (dX != nullptr && !aligned16(dX)) return LORA_ERR_ALIGN;
-  if (loss_sum != nullptr && !aligned16(loss_sum)) return LORA_ERR_ALIGN;
+  if (loss_total != nullptr && !aligned16(loss_total)) return LORA_ERR_ALIGN;
   const bool grad = dX != nullptr;
   const CeLayout lay = ce_layout(M, V, K, chunk, grad);
   if (M > 0 && (ws == nullptr || ws_bytes < lay.total)) return LORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return LORA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  const int64_t C = ce_chunk(M, chunk);
+  const int64_t C = ce_chunk(M, V, chunk);
   const int P = (int)(2 * ((V + 255) / 256));
+  float* stats = reinterpret_cast<float*>(base + lay.stats);
+  float* lab = reinterpret_cast<float*>(base + lay.lab);
+  float* lse = reinterpret_cast<float*>(base + lay.lse);
+  uint16_t* hi = grad ? reinterpret_cast<uint16_t*>(base + lay.hi) : nullptr;
+  uint16_t* lo = grad ? reinterpret_cast<uint16_t*>(base + lay.lo) : nullptr;
   hipError_t e = hipSuccess;
-  if (M > 0 && grad) {
-    e = launch_fill_u32(base + lay.azero, lay.logits - lay.azero, 0u, s);  // the zero adapters
+  if (M > 0) {
+    // a label outside [0, V) is never found: its slot keeps NaN and so does its loss (every
+    // reduction puts NaN back for the next chunk)
+    e = launch_fill_u32(lab, (size_t)C * 4, 0x7fc00000u, s);
     if (e != hipSuccess) return from_hip(e);
+    if (grad) {
+      e = launch_fill_u32(base + lay.azero, lay.hi - lay.azero, 0u, s);  // the zero adapters
+      if (e != hipSuccess) return from_hip(e);
+    }
   }
   for (int64_t c0 = 0; c0 < M; c0 += C) {
     const int64_t Mc = (M - c0 < C) ? M - c0 : C;
-    float* stats = reinterpret_cast<float*>(base + lay.stats);
-    float* lab = reinterpret_cast<float*>(base + lay.lab);
-    float* lse = reinterpret_cast<float*>(base + lay.lse);
-    // a label outside [0, V) is never found: its slot keeps NaN and so does its loss
-    e = launch_fill_u32(lab, (size_t)Mc * 4, 0x7fc00000u, s);
-    if (e != hipSuccess) return from_hip(e);
     FwdArgs a{static_cast<const uint16_t*>(X) + c0 * K, W, nullptr, nullptr, nullptr, nullptr, nullptr, Mc, V, K,
               kCeRank, grad_scale};
     a.ce.labels = labels + c0;
     a.ce.stats = stats;
     a.ce.lab_logit = lab;
-    a.ce.logits = grad ? reinterpret_cast<float*>(base + lay.logits) : nullptr;
+    a.ce.hi = hi;
+    a.ce.lo = lo;
     e = launch_ce_logits(a, s);
     if (e != hipSuccess) return from_hip(e);
     e = launch_ce_reduce(stats, lab, lse, loss + c0, P, Mc, s);
     if (e != hipSuccess) return from_hip(e);
     if (!grad) continue;
-    // dlogits = grad_scale (softmax - onehot) from the stored fp32 logits, then dX = dlogits W
-    e = launch_ce_grad(a.ce.logits, lse, labels + c0, reinterpret_cast<uint16_t*>(base + lay.dl), Mc, V, grad_scale,
-                       s);
+    // dlogits = grad_scale (softmax - onehot) over the high plane, then dX = dlogits W
+    e = launch_ce_grad(hi, lo, lse, labels + c0, Mc, V, grad_scale, s);
     if (e != hipSuccess) return from_hip(e);
-    st = bwd_dx_common(false, LORA_BF16, Mc, V, K, kCeRank, 0.f, base + lay.dl, W, nullptr, base + lay.azero,
-                       base + lay.bzero, static_cast<uint16_t*>(dX) + c0 * K, base + lay.inner,
-                       ws_bytes - lay.inner, stream);
+    st = bwd_dx_common(false, LORA_BF16, Mc, V, K, kCeRank, 0.f, hi, W, nullptr, base + lay.azero, base + lay.bzero,
+                       static_cast<uint16_t*>(dX) + c0 * K, base + lay.inner, ws_bytes - lay.inner, stream);
     if (st != LORA_OK) return st;
   }
-  if (loss_sum != nullptr) return from_hip(launch_ce_sum(loss, loss_sum, M, s));
+  if (loss_total != nullptr) return from_hip(launch_ce_sum(loss, loss_total, M, grad_scale, s));
   return LORA_OK;
+}
+
+lora_status lora_ce_scale_grad(int64_t M, int64_t K, const float* g, const void* dX, void* out, void* stream) {
+  if (M < 0 || K <= 0 || K % 8 != 0 || M >= kMaxElems || K >= kMaxElems || M * K >= kMaxElems) return LORA_ERR_SHAPE;
+  if (g == nullptr) return LORA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(g) & 3u) != 0) return LORA_ERR_ALIGN;
+  if (M == 0) return LORA_OK;
+  const lora_status st = check_ptrs(dX, out);
+  if (st != LORA_OK) return st;
+  return from_hip(launch_scale_bf16(static_cast<const uint16_t*>(dX), static_cast<uint16_t*>(out), M * K, g,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -51,6 +51,8 @@ SIGNATURES = {
     "mxfp4_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "mxfp4_decode_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "lora_ce_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
+    "lora_ce_default_chunk": (_i64, [_i64]),
+    "lora_ce_scale_grad": (_i32, [_i64, _i64, _p, _p, _p, _p]),
     "lora_ce": (_i32, [_i64, _i64, _i64, _i64, _f32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "lora_rope": (_i32, [_i64, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
     "qlora_swiglu_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 11 + [_sz, _p]),
@@ -522,11 +524,16 @@ def lora_ce_workspace_bytes(M: int, V: int, K: int, chunk: int = 0, grad: bool =
     return int(load().lora_ce_workspace_bytes(M, V, K, chunk, int(grad)))
 
 
+def lora_ce_default_chunk(V: int) -> int:
+    return int(load().lora_ce_default_chunk(V))
+
+
 def lora_ce(X, W, labels, *, grad: bool = True, grad_scale: Optional[float] = None, chunk: int = 0, loss=None,
             dX=None, ws=None, stream=None):
     """Cross-entropy of the logits X W^T (X: M x K bf16, W: the V x K bf16 LM head, labels: M int32) in
-    chunks of tokens.  Returns (loss_sum (1,) fp32, loss (M,) fp32, dX (M x K bf16) or None); dX is the
-    gradient of grad_scale * loss_sum (grad_scale defaults to 1/M, the mean loss)."""
+    chunks of tokens.  Returns (loss_total (1,) fp32 = grad_scale * the sum of the losses, loss (M,) fp32,
+    dX (M x K bf16) or None), dX being the gradient of loss_total (grad_scale defaults to 1/M: the mean
+    loss)."""
     lib = load()
     _want(X, "X", torch.bfloat16)
     _want(W, "W", torch.bfloat16)
@@ -538,37 +545,49 @@ def lora_ce(X, W, labels, *, grad: bool = True, grad_scale: Optional[float] = No
         grad_scale = 1.0 / max(M, 1)
     if loss is None:
         loss = torch.empty(M, dtype=torch.float32, device=dev)
-    loss_sum = torch.empty(4, dtype=torch.float32, device=dev)
+    loss_total = torch.empty(4, dtype=torch.float32, device=dev)
     if grad and dX is None:
         dX = torch.empty_like(X)
     if not grad:
         dX = None
     if ws is None:
         ws = torch.empty(max(lora_ce_workspace_bytes(M, V, K, chunk, grad), 256), dtype=torch.uint8, device=dev)
-    st = lib.lora_ce(M, V, K, chunk, float(grad_scale), _ptr(X), _ptr(W), _ptr(labels), _ptr(loss), _ptr(loss_sum),
-                     _ptr(dX), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    st = lib.lora_ce(M, V, K, chunk, float(grad_scale), _ptr(X), _ptr(W), _ptr(labels), _ptr(loss),
+                     _ptr(loss_total), _ptr(dX), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("lora_ce", st)
-    return loss_sum[:1], loss, dX
+    return loss_total[:1], loss, dX
+
+
+def lora_ce_scale_grad(dX, g, *, out=None, stream=None):
+    """out = bf16(dX * g) with g a one-element fp32 device tensor (read on the device)."""
+    lib = load()
+    _want(dX, "dX", torch.bfloat16)
+    if g.dtype != torch.float32 or g.numel() != 1 or g.device != dX.device:
+        raise ValueError("g: one fp32 value on dX's device")
+    g = g.reshape(1).contiguous()
+    M, K = dX.shape
+    if out is None:
+        out = torch.empty_like(dX)
+    _check("lora_ce_scale_grad", lib.lora_ce_scale_grad(M, K, _ptr(g), _ptr(dX), _ptr(out), _stream(stream)))
+    return out
 
 
 class LMHeadCrossEntropyFunction(torch.autograd.Function):
     """Mean cross-entropy of the logits X W^T with W frozen: the forward runs the chunked loss and
     gradient together (the gradient of the logits is never kept past its chunk) and saves dX; the
-    backward returns it (scaled by the upstream gradient unless that is 1)."""
+    backward scales it by the upstream gradient on the device."""
 
     @staticmethod
     def forward(ctx, X, W, labels, chunk=0):
         M = X.shape[0]
-        loss_sum, _, dX = lora_ce(X, W, labels, grad=True, grad_scale=1.0 / max(M, 1), chunk=chunk)
+        loss_total, _, dX = lora_ce(X, W, labels, grad=True, grad_scale=1.0 / max(M, 1), chunk=chunk)
         ctx.save_for_backward(dX)
-        return loss_sum[0] / max(M, 1)
+        return loss_total[0]
 
     @staticmethod
     def backward(ctx, g):
         (dX,) = ctx.saved_tensors
-        if not torch.equal(g, torch.ones_like(g)):
-            dX = (dX.float() * g).to(dX.dtype)
-        return dX, None, None, None
+        return lora_ce_scale_grad(dX, g.float()), None, None, None
 
 
 def lora_rope(Q, K, positions, base: float, *, rot: Optional[int] = None, inverse: bool = False, stream=None):

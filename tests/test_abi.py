@@ -321,11 +321,11 @@ def test_mxfp4_decode_workspace_matches_qlora_decode(lib):
 # ---- Cross-entropy over an LM head ------------------------------------------------------
 
 def ce_call(lib, M=64, V=1024, K=256, chunk=0, gs=1.0, ws=P, ws_bytes=None, **ptrs):
-    p = dict(X=P, W=P, labels=P, loss=P, loss_sum=P, dX=P)
+    p = dict(X=P, W=P, labels=P, loss=P, loss_total=P, dX=P)
     p.update(ptrs)
     if ws_bytes is None:
         ws_bytes = lib.lora_ce_workspace_bytes(M, V, K, chunk, 1)
-    return lib.lora_ce(M, V, K, chunk, gs, p["X"], p["W"], p["labels"], p["loss"], p["loss_sum"], p["dX"], ws,
+    return lib.lora_ce(M, V, K, chunk, gs, p["X"], p["W"], p["labels"], p["loss"], p["loss_total"], p["dX"], ws,
                        ws_bytes, None)
 
 
@@ -333,26 +333,59 @@ def ce_call(lib, M=64, V=1024, K=256, chunk=0, gs=1.0, ws=P, ws_bytes=None, **pt
     (dict(V=100), 2), (dict(K=96), 2), (dict(M=-1), 2), (dict(chunk=-1), 2),
     (dict(gs=float("nan")), 8),
     (dict(X=NUL), 1), (dict(W=NUL), 1), (dict(labels=NUL), 1), (dict(loss=NUL), 1),
-    (dict(dX=MIS), 4), (dict(loss_sum=MIS), 4), (dict(ws=MIS), 4),
+    (dict(dX=MIS), 4), (dict(loss_total=MIS), 4), (dict(ws=MIS), 4),
     (dict(ws=NUL), 6), (dict(ws_bytes=1024), 6),
 ])
 def test_lora_ce_validation(lib, kw, code):
     assert ce_call(lib, **kw) == code
 
 
+def test_lora_ce_default_chunk(lib):
+    # the largest multiple of 256 tokens whose fp32 logits fit in 512 MiB, at least 256
+    budget = 512 << 20
+    for V in (64, 32000, 128000, 152064, 600000, 1 << 20):
+        c = lib.lora_ce_default_chunk(V)
+        assert c % 256 == 0 and c >= 256
+        assert c * V * 4 <= budget or c == 256
+        assert (c + 256) * V * 4 > budget
+    assert lib.lora_ce_default_chunk(128000) == 1024 and lib.lora_ce_default_chunk(152064) == 768
+
+
 def test_lora_ce_workspace(lib):
     # per chunk: (max, sum) per row and 128 columns, the label logits and lse; with the gradient
-    # also the zero adapters, the chunk's bf16 gradient of the logits and the input-gradient
-    # workspace of the full and the last chunk
-    M, V, K, C = 16384, 128000, 4096, 8192
+    # also the zero adapters, the chunk's fp32 logits as two 16-bit planes (the bf16 gradient of the
+    # logits overwrites the high one) and the input-gradient workspace of the full and the last chunk
+    M, V, K = 16384, 128000, 4096
+    C = lib.lora_ce_default_chunk(V)
     pad = lambda b: (b + 255) // 256 * 256
     loss_only = pad(1000 * C * 8) + pad(C * 4) + pad(C * 4)
     assert lib.lora_ce_workspace_bytes(M, V, K, 0, 0) == loss_only
-    full = (loss_only + pad(8 * K * 2) + pad(V * 8 * 2) + pad(C * V * 4) + pad(C * V * 2)
+    full = (loss_only + pad(8 * K * 2) + pad(V * 8 * 2) + 2 * pad(C * V * 2)
             + lib.lora_bwd_workspace_bytes(1, C, V, K, 8))
     assert lib.lora_ce_workspace_bytes(M, V, K, 0, 1) == full
-    assert full < 6.5e9  # the chunk's fp32 logits and bf16 gradient: 4.2 + 2.1 GB
+    assert full < 0.7e9  # the default chunk's fp32 logits are 524 MB whatever M is
+    assert lib.lora_ce_workspace_bytes(4 * M, V, K, 0, 1) == full
+    # an explicit chunk, with a shorter last chunk whose input-gradient split may differ
+    full256 = lib.lora_ce_workspace_bytes(M + 100, V, K, 256, 1)
+    assert full256 >= pad(1000 * 256 * 8) + 2 * pad(256 * V * 2) + lib.lora_bwd_workspace_bytes(1, 100, V, K, 8)
+    assert full256 < 0.3e9
     assert lib.lora_ce_workspace_bytes(M, 100, K, 0, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 2), (dict(K=0), 2), (dict(K=12), 2), (dict(M=1 << 31), 2),
+    (dict(g=NUL), 1), (dict(dX=NUL), 1), (dict(out=NUL), 1),
+    (dict(dX=MIS), 4), (dict(out=MIS), 4),
+])
+def test_lora_ce_scale_grad_validation(lib, kw, code):
+    p = dict(M=64, K=256, g=P, dX=P, out=P)
+    p.update(kw)
+    assert lib.lora_ce_scale_grad(p["M"], p["K"], p["g"], p["dX"], p["out"], None) == code
+
+
+def test_lora_ce_scale_grad_g_alignment(lib):
+    assert lib.lora_ce_scale_grad(64, 256, 0x10002, P, P, None) == 4
+    assert lib.lora_ce_scale_grad(0, 256, P, None, None, None) == 0  # nothing to scale
 
 
 # ---- RoPE ---------------------------------------------------------------------------------
