@@ -65,7 +65,8 @@ typedef enum lora_status {
   LORA_ERR_HIP = 9        /* a HIP launch failed; lora_last_hip_error() names it */
 } lora_status;
 
-/* Element type of X, W, A, B, Y, dY and dX.  dA, dB, XA and G are always fp32. */
+/* Element type of X, W, A, B, Y, dY and dX.  dA, dB, XA and G are always fp32.  The entry points
+ * take it as an int32_t `dt` holding one of these values (any other value is LORA_ERR_DTYPE). */
 typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
 
 /* Forward: Y = X W^T + scale (X A^T) B^T  (tutorial ch. 5, §5.3: one kernel per output tile
@@ -76,7 +77,7 @@ typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
  * For R > 32 (bf16) with XA given, X A^T is computed by a pass of its own ahead of the main
  * kernel, which parks its partial sums in Y before overwriting Y; with XA NULL the main
  * kernel computes it (correct, but slower at that rank). */
-lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_fwd(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                      const void* X, const void* W, const void* A, const void* B,
                      void* Y, float* XA, void* stream);
 
@@ -86,7 +87,7 @@ lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
  * most 2048); for bf16, the input gradient's split partials (when its output has few tiles);
  * and, for R > 32, the scratch of its G = dY B pass.  The workspace needs no initialisation:
  * calls clear what they use. */
-size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R);
+size_t lora_bwd_workspace_bytes(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R);
 
 /* Backward with W frozen (tutorial ch. 5, §5.3, fused backward; hand-derived gradients):
  *   dX = dY W + scale (dY B) A,  dA = scale (dY B)^T X,  dB = scale dY^T XA.
@@ -94,7 +95,7 @@ size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, 
  *   XA [M][R] fp32 as saved by lora_fwd                             (input)
  *   dX [M][K] of type `dt`; dA [R][K] fp32; dB [N][R] fp32           (outputs)
  *   ws: device workspace of at least lora_bwd_workspace_bytes() bytes. */
-lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_bwd(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                      const void* dY, const void* X, const void* W, const void* A, const void* B,
                      const float* XA, void* dX, float* dA, float* dB,
                      void* ws, size_t ws_bytes, void* stream);
@@ -107,10 +108,10 @@ lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
  *                  lora_bwd_dx (or qlora_bwd_dx) with the same sizes.
  * Same argument meanings and workspace size as lora_bwd.  lora_bwd_dadb takes dt = LORA_BF16 for
  * the QLoRA path (its activations are bf16). */
-lora_status lora_bwd_dx(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_bwd_dx(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                         const void* dY, const void* W, const void* A, const void* B, void* dX,
                         void* ws, size_t ws_bytes, void* stream);
-lora_status lora_bwd_dadb(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_bwd_dadb(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                           const void* dY, const void* X, const float* XA, float* dA, float* dB,
                           void* ws, size_t ws_bytes, void* stream);
 
@@ -381,8 +382,9 @@ lora_status lora_rope(int64_t M, int32_t H, int32_t Hk, int32_t D, int32_t rot, 
  * LORA_ERR_NULL, LORA_ERR_ALIGN, LORA_ERR_VALUE (ticks), LORA_ERR_HIP. */
 lora_status lora_probe_sclk(uint64_t* out, uint32_t ticks, void* stream);
 
-/* Human-readable name of a status code (static storage). */
-const char* lora_status_str(lora_status s);
+/* Human-readable name of a status code, a lora_status value held in an int32_t (static storage;
+ * "unknown lora_status" for any other value). */
+const char* lora_status_str(int32_t s);
 
 /* Name of the HIP error behind the last LORA_ERR_HIP on the calling thread (static storage). */
 const char* lora_last_hip_error(void);

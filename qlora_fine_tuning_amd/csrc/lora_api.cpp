@@ -231,8 +231,9 @@ lora_status swiglu_bwd_impl(int fmt, int64_t M, int64_t N, int64_t K, int32_t R,
 
 extern "C" {
 
-const char* lora_status_str(lora_status st) {
-  switch (st) {
+const char* lora_status_str(int32_t code) {
+  if (code < LORA_OK || code > LORA_ERR_HIP) return "unknown lora_status";
+  switch (static_cast<lora_status>(code)) {
     case LORA_OK: return "LORA_OK";
     case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
     case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: M < 0, N or K not a positive multiple of 64, or a tensor too large";
@@ -249,7 +250,7 @@ const char* lora_status_str(lora_status st) {
 
 const char* lora_last_hip_error(void) { return g_last_hip_error; }
 
-lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_fwd(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                      const void* X, const void* W, const void* A, const void* B, void* Y, float* XA,
                      void* stream) {
   if (dt != LORA_F32 && dt != LORA_BF16) return LORA_ERR_DTYPE;
@@ -267,13 +268,13 @@ lora_status lora_fwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
   return from_hip(dt == LORA_F32 ? launch_fwd_f32(a, s) : launch_fwd_mfma(a, false, s));
 }
 
-size_t lora_bwd_workspace_bytes(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R) {
+size_t lora_bwd_workspace_bytes(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R) {
   if (dt != LORA_F32 && dt != LORA_BF16) return 0;
   if (check_dims(M, N, K, R) != LORA_OK) return 0;
   return bwd_layout(M, N, K, R, dt != LORA_F32).total;
 }
 
-lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_bwd(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                      const void* dY, const void* X, const void* W, const void* A, const void* B,
                      const float* XA, void* dX, float* dA, float* dB, void* ws, size_t ws_bytes,
                      void* stream) {
@@ -284,12 +285,13 @@ lora_status lora_bwd(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, 
   st = check_ptrs(W, A, B, dA, dB);
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, X, XA, dX)) != LORA_OK) return st;
-  st = bwd_dx_common(false, dt, M, N, K, R, scale, dY, W, nullptr, A, B, dX, ws, ws_bytes, stream);
+  st = bwd_dx_common(false, static_cast<lora_dtype>(dt), M, N, K, R, scale, dY, W, nullptr, A, B, dX, ws, ws_bytes,
+                     stream);
   if (st != LORA_OK) return st;
-  return bwd_dadb_common(dt, M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
+  return bwd_dadb_common(static_cast<lora_dtype>(dt), M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
 }
 
-lora_status lora_bwd_dx(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_bwd_dx(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                         const void* dY, const void* W, const void* A, const void* B, void* dX,
                         void* ws, size_t ws_bytes, void* stream) {
   if (dt != LORA_F32 && dt != LORA_BF16) return LORA_ERR_DTYPE;
@@ -299,10 +301,11 @@ lora_status lora_bwd_dx(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t 
   st = check_ptrs(W, A, B);
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, dX)) != LORA_OK) return st;
-  return bwd_dx_common(false, dt, M, N, K, R, scale, dY, W, nullptr, A, B, dX, ws, ws_bytes, stream);
+  return bwd_dx_common(false, static_cast<lora_dtype>(dt), M, N, K, R, scale, dY, W, nullptr, A, B, dX, ws, ws_bytes,
+                       stream);
 }
 
-lora_status lora_bwd_dadb(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
+lora_status lora_bwd_dadb(int32_t dt, int64_t M, int64_t N, int64_t K, int32_t R, float scale,
                           const void* dY, const void* X, const float* XA, float* dA, float* dB,
                           void* ws, size_t ws_bytes, void* stream) {
   if (dt != LORA_F32 && dt != LORA_BF16) return LORA_ERR_DTYPE;
@@ -312,7 +315,7 @@ lora_status lora_bwd_dadb(lora_dtype dt, int64_t M, int64_t N, int64_t K, int32_
   st = check_ptrs(dA, dB);
   if (st != LORA_OK) return st;
   if (M > 0 && (st = check_ptrs(dY, X, XA)) != LORA_OK) return st;
-  return bwd_dadb_common(dt, M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
+  return bwd_dadb_common(static_cast<lora_dtype>(dt), M, N, K, R, scale, dY, X, XA, dA, dB, ws, ws_bytes, stream);
 }
 
 lora_status qlora_quantize(int64_t N, int64_t K, int32_t group, const float* W, uint8_t* Wq,

@@ -13,7 +13,8 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblora_mi355x.so")
+# QLORA_AMD_LIB may name another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("QLORA_AMD_LIB") or os.path.join(_PKG, "liblora_mi355x.so")
 
 LORA_F32, LORA_BF16 = 0, 1
 GROUP = 64

@@ -47,6 +47,8 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     for code, name in lora.STATUS.items():
         assert lib.lora_status_str(code).decode().startswith(name)
+    for code in (-1, 10, 1 << 30):
+        assert lib.lora_status_str(code).decode() == "unknown lora_status"
 
 
 # Fake, 16-byte aligned, never dereferenced: validation fails before any HIP call.
