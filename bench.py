@@ -420,6 +420,40 @@ def bench_decode(lora, torch, dev, reps, copies=6):
     return out
 
 
+def measure_ceilings(lora, torch, dev, stream, iters=4000, read_mb=96, copies=6, reads=30):
+    """The chip's practical ceilings, measured after the timed steps: the bf16 MFMA rate when
+    every SIMD issues nothing but independent MFMAs (the chip's own power and clock limits set the
+    clock), and the streaming-read rate over buffers larger than the 256 MB last-level cache."""
+    out = None
+    for _ in range(2):  # the second run is reported
+        out = lora.lora_probe_mfma(256, iters, stream=stream)
+        torch.cuda.synchronize()
+    d = out.cpu().numpy().astype(np.float64)
+    us = d[:, 1] / 100.0
+    mfmas = 64.0 * iters
+    tflops = float((mfmas * 16384.0 / us).sum() / 1e6)
+    bufs = [torch.zeros(read_mb << 20, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for b in bufs:
+        lora.lora_probe_hbm_read(b, sink, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reads):
+        lora.lora_probe_hbm_read(bufs[i % copies], sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tbs = reads * (read_mb << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del bufs
+    return {"mfma_bf16_TFLOP/s": round(tflops, 1), "mfma_frac_of_nominal_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "mfma_clock_MHz": round(float(np.median(d[:, 0] / us)), 1),
+            "cycles_per_mfma": round(float(np.median(d[:, 0] / mfmas)), 2),
+            "hbm_read_TB/s": round(tbs, 3), "hbm_read_frac_of_peak": round(tbs / (PEAK_HBM_GBS / 1000), 4),
+            "how": "lora_probe_mfma: 256 workgroups x 4 waves, each 64 independent bf16 16x16x32 MFMAs into "
+                   f"AGPRs per block, {iters} blocks, nothing else issued; lora_probe_hbm_read: {reads} reads of "
+                   f"{copies} rotating {read_mb} MiB buffers, 1 KB contiguous per wave load"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,6 +555,9 @@ def main(argv=None):
             "how": "shader-cycle counter against the 100 MHz real-time counter over a 20 us spin enqueued "
                    "right after the last timed step"}
 
+    ceilings = measure_ceilings(lora, torch, dev, stream)
+    roofline["frac_of_measured_mfma_ceiling"] = round(ach / ceilings["mfma_bf16_TFLOP/s"], 4)
+
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -533,6 +570,7 @@ def main(argv=None):
         "step_ms": step_stats,
         "sclk": sclk,
         "roofline": roofline,
+        "ceilings": ceilings,
     }
     if not args.no_secondary:
         lines = {"mlp": lambda: bench_mlp(lora, torch, dev, 20),
@@ -546,6 +584,8 @@ def main(argv=None):
                  "torch_unfused": lambda: bench_torch_unfused(torch, X, W, A, B, dY, inp.scale, 20)}
         only = set(args.only.split(",")) if args.only else None
         result["secondary"] = {k: f() for k, f in lines.items() if only is None or k in only}
+        for row in result["secondary"].get("decode", []):
+            row["frac_hbm_read_ceiling"] = round(row["GB/s"] / (ceilings["hbm_read_TB/s"] * 1000), 4)
     if args.calib_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -382,6 +382,23 @@ lora_status lora_rope(int64_t M, int32_t H, int32_t Hk, int32_t D, int32_t rot, 
  * LORA_ERR_NULL, LORA_ERR_ALIGN, LORA_ERR_VALUE (ticks), LORA_ERR_HIP. */
 lora_status lora_probe_sclk(uint64_t* out, uint32_t ticks, void* stream);
 
+/* The matrix-core ceiling under the chip's own power and clock limits (measurement support):
+ * `blocks` workgroups of four waves (one per SIMD) each issue `iters` blocks of 64 independent
+ * bf16 16x16x32 MFMAs with nothing in between.  Wave w writes out[3w] (shader cycles),
+ * out[3w + 1] (100 MHz real-time ticks) and out[3w + 2] (a value that keeps its results live);
+ * 64 x iters x 16384 FLOP per wave over its real time is the rate a bf16 GEMM cannot beat on
+ * this chip.  out: device memory of 12 x blocks uint64, 8-byte aligned; blocks in [1, 65536],
+ * iters in [1, 10^6].  Errors: LORA_ERR_NULL, LORA_ERR_ALIGN, LORA_ERR_VALUE, LORA_ERR_HIP. */
+lora_status lora_probe_mfma(uint64_t* out, int32_t blocks, uint32_t iters, void* stream);
+
+/* The streaming-read ceiling (measurement support): reads `bytes` of device memory at `buf`
+ * once, 1 KB contiguous per wave load instruction, and writes nothing in practice (`sink`, one
+ * device uint32, is written only if the folded words equal a fixed constant; a zero-filled buffer
+ * folds to 0).  Time it with events over buffers larger than the 256 MB last-level cache.  buf
+ * 16-byte aligned, bytes a positive multiple of 16.  Errors: LORA_ERR_NULL, LORA_ERR_ALIGN,
+ * LORA_ERR_VALUE, LORA_ERR_HIP. */
+lora_status lora_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Human-readable name of a status code, a lora_status value held in an int32_t (static storage;
  * "unknown lora_status" for any other value). */
 const char* lora_status_str(int32_t s);

@@ -1,9 +1,20 @@
-// Diagnostics: the shader clock seen by a kernel, for the measurement harness.
+// Diagnostics for the measurement harness (not part of the layer).
 //
-// One workgroup of one wave reads the shader-cycle counter and the constant 100 MHz real-time
-// counter, spins until the real-time counter has advanced by `ticks` (10 ns each), and reads
-// both again.  The ratio of the two deltas is the average shader clock over the spin.  The
-// spin ends on the real-time counter alone, so it always finishes.
+//  * sclk_probe_kernel: the shader clock seen by a kernel.  One wave reads the shader-cycle
+//    counter and the constant 100 MHz real-time counter, spins until the real-time counter has
+//    advanced by `ticks` (10 ns each), and reads both again; the ratio of the deltas is the
+//    average shader clock over the spin.  The spin ends on the real-time counter alone.
+//  * mfma_rate_kernel: the matrix-core ceiling under the chip's own power limit.  Every wave
+//    (one per SIMD: 256 threads per workgroup, all registers of the SIMD) issues `iters` blocks
+//    of 64 independent v_mfma_f32_16x16x32_bf16 into 64 accumulators held in AGPRs, with no
+//    other instruction in between, and records its shader cycles and real-time ticks.  The
+//    MFMA rate it reaches bounds every bf16 GEMM on the same chip.
+//  * hbm_read_kernel: the streaming-read ceiling.  Each wave reads 1 KB contiguous per load
+//    instruction (16 bytes per lane), four loads in flight per thread, grid-stride over the
+//    buffer; the words are folded into a value that is stored only if it equals a fixed
+//    constant (a zero-filled buffer folds to 0), so the loads cannot be removed and, in
+//    practice, nothing is written.
+#include "common.hpp"
 #include "launch.hpp"
 
 namespace lora {
@@ -22,6 +33,66 @@ __global__ void __launch_bounds__(64) sclk_probe_kernel(unsigned long long* out,
 
 hipError_t launch_sclk_probe(unsigned long long* out, unsigned int ticks, hipStream_t s) {
   hipLaunchKernelGGL(sclk_probe_kernel, dim3(1), dim3(64), 0, s, out, ticks);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) mfma_rate_kernel(unsigned long long* out, unsigned int iters) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // operands: arbitrary finite bf16 patterns (small exponents), different per lane
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t x = 0x3f003f00u ^ ((uint32_t)(lane * 8 + i) * 0x00070007u & 0x007f007fu);
+    a[i] = (u32x4){x, x ^ 0x00010001u, x ^ 0x00020002u, x ^ 0x00030003u};
+    b[i] = (u32x4){x ^ 0x00040004u, x ^ 0x00050005u, x ^ 0x00060006u, x ^ 0x00070007u};
+  }
+  f32x4 acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = fzero4();
+  mfma_acc_ready(acc);
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (unsigned int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mfma16_acc(acc[i * 8 + j], a[i], b[j]);
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  mfma_drain(acc);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) s += acc[i][0];
+  if (lane == 0) {
+    const size_t w = (size_t)blockIdx.x * 4 + (tid >> 6);
+    out[3 * w + 0] = c1 - c0;
+    out[3 * w + 1] = r1 - r0;
+    out[3 * w + 2] = (unsigned long long)__float_as_uint(s);  // keeps the accumulators live
+  }
+}
+
+hipError_t launch_mfma_rate(unsigned long long* out, int blocks, unsigned int iters, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, iters);
+  return hipGetLastError();
+}
+
+constexpr uint32_t kReadMagic = 0x9e3779b9u;
+
+__global__ void __launch_bounds__(256)
+hbm_read_kernel(const u32x4* __restrict__ p, size_t n16, uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 v0 = p[i], v1 = p[i + stride], v2 = p[i + 2 * stride], v3 = p[i + 3 * stride];
+    acc ^= (v0[0] + v1[1]) ^ (v2[2] + v3[3]) ^ (v0[3] - v3[0]) ^ (v1[2] - v2[1]);
+  }
+  for (; i < n16; i += stride) acc ^= p[i][0] ^ p[i][2];
+  if (acc == kReadMagic) sink[0] = acc;
+}
+
+hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(2048), dim3(256), 0, s, static_cast<const u32x4*>(buf), n16, sink);
   return hipGetLastError();
 }
 

@@ -71,8 +71,10 @@ struct DadbArgs {
   int split_rows;  // tokens per split (the last split may be shorter)
 };
 
-// shader-clock probe (diag.hip)
+// diagnostics (diag.hip): shader clock, matrix-core rate, streaming-read rate
 hipError_t launch_sclk_probe(unsigned long long* out, unsigned int ticks, hipStream_t s);
+hipError_t launch_mfma_rate(unsigned long long* out, int blocks, unsigned int iters, hipStream_t s);
+hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // bf16 / int4 MFMA paths
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);

@@ -758,6 +758,21 @@ lora_status lora_probe_sclk(uint64_t* out, uint32_t ticks, void* stream) {
                                     static_cast<hipStream_t>(stream)));
 }
 
+lora_status lora_probe_mfma(uint64_t* out, int32_t blocks, uint32_t iters, void* stream) {
+  if (out == nullptr) return LORA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0) return LORA_ERR_ALIGN;
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > 1000000u) return LORA_ERR_VALUE;
+  return from_hip(launch_mfma_rate(reinterpret_cast<unsigned long long*>(out), blocks, iters,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+lora_status lora_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr) return LORA_ERR_NULL;
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return LORA_ERR_ALIGN;
+  if (bytes == 0 || bytes % 16 != 0) return LORA_ERR_VALUE;
+  return from_hip(launch_hbm_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---- The decode product without a caller workspace ----

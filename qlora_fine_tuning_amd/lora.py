@@ -59,6 +59,8 @@ SIGNATURES = {
     "qlora_swiglu_fwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 11 + [_sz, _p]),
     "qlora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 16 + [_sz, _p]),
     "lora_probe_sclk": (_i32, [_p, ctypes.c_uint32, _p]),
+    "lora_probe_mfma": (_i32, [_p, _i32, ctypes.c_uint32, _p]),
+    "lora_probe_hbm_read": (_i32, [_p, _sz, _p, _p]),
     "qlora_decode_status": (_i32, [_p, _sz, _p, _i32, _p]),
     "qlora_decode_fwd_noalloc": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]),
     "qlora_decode_set_hold": (_i32, [_p, _sz, _i32, _p]),
@@ -679,6 +681,23 @@ def lora_probe_sclk(ticks: int = 2000, *, out=None, stream=None) -> torch.Tensor
         out = torch.zeros(2, dtype=torch.int64, device="cuda")
     _check("lora_probe_sclk", lib.lora_probe_sclk(_ptr(out), int(ticks), _stream(stream)))
     return out
+
+
+def lora_probe_mfma(blocks: int = 256, iters: int = 2000, *, out=None, stream=None) -> torch.Tensor:
+    """Enqueue the matrix-core ceiling probe; returns the device tensor [waves, 3] (int64) of
+    (shader cycles, 100 MHz ticks, live value) per wave, to be read after the stream has run it."""
+    lib = load()
+    if out is None:
+        out = torch.zeros(blocks * 4, 3, dtype=torch.int64, device="cuda")
+    _check("lora_probe_mfma", lib.lora_probe_mfma(_ptr(out), int(blocks), int(iters), _stream(stream)))
+    return out
+
+
+def lora_probe_hbm_read(buf: torch.Tensor, sink: torch.Tensor, *, stream=None) -> None:
+    """Enqueue one streaming read of `buf` (its whole storage); `sink`: one int32 on the device."""
+    lib = load()
+    _check("lora_probe_hbm_read", lib.lora_probe_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                          _stream(stream)))
 
 
 def qlora_decode_status(ws: torch.Tensor, *, clear: bool = False, stream=None) -> int:

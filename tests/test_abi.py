@@ -463,3 +463,15 @@ def test_decode_noalloc_validation(lib):
     assert f(*args(X=None)) == 1 and f(*args(Y=None)) == 1 and f(*args(Ws=None)) == 1
     assert f(*args(XA=MIS)) == 4
     assert f(*args(M=8, N=1 << 20)) == 6
+
+
+def test_probe_mfma_and_hbm_read_validation(lib):
+    assert lib.lora_probe_mfma(None, 256, 10, None) == 1
+    assert lib.lora_probe_mfma(ctypes.c_void_p(0x10004), 256, 10, None) == 4
+    for blocks, iters in ((0, 10), (65537, 10), (256, 0), (256, 1000001)):
+        assert lib.lora_probe_mfma(P, blocks, iters, None) == 8
+    assert lib.lora_probe_hbm_read(None, 1024, P, None) == 1
+    assert lib.lora_probe_hbm_read(P, 1024, None, None) == 1
+    assert lib.lora_probe_hbm_read(MIS, 1024, P, None) == 4
+    assert lib.lora_probe_hbm_read(P, 1024, ctypes.c_void_p(0x10002), None) == 4
+    assert lib.lora_probe_hbm_read(P, 0, P, None) == 8 and lib.lora_probe_hbm_read(P, 1000, P, None) == 8
