@@ -48,6 +48,10 @@ __device__ __forceinline__ f32x4 ld_part(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCpolSc1);
 }
 
+// The bf16 instance of rank 16 loops over units (one resident workgroup per CU); the others keep
+// one unit per workgroup: with the loop around them the compiler fails or spills in the main loop.
+constexpr bool dx_persistent(int rp, bool int4) { return rp <= 16 && !int4; }
+
 // FP4 (with INT4): the 4-bit weight is MXFP4 (E2M1 codes, one E8M0 byte per 32 k; a thread's 64
 // codes are two blocks, whose two bytes sit where the int4 fp16 scale would).
 template <int RP, bool INT4, bool FP4 = false>
@@ -67,6 +71,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   // 16 accumulator blocks and B fragments do not fit next to the main tile's, and with them
   // the compiler spills and moves accumulators.
   constexpr bool PANEL = RP <= 32;
+  constexpr bool PERSIST = dx_persistent(RP, INT4);
   constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
   constexpr int TT = kTile * kStep;  // 16384 elements: dY tile 256 x 64, W tile 64 x 256
   constexpr int BT = kStep * RP;     // B tile: 64 rows (n) x RP ranks
@@ -75,18 +80,32 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   __shared__ __attribute__((aligned(1024))) uint16_t sD0[TT], sD1[TT], sW0[TT], sW1[TT];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[BTA], sB1[BTA];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tiles_m = (M + kTile - 1) / kTile, tiles_k = (K + kTile - 1) / kTile;
+  const int tiles = tiles_m * tiles_k;
+  const int units = tiles * splits;
+  // Persistent: one workgroup per CU walks the units the non-persistent launch would give the
+  // workgroups blockIdx, blockIdx + gridDim, ... (the grid a multiple of the 8 XCDs, so all run on
+  // this workgroup's XCD); those lie in one row of tiles and one split, so the rank panel
+  // G = dY B computed on the first of them is reused by the rest.
+  f32x4 pacc[NB][4];
+  int panel_tm = -1, panel_sp = -1;
+  auto unit_body = [&](int vb) {
+  int tid = (int)threadIdx.x;
+  // (the lane's values are derived afresh for every unit: hoisted out of the unit loop, the
+  // addresses computed from them would stay live across the main loop and be spilled)
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave >> 1, wm = wave & 1;
   const int l16 = lane & 15, g4 = lane >> 4;
-
-  const int tiles_m = (M + kTile - 1) / kTile, tiles_k = (K + kTile - 1) / kTile;
-  const int tiles = tiles_m * tiles_k;
   // unit -> (split, tile), split-major: units running together share operand panels in L2
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = xcd_remap(vb, units);
   const int sp = unit / tiles, tile = unit - sp * tiles;
   int tm, tk;
   grouped_tile(tile, tiles_m, tiles_k, 8, tm, tk);
+  const bool new_panel = PANEL && (!PERSIST || tm != panel_tm || sp != panel_sp);
+  panel_tm = tm;
+  panel_sp = sp;
   const int m0 = tm * kTile, k0 = tk * kTile;
   const int ntot = N / kStep;
   const int sbeg = sp * ntot / splits;  // this unit's N steps: [sbeg, sbeg + nsteps)
@@ -175,13 +194,15 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   };
 
   f32x4 acc[64];  // acc[i * 8 + j]: dX^T rows (k) block i, columns (m) block j
-  f32x4 pacc[NB][4];
 #pragma unroll
   for (int i = 0; i < 64; ++i) acc[i] = fzero4();
+  if (new_panel)
 #pragma unroll
-  for (int c = 0; c < NB; ++c)
+    for (int c = 0; c < NB; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
+      for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
+  // with (pan) or without the panel's MFMAs and B copies: only the first unit of a row and split
+  const bool pan = PERSIST ? new_panel : PANEL;
   if constexpr (ASM) mfma_acc_ready(acc);
 
   // transposing-read addresses: lane (l16, g4) reads rows 4 (l16 >> 2) + .. of its 16-lane
@@ -239,7 +260,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (PANEL) {
+    if constexpr (PANEL) if (pan) {  // wave-uniform
 #pragma unroll
       for (int c = 0; c < RP / 16; ++c) nx.b[c] = bfrag(b, kk, c);
       __builtin_amdgcn_sched_barrier(0);
@@ -260,8 +281,9 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       f.d[i] = ld16(d + lds_offf(wm * 128 + i * 16 + l16, ch));
     }
     if constexpr (PANEL)
+      if (pan)
 #pragma unroll
-      for (int c = 0; c < RP / 16; ++c) f.b[c] = bfrag(b, kk, c);
+        for (int c = 0; c < RP / 16; ++c) f.b[c] = bfrag(b, kk, c);
   };
   // wait for the copies of the next step: for int4 W, the three register loads issued after
   // them stay in flight
@@ -274,7 +296,8 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const int n0 = nbase + min(st, nsteps - 1) * kStep;
     dma_d(dn, n0);
     if constexpr (!INT4) dma_w(wn, n0);
-    if constexpr (PANEL) load_b(n0);
+    if constexpr (PANEL)
+      if (pan) load_b(n0);
     (void)bn;
   };
   // the same copies in 16 parts for phase(): the B rows first (a register load, waited for
@@ -283,7 +306,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   auto prefetch_part = [&](int q, int st, uint16_t* dn, uint16_t* wn) {
     const int n0 = nbase + min(st, nsteps - 1) * kStep;
     if constexpr (PANEL)
-      if (q == 0) load_b(n0);
+      if (pan && q == 0) load_b(n0);
     if (q < 8) {
       dma16(rD, dn + (4 * q + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)q * 32u * rowD);
     } else if constexpr (!INT4) {
@@ -295,12 +318,18 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   const NoCopy nocopy;
   auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch (bf16)
     (void)wn;
-    if constexpr (PANEL) store_b(bn);
-    else (void)bn;
+    if constexpr (PANEL) {
+      if (pan) store_b(bn);
+    } else {
+      (void)bn;
+    }
   };
   auto finish_b = [&](uint16_t* bn) {
-    if constexpr (PANEL) store_b(bn);
-    else (void)bn;
+    if constexpr (PANEL) {
+      if (pan) store_b(bn);
+    } else {
+      (void)bn;
+    }
   };
 
   // Same pipeline as the forward kernel (see there), over N steps of 64.
@@ -421,6 +450,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
         pacc[c][j] = t;
       }
     if (tid == 0) __hip_atomic_store(ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    panel_tm = -1;  // pacc now holds the sum over the splits, not this unit's share
   }
 
   // ---- epilogue: G panel -> LDS (and HBM once per row tile); A tile -> LDS ----
@@ -506,6 +536,15 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   uint16_t* const stage = wave == 0 ? sD0 : (wave == 1 ? sD1 : (wave == 2 ? sW0 : sW1));
   const int mw = m0 + wm * 128, kw = k0 + wk * 128;
   store_block_bf16(acc, stage, dX + (size_t)mw * K + kw, (size_t)K, M - mw, K - kw, lane);
+  };
+  if constexpr (PERSIST) {
+    for (int vb = blockIdx.x; vb < units; vb += gridDim.x) {
+      unit_body(vb);
+      __syncthreads();  // the next unit's copies reuse every wave's LDS
+    }
+  } else {
+    unit_body(blockIdx.x);
+  }
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {  // the split arrival counters
@@ -522,7 +561,9 @@ static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4, FP4>), dim3(tiles * splits), dim3(kThreads), 0, s,
+  const int units = tiles * splits, cus = device_cus() & ~7;  // a multiple of the 8 XCDs
+  const int grid = (dx_persistent(RP, INT4) && cus > 0 && units > cus) ? cus : units;
+  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4, FP4>), dim3(grid), dim3(kThreads), 0, s,
                      (const uint16_t*)a.dY, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.dX, a.G, (int)a.M, (int)a.N, (int)a.K,
                      (int)a.R, a.scale, splits, a.part, a.ctr);

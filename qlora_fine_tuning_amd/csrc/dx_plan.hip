@@ -7,6 +7,14 @@
 
 namespace lora {
 
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return kNormCUs;
+  return n;
+}
+
 int dx_tiles(int64_t M, int64_t K) { return (int)(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile)); }
 
 // Number of N ranges per output tile (1..32, at least 8 steps of 64 each), minimising an

@@ -68,6 +68,8 @@ __device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stag
 // reads them).
 // FP4 (with INT4): the 4-bit weight is MXFP4, E2M1 codes in the same nibble layout and one E8M0
 // exponent byte per 32 k (the two bytes of a 64-k step sit where the int4 fp16 scale would).
+constexpr bool fwd_persistent(int rp, int epi, bool int4) { return rp <= 16 && epi != kEpiSwiglu && !int4; }
+
 template <int RP, bool INT4, bool PANEL, int EPI, bool FP4 = false>
 __global__ void __launch_bounds__(kThreads)
 fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
@@ -76,6 +78,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 float* __restrict__ XA, uint16_t* __restrict__ H, CeArgs ce, int M, int N, int K, int R,
                 float scale) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu, CE = EPI >= kEpiCeStats, LORA = !CE;
+  constexpr bool PERSIST = fwd_persistent(RP, EPI, INT4);
   static_assert(!(CE && INT4), "the LM head takes a bf16 weight");
   static_assert(!(CE && PANEL), "the LM head has no adapter");
   constexpr int TT = kTile * kStep;  // elements of one 256 x 64 operand tile
@@ -86,15 +89,34 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   __shared__ __attribute__((aligned(1024))) uint16_t sX0[TT], sX1[TT], sW0[TT], sW1[TT];
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[AT], sA1[AT];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+
+  const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
+  // Persistent instances: one workgroup per CU walks the tiles the non-persistent launch would
+  // give the workgroups blockIdx, blockIdx + gridDim, ... (the grid a multiple of the 8 XCDs, so
+  // all of them run on this workgroup's XCD and keep its L2 footprint); in the grouped order those
+  // tiles lie in one row of tiles, so the rank panel X A^T computed on the first of them is reused
+  // by the rest.  (Only the bf16 instances of rank 16 and the LM head loop over tiles; the others
+  // keep one tile per workgroup: with the tile loop around them the compiler fails or spills
+  // inside the main loop.)
+  const int tiles = tiles_m * tiles_n;
+  constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
+  f32x4 pacc[NB][4];
+  int panel_tm = -1;
+  auto tile = [&](int vb) {
+  // The lane's values are derived afresh on every tile (through an opaque copy of the thread id):
+  // hoisted out of the tile loop, the addresses computed from them would stay live across the
+  // main loop, which has no registers to spare, and be spilled.
+  int tid = (int)threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wm = wave & 1;  // this wave's 128-row half of n and of m
   const int l16 = lane & 15, g4 = lane >> 4;
-
-  const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
   int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 8, tm, tn);
+  grouped_tile(xcd_remap(vb, tiles), tiles_m, tiles_n, 8, tm, tn);
   const int m0 = tm * kTile, n0 = tn * kTile;
+  const bool new_panel = PANEL && (!PERSIST || tm != panel_tm);
+  panel_tm = tm;
   const int nk = K / kStep;
   const uint32_t rowb = (uint32_t)K * 2;  // bytes per row of X, W (bf16) and A
 
@@ -201,15 +223,14 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   };
 
   f32x4 acc[64];  // acc[i * 8 + j]: Y^T rows (W) block i, columns (X) block j
-  constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
-  f32x4 pacc[NB][4];
 #pragma unroll
   for (int i = 0; i < 64; ++i) acc[i] = fzero4();
   mfma_acc_ready(acc);
+  if (new_panel)
 #pragma unroll
-  for (int c = 0; c < NB; ++c)
+    for (int c = 0; c < NB; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
+      for (int j = 0; j < 4; ++j) pacc[c][j] = fzero4();
 
   // adapter rows R .. AROWS-1 stay zero in both buffers
   if constexpr (PANEL)
@@ -229,7 +250,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   // (d = 2 i, 2 i + 1): spread out, the copies never hold up the wave's MFMA issue the way a
   // burst of 17 copies right after the barrier does.
   auto phase = [&](const Frag& cu, Frag& nx, const uint16_t* x, const uint16_t* w,
-                   const uint16_t* a, int kk, auto&& copy) {
+                   const uint16_t* a, int kk, bool pan, auto&& copy) {
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -253,7 +274,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (PANEL) {
+    if constexpr (PANEL) if (pan) {  // a wave-uniform branch: only the first tile of a row
 #pragma unroll
       for (int c = 0; c < RP / 16; ++c) nx.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
       __builtin_amdgcn_sched_barrier(0);
@@ -266,15 +287,16 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto read_frags = [&](Frag& f, const uint16_t* x, const uint16_t* w, const uint16_t* a, int kk) {
+  auto read_frags = [&](Frag& f, const uint16_t* x, const uint16_t* w, const uint16_t* a, int kk, bool pan) {
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) f.x[i] = ld16(x + lds_offf(wm * 128 + i * 16 + l16, ch));
 #pragma unroll
     for (int i = 0; i < 8; ++i) f.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
     if constexpr (PANEL)
+      if (pan)
 #pragma unroll
-      for (int c = 0; c < RP / 16; ++c) f.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
+        for (int c = 0; c < RP / 16; ++c) f.a[c] = ld16(a + lds_offf(c * 16 + l16, ch));
   };
   // wait for the copies of the next step: for int4 W, the four register loads issued after
   // them (two steps ahead) stay in flight
@@ -285,20 +307,21 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   };
   // Copies of step kn (clamped to the last step: a repeated copy of the last step into the
   // idle buffer is harmless and keeps the loop free of branches).
-  auto prefetch = [&](int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an) {
+  auto prefetch = [&](int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an, bool pan) {
     const int k1 = min(kn, nk - 1) * kStep;
     dma_tile(rX, xn, k1);
     if constexpr (!INT4)
 #pragma unroll
       for (int i = 0; i < 8; ++i) dma_w_part(wnx, k1, i);
-    if constexpr (PANEL) dma_a(an, k1);
+    if constexpr (PANEL)
+      if (pan) dma_a(an, k1);
   };
   // The same copies in 16 parts for phase(): the adapter rows first, then X rows 8d.. (d < 8),
   // W rows (bf16) or the int4 register loads.
-  auto prefetch_part = [&](int d, int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an) {
+  auto prefetch_part = [&](int d, int kn, uint16_t* xn, uint16_t* wnx, uint16_t* an, bool pan) {
     const int k1 = min(kn, nk - 1) * kStep;
     if constexpr (PANEL)
-      if (d == 0) dma_a(an, k1);
+      if (pan && d == 0) dma_a(an, k1);
     if (d < 8) {
       dma16(rX, xn + (4 * d + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)d * 32u * rowb);
     } else if constexpr (!INT4) {
@@ -313,8 +336,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   //   wait for the step kt+1 copies; barrier (everyone is done reading buffer b)
   //   start the copies of step kt+2 into buffer b
   //   read kk = 0 fragments of step kt+1  ||  MFMAs of kk = 1
+  // The main loop, with (pan) or without the rank panel's MFMAs and adapter copies
+  const bool pan = PERSIST ? new_panel : PANEL;  // one tile per workgroup: always
+  {
   Frag f0, f1;
-  prefetch(0, sX0, sW0, sA0);
+  prefetch(0, sX0, sW0, sA0, pan);
   if constexpr (INT4) {
     load_w4(w4a, 0);
     if constexpr (AHEAD) load_w4(w4b, 1);
@@ -322,8 +348,8 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   }
   wait_vmem();
   __syncthreads();
-  read_frags(f0, sX0, sW0, sA0, 0);
-  prefetch(1, sX1, sW1, sA1);
+  read_frags(f0, sX0, sW0, sA0, 0, pan);
+  prefetch(1, sX1, sW1, sA1, pan);
   if constexpr (INT4) load_w4(w4a, AHEAD ? 2 : 1);
 
   // One K step on fixed buffers (c = this step's, o = the other): the buffer identities are
@@ -333,12 +359,12 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   auto step = [&](int kt, W4& w4n, uint16_t* xc, uint16_t* wc, uint16_t* ac, uint16_t* xo,
                   uint16_t* wo, uint16_t* ao) {
     if constexpr (INT4)  // the unpacked W of step kt+1, spread between the MFMAs
-      phase(f0, f1, xc, wc, ac, 1, [&](int d) { if (d % 2 == 0) store_w4_part(w4n, wo, d / 2); });
+      phase(f0, f1, xc, wc, ac, 1, pan, [&](int d) { if (d % 2 == 0) store_w4_part(w4n, wo, d / 2); });
     else
-      phase(f0, f1, xc, wc, ac, 1, nocopy);
+      phase(f0, f1, xc, wc, ac, 1, pan, nocopy);
     wait_all();
-    phase(f1, f0, xo, wo, ao, 0, [&](int d) {
-      prefetch_part(d, kt + 2, xc, wc, ac);
+    phase(f1, f0, xo, wo, ao, 0, pan, [&](int d) {
+      prefetch_part(d, kt + 2, xc, wc, ac, pan);
       if constexpr (INT4) { if (d == 15) load_w4(w4n, kt + (AHEAD ? 3 : 2)); }  // after every copy
     });
   };
@@ -349,6 +375,8 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     step(kt + 1, w4a, sX1, sW1, sA1, sX0, sW0, sA0);
   }
   if (kt < nk) step(kt, w4odd, sX0, sW0, sA0, sX1, sW1, sA1);
+  }
+
   // B fragments of the low-rank epilogue, loaded now so their latency overlaps the panel work
   // (ranks up to 32; the rank-64 instances load them later, prefetching there crashes the
   // compiler)
@@ -552,13 +580,25 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     __syncthreads();  // the partner is done reading this wave's buffer
     if (wn) put(up_half); else put(gate_half);
   }
+  };
+  if constexpr (PERSIST) {
+    for (int vb = blockIdx.x; vb < tiles; vb += gridDim.x) {
+      tile(vb);
+      __syncthreads();  // the next tile's copies reuse every wave's LDS
+    }
+  } else {
+    tile(blockIdx.x);
+  }
 }
 
 template <int RP, bool INT4, bool PANEL, int EPI = kEpiLora, bool FP4 = false>
 static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
   // SwiGLU: N = 2 Nh stacked rows, one tile per 128 outputs of H: ceil(2 Nh / 256) of them
   const int tiles = (int)(((a.M + kTile - 1) / kTile) * ((a.N + kTile - 1) / kTile));
-  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, EPI, FP4>), dim3(tiles), dim3(kThreads), 0, s,
+  // persistent instances: one resident workgroup per CU, each looping over its run of tiles
+  const int cus = device_cus() & ~7;  // a multiple of the 8 XCDs
+  const int grid = (fwd_persistent(RP, EPI, INT4) && cus > 0 && tiles > cus) ? cus : tiles;
+  hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, EPI, FP4>), dim3(grid), dim3(kThreads), 0, s,
                      (const uint16_t*)a.X, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (uint16_t*)a.H, a.ce, (int)a.M, (int)a.N,
                      (int)a.K, (int)a.R, a.scale);

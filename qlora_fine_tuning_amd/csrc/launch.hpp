@@ -76,6 +76,9 @@ hipError_t launch_sclk_probe(unsigned long long* out, unsigned int ticks, hipStr
 hipError_t launch_mfma_rate(unsigned long long* out, int blocks, unsigned int iters, hipStream_t s);
 hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
+// compute units of the current device (the persistent MFMA kernels launch one workgroup per CU)
+int device_cus();
+
 // bf16 / int4 MFMA paths
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s);
 hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s);
