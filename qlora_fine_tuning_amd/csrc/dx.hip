@@ -48,9 +48,9 @@ __device__ __forceinline__ f32x4 ld_part(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCpolSc1);
 }
 
-// The bf16 instance of rank 16 loops over units (one resident workgroup per CU); the others keep
-// one unit per workgroup: with the loop around them the compiler fails or spills in the main loop.
-constexpr bool dx_persistent(int rp, bool int4) { return rp <= 16 && !int4; }
+// The instances of rank 16 loop over units (one resident workgroup per CU); the others keep one
+// unit per workgroup: with the loop around them the compiler fails or spills in the main loop.
+constexpr bool dx_persistent(int rp, bool int4) { return rp <= 16; }
 
 // FP4 (with INT4): the 4-bit weight is MXFP4 (E2M1 codes, one E8M0 byte per 32 k; a thread's 64
 // codes are two blocks, whose two bytes sit where the int4 fp16 scale would).

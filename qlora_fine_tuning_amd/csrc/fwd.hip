@@ -68,7 +68,7 @@ __device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stag
 // reads them).
 // FP4 (with INT4): the 4-bit weight is MXFP4, E2M1 codes in the same nibble layout and one E8M0
 // exponent byte per 32 k (the two bytes of a 64-k step sit where the int4 fp16 scale would).
-constexpr bool fwd_persistent(int rp, int epi, bool int4) { return rp <= 16 && epi != kEpiSwiglu && !int4; }
+constexpr bool fwd_persistent(int rp, int epi, bool int4) { return rp <= 16 && epi != kEpiSwiglu; }
 
 template <int RP, bool INT4, bool PANEL, int EPI, bool FP4 = false>
 __global__ void __launch_bounds__(kThreads)
@@ -95,9 +95,9 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   // give the workgroups blockIdx, blockIdx + gridDim, ... (the grid a multiple of the 8 XCDs, so
   // all of them run on this workgroup's XCD and keep its L2 footprint); in the grouped order those
   // tiles lie in one row of tiles, so the rank panel X A^T computed on the first of them is reused
-  // by the rest.  (Only the bf16 instances of rank 16 and the LM head loop over tiles; the others
-  // keep one tile per workgroup: with the tile loop around them the compiler fails or spills
-  // inside the main loop.)
+  // by the rest.  (Only the rank-16 instances other than the SwiGLU pair, and the LM head, loop
+  // over tiles; the others keep one tile per workgroup: with the tile loop around them the
+  // compiler fails or spills inside the main loop.)
   const int tiles = tiles_m * tiles_n;
   constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
   f32x4 pacc[NB][4];
