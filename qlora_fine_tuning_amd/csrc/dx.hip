@@ -54,7 +54,9 @@ constexpr bool dx_persistent(int rp, bool int4) { return rp <= 16; }
 
 // FP4 (with INT4): the 4-bit weight is MXFP4 (E2M1 codes, one E8M0 byte per 32 k; a thread's 64
 // codes are two blocks, whose two bytes sit where the int4 fp16 scale would).
-template <int RP, bool INT4, bool FP4 = false>
+// NOADP: no adapter at all (dX = dY W, the gradient of an LM head's logits): no panel, no B or A
+// copies and no low-rank epilogue; A, B and G are not read or written.
+template <int RP, bool INT4, bool FP4 = false, bool NOADP = false>
 __global__ void __launch_bounds__(kThreads)
 dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
                const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
@@ -70,7 +72,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   // The rank-64 instances read G, computed by a pass of its own, in the epilogue: the panel's
   // 16 accumulator blocks and B fragments do not fit next to the main tile's, and with them
   // the compiler spills and moves accumulators.
-  constexpr bool PANEL = RP <= 32;
+  constexpr bool PANEL = RP <= 32 && !NOADP;
   constexpr bool PERSIST = dx_persistent(RP, INT4);
   constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
   constexpr int TT = kTile * kStep;  // 16384 elements: dY tile 256 x 64, W tile 64 x 256
@@ -382,7 +384,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   // (ranks up to 32; the rank-64 instances load it later, prefetching there crashes the compiler)
   constexpr int AQ = RP <= 32 ? (RP * 32 + kThreads - 1) / kThreads : 1;
   u32x4 av[AQ];
-  if constexpr (RP <= 32) {
+  if constexpr (RP <= 32 && !NOADP) {
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
       const int c = q * kThreads + tid, rank = c >> 5, kc = c & 31;
@@ -398,7 +400,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     // partial slot: [wave][acc block][lane] f32x4, then (with a panel) the G panel [wave][block][lane]
     constexpr uint32_t kAccBytes = 4 * 64 * 64 * 16, kPanBytes = PANEL ? 4 * (RP / 16) * 4 * 64 * 16 : 0;
     constexpr uint32_t kSlot = kAccBytes + kPanBytes;
-    static_assert(kSlot == dx_slot_bytes(RP), "the host sizes the partials with dx_slot_bytes");
+    static_assert(kSlot <= dx_slot_bytes(RP), "the host sizes the partials with dx_slot_bytes");
     const rsrc_t rP = make_rsrc(part + (size_t)tile * splits * (kSlot / 4), (uint32_t)splits * kSlot);
     const uint32_t wa = ((uint32_t)wave * 64 * 64 + lane) * 16u;
     const uint32_t wp = kAccBytes + ((uint32_t)wave * (RP / 16) * 4 * 64 + lane) * 16u;
@@ -453,6 +455,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     panel_tm = -1;  // pacc now holds the sum over the splits, not this unit's share
   }
 
+  if constexpr (!NOADP) {
   // ---- epilogue: G panel -> LDS (and HBM once per row tile); A tile -> LDS ----
   // The four freed tile buffers each take 64 rows of G (fp32, stride GS) followed by RP/4
   // rows of the A tile (bf16, stride AS; the 32-byte pad staggers the banks of the 4 rows a
@@ -531,6 +534,8 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     }
   }
 
+  }
+
   // ---- store dX (one rounding), staged through this wave's freed tile buffer ----
   __syncthreads();  // every wave is done with G and A in LDS
   uint16_t* const stage = wave == 0 ? sD0 : (wave == 1 ? sD1 : (wave == 2 ? sW0 : sW1));
@@ -552,7 +557,7 @@ __global__ void zero_u32_kernel(uint32_t* p, int n) {  // the split arrival coun
   if (i < n) p[i] = 0u;
 }
 
-template <int RP, bool INT4, bool FP4 = false>
+template <int RP, bool INT4, bool FP4 = false, bool NOADP = false>
 static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
   const int tiles = dx_tiles(a.M, a.K);
   const int splits = dx_splits(a.M, a.N, a.K, a.R);
@@ -563,7 +568,7 @@ static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
   }
   const int units = tiles * splits, cus = device_cus() & ~7;  // a multiple of the 8 XCDs
   const int grid = (dx_persistent(RP, INT4) && cus > 0 && units > cus) ? cus : units;
-  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4, FP4>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4, FP4, NOADP>), dim3(grid), dim3(kThreads), 0, s,
                      (const uint16_t*)a.dY, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.dX, a.G, (int)a.M, (int)a.N, (int)a.K,
                      (int)a.R, a.scale, splits, a.part, a.ctr);
@@ -586,5 +591,9 @@ hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s) {
   if (rp == 32) return launch_dx_rp<32, false>(a, s);
   return launch_dx_rp<64, false>(a, s);
 }
+
+// dX = dY W alone (bf16, no adapter): the LM head's input gradient.  a.A, a.B and a.G are unused;
+// a.ctr and a.part as for the rank-16 instance.
+hipError_t launch_dx_noadapter(const DxArgs& a, hipStream_t s) { return launch_dx_rp<16, false, false, true>(a, s); }
 
 }  // namespace lora

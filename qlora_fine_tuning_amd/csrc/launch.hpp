@@ -97,6 +97,8 @@ hipError_t launch_ce_grad(uint16_t* hi, const uint16_t* lo, const float* lse, co
 hipError_t launch_scale_bf16(const uint16_t* in, uint16_t* out, int64_t n, const float* g, hipStream_t s);
 hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_dx_mfma(const DxArgs& a, bool int4, hipStream_t s);
+// dX = dY W with no adapter (the LM head's gradient; bf16, rank-16 tiling of the split partials)
+hipError_t launch_dx_noadapter(const DxArgs& a, hipStream_t s);
 // ranks 33..64: G = dY B as a pass of its own (written to G), ahead of the input-gradient kernel,
 // which then reads G in its epilogue; `ws` holds panel_workspace_bytes() bytes
 int panel_shares(int64_t M, int64_t C);

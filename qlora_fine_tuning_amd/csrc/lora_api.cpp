@@ -2,6 +2,7 @@
 // layout, and dispatch to the gfx950 kernels.  Declarations and conventions: include/lora.h.
 #include "lora.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -589,7 +590,7 @@ namespace {
 // budget, in whole multiples of 256 tokens and never fewer than 256.
 constexpr size_t kCeLogitsBudget = (size_t)512 << 20;
 constexpr int64_t kCeChunkUnit = 256;
-constexpr int32_t kCeRank = 8;  // the input-gradient kernel runs with zero adapters of this rank
+constexpr int32_t kCeRank = 8;  // the rank the shape checks take (the LM head has no adapter)
 
 int64_t ce_default_chunk(int64_t V) {
   if (V <= 0) return kCeChunkUnit;
@@ -609,11 +610,14 @@ lora_status check_ce(int64_t M, int64_t V, int64_t K, int64_t chunk) {
 }
 
 // Per chunk: the (max, sum of exp) pairs, label logits and lse of its rows; with the gradient also
-// the zero adapters, the chunk's fp32 logits as a high and a low 16-bit plane (the gradient of the
-// logits is written over the high plane), and the input-gradient kernel's workspace.
+// the chunk's fp32 logits as a high and a low 16-bit plane (the gradient of the logits is written
+// over the high plane), and the input-gradient kernel's split counters and partials.
 struct CeLayout {
-  size_t stats, lab, lse, azero, bzero, hi, lo, inner, total;
+  size_t stats, lab, lse, hi, lo, ctr, part, total;
 };
+// input-gradient scratch of a chunk of m tokens: per-tile arrival counters, split partials
+size_t ce_dx_ctr_bytes(int64_t m, int64_t K) { return align256((size_t)dx_tiles(m, K) * 4); }
+size_t ce_dx_part_bytes(int64_t m, int64_t V, int64_t K) { return align256(dx_part_bytes(m, V, K, 16)); }
 CeLayout ce_layout(int64_t M, int64_t V, int64_t K, int64_t chunk, bool grad) {
   const int64_t C = ce_chunk(M, V, chunk);
   const int64_t P = 2 * ((V + 255) / 256);  // partials per row: one per wave's 128 columns
@@ -623,20 +627,19 @@ CeLayout ce_layout(int64_t M, int64_t V, int64_t K, int64_t chunk, bool grad) {
   l.lse = l.lab + align256((size_t)C * 4);
   l.total = l.lse + align256((size_t)C * 4);
   if (grad) {
-    l.azero = l.total;
-    l.bzero = l.azero + align256((size_t)kCeRank * K * 2);
-    l.hi = l.bzero + align256((size_t)V * kCeRank * 2);
+    l.hi = l.total;
     l.lo = l.hi + align256((size_t)C * V * 2);
-    l.inner = l.lo + align256((size_t)C * V * 2);
-    // the input-gradient workspace of a full chunk and of the last, shorter one (whose split
-    // of V may differ)
+    l.ctr = l.lo + align256((size_t)C * V * 2);
+    // the input-gradient scratch of a full chunk and of the last, shorter one (whose split of V
+    // may differ)
     const int64_t tail = M % C;
-    size_t inner = bwd_layout(C, V, K, kCeRank, true).total;
+    size_t ctr = ce_dx_ctr_bytes(C, K), part = ce_dx_part_bytes(C, V, K);
     if (tail > 0) {
-      const size_t t = bwd_layout(tail, V, K, kCeRank, true).total;
-      inner = t > inner ? t : inner;
+      ctr = std::max(ctr, ce_dx_ctr_bytes(tail, K));
+      part = std::max(part, ce_dx_part_bytes(tail, V, K));
     }
-    l.total = l.inner + inner;
+    l.part = l.ctr + ctr;
+    l.total = l.part + part;
   }
   return l;
 }
@@ -682,10 +685,6 @@ lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_s
     // reduction puts NaN back for the next chunk)
     e = launch_fill_u32(lab, (size_t)C * 4, 0x7fc00000u, s);
     if (e != hipSuccess) return from_hip(e);
-    if (grad) {
-      e = launch_fill_u32(base + lay.azero, lay.hi - lay.azero, 0u, s);  // the zero adapters
-      if (e != hipSuccess) return from_hip(e);
-    }
   }
   for (int64_t c0 = 0; c0 < M; c0 += C) {
     const int64_t Mc = (M - c0 < C) ? M - c0 : C;
@@ -704,9 +703,10 @@ lora_status lora_ce(int64_t M, int64_t V, int64_t K, int64_t chunk, float grad_s
     // dlogits = grad_scale (softmax - onehot) over the high plane, then dX = dlogits W
     e = launch_ce_grad(hi, lo, lse, labels + c0, Mc, V, grad_scale, s);
     if (e != hipSuccess) return from_hip(e);
-    st = bwd_dx_common(false, LORA_BF16, Mc, V, K, kCeRank, 0.f, hi, W, nullptr, base + lay.azero, base + lay.bzero,
-                       static_cast<uint16_t*>(dX) + c0 * K, base + lay.inner, ws_bytes - lay.inner, stream);
-    if (st != LORA_OK) return st;
+    DxArgs d{hi, W, nullptr, nullptr, nullptr, static_cast<uint16_t*>(dX) + c0 * K, nullptr, Mc, V, K, kCeRank, 0.f,
+             reinterpret_cast<uint32_t*>(base + lay.ctr), reinterpret_cast<float*>(base + lay.part)};
+    e = launch_dx_noadapter(d, s);
+    if (e != hipSuccess) return from_hip(e);
   }
   if (loss_total != nullptr) return from_hip(launch_ce_sum(loss, loss_total, M, grad_scale, s));
   return LORA_OK;
