@@ -5,7 +5,7 @@ through inline-asm MFMAs, whose result latency the compiler cannot see.  That is
 while the compiler never copies an accumulator inside the main loop, and the loop is only fast
 while nothing spills to scratch there.  This module compiles a kernel source to device assembly
 with the library's own flags and reports, for every kernel instance, the MFMA, scratch and
-`v_accvgpr` instruction counts of its main loop (the loop with the most MFMAs).
+`v_accvgpr` instruction counts of its main loop (the innermost loop with the most MFMAs).
 
     python -m qlora_fine_tuning_amd.asm_loops            # fwd.hip and dx.hip
 """
@@ -31,11 +31,14 @@ def device_asm(source: str) -> str:
         return open(out).read()
 
 
-_LABEL = re.compile(r"^(\.LBB\w+):.*Loop Header")
+_LABEL = re.compile(r"^(\.LBB\w+):")
+_BRANCH = re.compile(r"\bs_(?:cbranch\w*|branch)\s+(\.LBB\w+)\b")
 
 
 def main_loops(asm: str, kernel_prefix: str) -> dict[str, tuple[int, int, int]]:
-    """{instance symbol: (mfma, scratch, accvgpr)} of each kernel's largest loop."""
+    """{instance symbol: (mfma, scratch, accvgpr)} of each kernel's main loop: of the innermost
+    loops (a backward branch to a label, with no other loop inside), the one with the most MFMAs.
+    (A persistent kernel's loop over tiles holds the main loop and so is not innermost.)"""
     lines = asm.split("\n")
     res = {}
     i = 0
@@ -48,15 +51,24 @@ def main_loops(asm: str, kernel_prefix: str) -> dict[str, tuple[int, int, int]]:
         while j < len(lines) and not lines[j].startswith(".Lfunc_end"):
             j += 1
         body = lines[i:j]
-        best = (0, 0, 0)
+        where = {}
         for k, line in enumerate(body):
-            hm = _LABEL.match(line)
-            if not hm:
-                continue
-            ends = [e for e, l in enumerate(body) if re.search(r"s_(cbranch\w*|branch)\s+" + re.escape(hm.group(1)) + r"\b", l)]
-            if not ends:
-                continue
-            seg = body[k:max(ends) + 1]
+            lm = _LABEL.match(line)
+            if lm:
+                where[lm.group(1)] = k
+        loops = []
+        for e, line in enumerate(body):
+            bm = _BRANCH.search(line)
+            if bm and bm.group(1) in where and where[bm.group(1)] < e:
+                loops.append((where[bm.group(1)], e))
+        spans = {}
+        for k, e in loops:  # one span per header: from the label to its last backward branch
+            spans[k] = max(e, spans.get(k, e))
+        inner = [(k, e) for k, e in spans.items()
+                 if not any(k < k2 and e2 <= e for k2, e2 in spans.items() if (k2, e2) != (k, e))]
+        best = (0, 0, 0)
+        for k, e in inner:
+            seg = body[k:e + 1]
             counts = (sum("v_mfma" in l for l in seg), sum("scratch_" in l for l in seg),
                       sum("v_accvgpr" in l for l in seg))
             best = max(best, counts)
