@@ -100,9 +100,11 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
   // compiler fails or spills inside the main loop.)
   const int tiles = tiles_m * tiles_n;
   constexpr int NB = PANEL ? RP / 16 : 1;  // panel rank blocks held in registers
-  f32x4 pacc[NB][4];
+  f32x4 pacc_keep[NB][4];  // the panel kept across tiles (persistent instances)
   int panel_tm = -1;
   auto tile = [&](int vb) {
+  f32x4 pacc_own[NB][4];  // one tile per workgroup: the panel lives with the tile
+  auto& pacc = PERSIST ? pacc_keep : pacc_own;
   // The lane's values are derived afresh on every tile (through an opaque copy of the thread id):
   // hoisted out of the tile loop, the addresses computed from them would stay live across the
   // main loop, which has no registers to spare, and be spilled.
