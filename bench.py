@@ -542,7 +542,7 @@ def main(argv=None):
     reps = max(args.steps, 10)
     fwd_ms = event_time_ms(fwd, reps, stream)
     ach = dx_flops(M, N, K, R) / dx_ms / 1e9
-    kernel = "dx_mfma_kernel<16,false>"
+    kernel = "dx_mfma_kernel<16,false,false,false>"
     roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(kernel, DX_SOURCES),
                 "traffic_unit": "HBM bytes per launch", "kernel": kernel,
