@@ -133,6 +133,13 @@ def test_mxfp4_qlora_small_shapes(gpu_lib, M, N, K, R):
     _check_qlora_mx(gpu_lib, make_inputs(M, N, K, R, seed=700 + M, int4=True), sampled=False)
 
 
+def test_mxfp4_qlora_persistent_row_change(gpu_lib):
+    # 11 x 24 tiles: workgroups walking several tiles, some across a change of row tile
+    M, N, K, R = 2816, 6144, 6144, 16
+    print(f"case mxfp4 qlora persistent M={M} N={N} K={K} R={R}", flush=True)
+    _check_qlora_mx(gpu_lib, make_inputs(M, N, K, R, seed=779, dtype="bf16", int4=True), sampled=False)
+
+
 def test_mxfp4_qlora_ffn_sampled(gpu_lib):
     # the QLoRA FFN shape (M=4096, K=5120 -> N=27648, r=16): the input gradient splits N
     print("case mxfp4 qlora_ffn (sampled rows)", flush=True)

@@ -76,6 +76,17 @@ def test_bf16_shapes(gpu_lib, M, N, K, R):
     check_full(gpu_lib, make_inputs(M, N, K, R, seed=200 + M + R, dtype="bf16"))
 
 
+# Above 256 tiles the rank-16 GEMMs launch one workgroup per CU, each walking several tiles and
+# reusing the rank panel while its tiles stay in one row of tiles.  With 11 row tiles the last
+# group of rows is 3 high, so some workgroups' consecutive tiles lie in different rows and the
+# panel is computed again: 11 x 24 = 264 tiles in the forward (M x N) and in the input gradient
+# (M x K); whole outputs.
+def test_bf16_persistent_row_change(gpu_lib):
+    M, N, K, R = 2816, 6144, 6144, 16
+    _say(f"case bf16 persistent M={M} N={N} K={K} R={R}")
+    check_full(gpu_lib, make_inputs(M, N, K, R, seed=777, dtype="bf16"))
+
+
 def _dadb_split_rows(M, N, K):
     # tokens per dA / dB split on the bf16 path: 256, doubled while 512 workgroups remain
     rows, tiles = 256, -(-K // 256) + -(-N // 256)
@@ -344,6 +355,13 @@ def check_qlora(lora, inp, sampled: bool):
 def test_qlora_small_shapes(gpu_lib, M, N, K, R):
     _say(f"case qlora M={M} N={N} K={K} R={R}")
     check_qlora(gpu_lib, make_inputs(M, N, K, R, seed=300 + M, dtype="bf16", int4=True), sampled=False)
+
+
+# the int4 forward and input gradient walk tiles the same way: the same row change, whole outputs
+def test_qlora_persistent_row_change(gpu_lib):
+    M, N, K, R = 2816, 6144, 6144, 16
+    _say(f"case qlora persistent M={M} N={N} K={K} R={R}")
+    check_qlora(gpu_lib, make_inputs(M, N, K, R, seed=778, dtype="bf16", int4=True), sampled=False)
 
 
 @pytest.mark.parametrize("b_dist", ["var", "std"])
