@@ -57,6 +57,23 @@ struct NoCopy {
   __device__ void operator()(int) const {}
 };
 
+// A K-loop phase hook called after every MFMA (with s = 8 * row + column) instead of after
+// MFMAs 1 and 5 of each row: for VALU work, which holds up the next MFMA issue when it comes
+// in one block (each VALU operation takes an issue slot the MFMA stream needs), and costs far
+// less in two or three operations per MFMA.
+// The hook's working values (type S) live in the phase's row loop, f(s, state).
+template <class S, class F>
+struct EveryMfma {
+  using State = S;
+  F f;
+};
+template <class S, class F>
+__device__ EveryMfma<S, F> every_mfma(F f) { return EveryMfma<S, F>{f}; }
+template <class T>
+struct IsEveryMfma : std::false_type {};
+template <class S, class F>
+struct IsEveryMfma<EveryMfma<S, F>> : std::true_type {};
+
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
@@ -168,6 +185,56 @@ __device__ __forceinline__ u32x4 dequant8_mix(uint32_t w, const I4Mix& m) {
   o[2] = pack_bf16(fmaf(f16hi(p0), m.s, m.c0), fmaf(f16hi(p1), m.s16, m.c1));
   o[3] = pack_bf16(fmaf(f16hi(p2), m.s, m.c0), fmaf(f16hi(p3), m.s16, m.c1));
   return o;
+}
+
+// dequant8_mix in stages of two or three VALU operations (stage s after MFMA s of a row, s =
+// 0..6), and the last pack (dequant8_mix_last) with the store after MFMA 7: the same operations
+// on the same values, hence the same bits.
+struct I4Stage {
+  uint32_t y, p0, p1, p2, p3;
+  u32x4 o;  // one vector, written element-wise: kept whole in registers
+  float t0, t1;
+};
+__device__ __forceinline__ void dequant8_mix_stage(int s, uint32_t w, const I4Mix& m, I4Stage& t) {
+  switch (s) {  // s is a constant after unrolling
+    case 0:
+      t.y = w >> 8;
+      t.p0 = (w & 0x000f000fu) ^ 0x64086408u;
+      t.p1 = (w & 0x00f000f0u) ^ 0x64806480u;
+      break;
+    case 1:
+      t.t0 = fmaf(f16lo(t.p0), m.s, m.c0);
+      t.t1 = fmaf(f16lo(t.p1), m.s16, m.c1);
+      break;
+    case 2:
+      t.o[0] = pack_bf16(t.t0, t.t1);
+      t.p2 = (t.y & 0x000f000fu) ^ 0x64086408u;
+      t.p3 = (t.y & 0x00f000f0u) ^ 0x64806480u;
+      break;
+    case 3:
+      t.t0 = fmaf(f16lo(t.p2), m.s, m.c0);
+      t.t1 = fmaf(f16lo(t.p3), m.s16, m.c1);
+      break;
+    case 4:
+      t.o[1] = pack_bf16(t.t0, t.t1);
+      t.t0 = fmaf(f16hi(t.p0), m.s, m.c0);
+      break;
+    case 5:
+      t.t1 = fmaf(f16hi(t.p1), m.s16, m.c1);
+      t.o[2] = pack_bf16(t.t0, t.t1);
+      break;
+    case 6:
+      t.t0 = fmaf(f16hi(t.p2), m.s, m.c0);
+      t.t1 = fmaf(f16hi(t.p3), m.s16, m.c1);
+      break;
+    default:
+      break;
+  }
+}
+__device__ __forceinline__ u32x4 dequant8_mix_last(const I4Stage& t) {
+  u32x4 r = t.o;
+  r[3] = pack_bf16(t.t0, t.t1);
+  return r;
 }
 
 // fp16 bits -> fp32 (exact).
