@@ -391,6 +391,16 @@ lora_status lora_probe_sclk(uint64_t* out, uint32_t ticks, void* stream);
  * iters in [1, 10^6].  Errors: LORA_ERR_NULL, LORA_ERR_ALIGN, LORA_ERR_VALUE, LORA_ERR_HIP. */
 lora_status lora_probe_mfma(uint64_t* out, int32_t blocks, uint32_t iters, void* stream);
 
+/* What other instructions between the MFMAs cost the matrix core (measurement support): the
+ * lora_probe_mfma stream (mode 0) with, per mode, 2, 4 or 6 s_nop after every MFMA (1-3); 20
+ * VALU operations after one MFMA in every 8 (4) or the same 20 spread two or three after each
+ * MFMA (5); operands read from LDS, two 16-byte reads per lane per 8 MFMAs, used 64 MFMAs later
+ * (6); one LDS DMA of 16 bytes per lane per 8 MFMAs (7).  Blocks of 64 MFMAs count in pairs:
+ * each wave issues 128 x iters MFMAs.  Same out layout, sizes and errors as lora_probe_mfma;
+ * mode in [0, 7] (else LORA_ERR_VALUE).  Mode 7 reads `out` itself as its copy source (before
+ * the results are written), so out must not be read by anything else meanwhile. */
+lora_status lora_probe_mfma_issue(uint64_t* out, int32_t blocks, uint32_t iters, int32_t mode, void* stream);
+
 /* The streaming-read ceiling (measurement support): reads `bytes` of device memory at `buf`
  * once, 1 KB contiguous per wave load instruction, and writes nothing in practice (`sink`, one
  * device uint32, is written only if the folded words equal a fixed constant; a zero-filled buffer

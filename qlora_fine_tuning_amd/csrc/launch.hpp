@@ -74,6 +74,7 @@ struct DadbArgs {
 // diagnostics (diag.hip): shader clock, matrix-core rate, streaming-read rate
 hipError_t launch_sclk_probe(unsigned long long* out, unsigned int ticks, hipStream_t s);
 hipError_t launch_mfma_rate(unsigned long long* out, int blocks, unsigned int iters, hipStream_t s);
+hipError_t launch_mfma_issue(unsigned long long* out, int blocks, unsigned int iters, int mode, hipStream_t s);
 hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // compute units of the current device (the persistent MFMA kernels launch one workgroup per CU)

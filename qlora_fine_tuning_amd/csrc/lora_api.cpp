@@ -766,6 +766,14 @@ lora_status lora_probe_mfma(uint64_t* out, int32_t blocks, uint32_t iters, void*
                                    static_cast<hipStream_t>(stream)));
 }
 
+lora_status lora_probe_mfma_issue(uint64_t* out, int32_t blocks, uint32_t iters, int32_t mode, void* stream) {
+  if (out == nullptr) return LORA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0) return LORA_ERR_ALIGN;
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > 1000000u || mode < 0 || mode > 7) return LORA_ERR_VALUE;
+  return from_hip(launch_mfma_issue(reinterpret_cast<unsigned long long*>(out), blocks, iters, mode,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 lora_status lora_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (buf == nullptr || sink == nullptr) return LORA_ERR_NULL;
   if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return LORA_ERR_ALIGN;

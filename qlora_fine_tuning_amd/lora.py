@@ -60,6 +60,7 @@ SIGNATURES = {
     "qlora_swiglu_bwd": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32] + [_p] * 16 + [_sz, _p]),
     "lora_probe_sclk": (_i32, [_p, ctypes.c_uint32, _p]),
     "lora_probe_mfma": (_i32, [_p, _i32, ctypes.c_uint32, _p]),
+    "lora_probe_mfma_issue": (_i32, [_p, _i32, ctypes.c_uint32, _i32, _p]),
     "lora_probe_hbm_read": (_i32, [_p, _sz, _p, _p]),
     "qlora_decode_status": (_i32, [_p, _sz, _p, _i32, _p]),
     "qlora_decode_fwd_noalloc": (_i32, [_i64, _i64, _i64, _i32, _f32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]),
@@ -690,6 +691,18 @@ def lora_probe_mfma(blocks: int = 256, iters: int = 2000, *, out=None, stream=No
     if out is None:
         out = torch.zeros(blocks * 4, 3, dtype=torch.int64, device="cuda")
     _check("lora_probe_mfma", lib.lora_probe_mfma(_ptr(out), int(blocks), int(iters), _stream(stream)))
+    return out
+
+
+def lora_probe_mfma_issue(mode: int, blocks: int = 256, iters: int = 1000, *, out=None, stream=None) -> torch.Tensor:
+    """Enqueue the MFMA issue-cost probe in `mode` (0-7); returns the device tensor [waves, 3]
+    (int64) of (shader cycles, 100 MHz ticks, live value) per wave; each wave issues 128 x iters
+    MFMAs."""
+    lib = load()
+    if out is None:
+        out = torch.zeros(blocks * 4, 3, dtype=torch.int64, device="cuda")
+    _check("lora_probe_mfma_issue",
+           lib.lora_probe_mfma_issue(_ptr(out), int(blocks), int(iters), int(mode), _stream(stream)))
     return out
 
 

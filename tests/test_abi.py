@@ -476,3 +476,11 @@ def test_probe_mfma_and_hbm_read_validation(lib):
     assert lib.lora_probe_hbm_read(MIS, 1024, P, None) == 4
     assert lib.lora_probe_hbm_read(P, 1024, ctypes.c_void_p(0x10002), None) == 4
     assert lib.lora_probe_hbm_read(P, 0, P, None) == 8 and lib.lora_probe_hbm_read(P, 1000, P, None) == 8
+
+
+def test_probe_mfma_issue_validation(lib):
+    assert lib.lora_probe_mfma_issue(None, 256, 10, 0, None) == 1
+    assert lib.lora_probe_mfma_issue(ctypes.c_void_p(0x10004), 256, 10, 0, None) == 4
+    for blocks, iters, mode in ((0, 10, 0), (65537, 10, 0), (256, 0, 0), (256, 1000001, 0), (256, 10, -1),
+                                (256, 10, 8)):
+        assert lib.lora_probe_mfma_issue(P, blocks, iters, mode, None) == 8
