@@ -19,7 +19,11 @@
 // gradient: 320 tiles, 432 steps), N is cut into S equal ranges and the grid holds S units per
 // tile.  Every unit stores its fp32 partial of the tile (and of its G panel) and moves the
 // tile's arrival counter; the last unit to arrive adds the S partials in split order (its own
-// from registers) and runs the epilogue, so the sum does not depend on arrival order.
+// from registers) and runs the epilogue, so the sum does not depend on arrival order.  When S
+// units per tile leave the last round of a persistent launch part empty, the first `split_hi`
+// tiles take S + 1 shorter units instead, chosen so that these fill whole rounds: every CU then
+// runs the same steps (the QLoRA FFN: 256 tiles x 3 units of 144 steps in three rounds, then
+// 64 tiles x 4 units of 108 steps in a fourth, 540 steps per CU against 576 with 3 units each).
 // QLoRA: W arrives as packed int4 codes plus fp16 group scales ("探微索隐：Unsloth 如何加速
 // LLM 推理？（以 Qwen 27B 为例）", §二.3); threads unpack them in registers into the same
 // row-major LDS tile.
@@ -62,7 +66,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
                const uint16_t* __restrict__ Wscale, const uint16_t* __restrict__ A,
                const uint16_t* __restrict__ Bm, uint16_t* __restrict__ dX,
                float* __restrict__ G, int M, int N, int K, int R, float scale, int splits,
-               float* __restrict__ part, uint32_t* __restrict__ ctr) {
+               int split_hi_arg, float* __restrict__ part, uint32_t* __restrict__ ctr) {
   // The accumulators stay in AGPRs through inline-asm MFMAs (this file is built with the
   // panel MFMAs in VGPR form).  That is only sound while the compiler never has to move an
   // accumulator inside the loop (it cannot see an asm MFMA's result latency); the builtin
@@ -84,7 +88,10 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_k = (K + kTile - 1) / kTile;
   const int tiles = tiles_m * tiles_k;
-  const int units = tiles * splits;
+  // (the MXFP4 instance of rank 16 keeps equal splits: with the mixed ones the compiler spills
+  // inside its main loop)
+  const int split_hi = (FP4 && RP == 16) ? 0 : split_hi_arg;
+  const int units = tiles * splits + split_hi;
   // Persistent: one workgroup per CU walks the units the non-persistent launch would give the
   // workgroups blockIdx, blockIdx + gridDim, ... (the grid a multiple of the 8 XCDs, so all run on
   // this workgroup's XCD); those lie in one row of tiles and one split, so the rank panel
@@ -100,18 +107,43 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wk = wave >> 1, wm = wave & 1;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // unit -> (split, tile), split-major: units running together share operand panels in L2
+  // unit -> (split, tile, splits of the tile), split-major: units running together share operand
+  // panels in L2.  With split_hi > 0 each XCD's range of units (units / 8 of them) holds first
+  // its share of the S-way tiles' units, in the rounds before, then its share of the (S+1)-way
+  // tiles' units, which make up the last round.
   const int unit = xcd_remap(vb, units);
-  const int sp = unit / tiles, tile = unit - sp * tiles;
+  int sp, tile, nsplit;
+  if (split_hi == 0) {
+    sp = unit / tiles;
+    tile = unit - sp * tiles;
+    nsplit = splits;
+  } else {
+    const int q = units >> 3, nlo = tiles - split_hi, lx = (nlo * splits) >> 3;
+    const int x = unit / q, local = unit - x * q;
+    if (local < lx) {
+      const int l = x * lx + local;
+      sp = l / nlo;
+      tile = split_hi + (l - sp * nlo);
+      nsplit = splits;
+    } else {
+      const int h = x * (q - lx) + (local - lx);
+      sp = h / split_hi;
+      tile = h - sp * split_hi;
+      nsplit = splits + 1;
+    }
+  }
   int tm, tk;
   grouped_tile(tile, tiles_m, tiles_k, 8, tm, tk);
-  const bool new_panel = PANEL && (!PERSIST || tm != panel_tm || sp != panel_sp);
+  // (the panel covers this unit's N range: the key is the row of tiles, the split and whether the
+  // tile is one of the (S+1)-way ones)
+  const int pkey = sp + (tile < split_hi ? 64 : 0);
+  const bool new_panel = PANEL && (!PERSIST || tm != panel_tm || pkey != panel_sp);
   panel_tm = tm;
-  panel_sp = sp;
+  panel_sp = pkey;
   const int m0 = tm * kTile, k0 = tk * kTile;
   const int ntot = N / kStep;
-  const int sbeg = sp * ntot / splits;  // this unit's N steps: [sbeg, sbeg + nsteps)
-  const int nsteps = (sp + 1) * ntot / splits - sbeg;
+  const int sbeg = sp * ntot / nsplit;  // this unit's N steps: [sbeg, sbeg + nsteps)
+  const int nsteps = (sp + 1) * ntot / nsplit - sbeg;
   const int nbase = sbeg * kStep;
   const uint32_t rowD = (uint32_t)N * 2, rowW = (uint32_t)K * 2;
 
@@ -396,12 +428,14 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   if constexpr (ASM) mfma_drain(acc);
 
   // ---- split N: store this unit's partial; the last unit of the tile adds them all ----
-  if (splits > 1) {
+  // (the split count again from the tile, rather than kept live across the main loop)
+  const int ns = splits + (tile < split_hi ? 1 : 0);
+  if (ns > 1) {
     // partial slot: [wave][acc block][lane] f32x4, then (with a panel) the G panel [wave][block][lane]
     constexpr uint32_t kAccBytes = 4 * 64 * 64 * 16, kPanBytes = PANEL ? 4 * (RP / 16) * 4 * 64 * 16 : 0;
     constexpr uint32_t kSlot = kAccBytes + kPanBytes;
     static_assert(kSlot <= dx_slot_bytes(RP), "the host sizes the partials with dx_slot_bytes");
-    const rsrc_t rP = make_rsrc(part + (size_t)tile * splits * (kSlot / 4), (uint32_t)splits * kSlot);
+    const rsrc_t rP = make_rsrc(part + (size_t)tile * (splits + (split_hi > 0)) * (kSlot / 4), (uint32_t)ns * kSlot);
     const uint32_t wa = ((uint32_t)wave * 64 * 64 + lane) * 16u;
     const uint32_t wp = kAccBytes + ((uint32_t)wave * (RP / 16) * 4 * 64 + lane) * 16u;
     const uint32_t own = (uint32_t)sp * kSlot;
@@ -417,14 +451,14 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     __syncthreads();
     if (tid == 0)
       s_last = __hip_atomic_fetch_add(ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(splits - 1);
+               (uint32_t)(ns - 1);
     __syncthreads();
     if (!s_last) return;
     // fixed order: ((p0 + p1) + p2) + ..., p_sp from registers; 16 blocks of loads in flight
 #pragma unroll
     for (int c0 = 0; c0 < 64; c0 += 16) {
       f32x4 tot[16];
-      for (int q = 0; q < splits; ++q) {
+      for (int q = 0; q < ns; ++q) {
         f32x4 v[16];
         if (q == sp) {
 #pragma unroll
@@ -445,7 +479,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 t = fzero4();
-        for (int q = 0; q < splits; ++q) {
+        for (int q = 0; q < ns; ++q) {
           const f32x4 v = q == sp ? pacc[c][j] : ld_part(rP, (uint32_t)q * kSlot + wp + (c * 4 + j) * 1024u);
           t = q == 0 ? v : t + v;
         }
@@ -561,17 +595,18 @@ template <int RP, bool INT4, bool FP4 = false, bool NOADP = false>
 static hipError_t launch_dx_rp(const DxArgs& a, hipStream_t s) {
   const int tiles = dx_tiles(a.M, a.K);
   const int splits = dx_splits(a.M, a.N, a.K, a.R);
+  const int split_hi = (FP4 && RP == 16) ? 0 : dx_split_hi(a.M, a.N, a.K, a.R);
   if (splits > 1) {
     hipLaunchKernelGGL(zero_u32_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s, a.ctr, tiles);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int units = tiles * splits, cus = device_cus() & ~7;  // a multiple of the 8 XCDs
+  const int units = tiles * splits + split_hi, cus = device_cus() & ~7;  // a multiple of the 8 XCDs
   const int grid = (dx_persistent(RP, INT4) && cus > 0 && units > cus) ? cus : units;
   hipLaunchKernelGGL((dx_mfma_kernel<RP, INT4, FP4, NOADP>), dim3(grid), dim3(kThreads), 0, s,
                      (const uint16_t*)a.dY, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.dX, a.G, (int)a.M, (int)a.N, (int)a.K,
-                     (int)a.R, a.scale, splits, a.part, a.ctr);
+                     (int)a.R, a.scale, splits, split_hi, a.part, a.ctr);
   return hipGetLastError();
 }
 

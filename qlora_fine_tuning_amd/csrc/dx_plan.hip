@@ -36,11 +36,28 @@ int dx_splits(int64_t M, int64_t N, int64_t K, int R) {
   return best;
 }
 
+// How many tiles (the first ones) take S + 1 units instead of S: the count that makes the units a
+// whole number of rounds of the persistent grid, used only when those (S + 1)-way units also
+// fill whole rounds by themselves (so they form the last round and every CU runs the same
+// number of steps) and still have at least 8 steps each; else 0.  The QLoRA FFN input gradient:
+// 320 tiles x 3 = 960 units on 256 CUs, 64 tiles x 4 = 256 units fill the fourth round (1.07 ->
+// ~1.0 ms measured).
+int dx_split_hi(int64_t M, int64_t N, int64_t K, int R) {
+  const int s = dx_splits(M, N, K, R);
+  if (s < 2) return 0;
+  const int64_t tiles = dx_tiles(M, K), units = tiles * s;
+  const int64_t cus = device_cus() & ~7;
+  if (cus <= 0 || units <= cus || units % cus == 0) return 0;
+  const int64_t hi = cus - units % cus;
+  if (hi > tiles || (hi * (s + 1)) % cus != 0 || (N / kStep) / (s + 1) < 8) return 0;
+  return (int)hi;
+}
+
 size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R) {
   const int s = dx_splits(M, N, K, R);
   if (s == 1) return 0;
   const int rp = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
-  return (size_t)dx_tiles(M, K) * s * dx_slot_bytes(rp);
+  return (size_t)dx_tiles(M, K) * (s + (dx_split_hi(M, N, K, R) > 0)) * dx_slot_bytes(rp);
 }
 
 }  // namespace lora

@@ -118,6 +118,7 @@ constexpr size_t dx_slot_bytes(int rp) {
 // input-gradient grid: output tiles, N ranges per tile, bytes of split partials (0 if unsplit)
 int dx_tiles(int64_t M, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K, int R);
+int dx_split_hi(int64_t M, int64_t N, int64_t K, int R);
 size_t dx_part_bytes(int64_t M, int64_t N, int64_t K, int R);
 hipError_t launch_dadb_partials_bf16(const DadbArgs& a, hipStream_t s);
 // RMSNorm ahead of a projection: forward (Y, reciprocal RMS r) and backward (dX, optional dg

@@ -119,10 +119,11 @@ def test_workspace_plan_qlora_ffn(lib):
     # aligned: G; dA / dB partials over 4 token splits of 1024 (128 column tiles: 256 tokens
     # doubled while 512 workgroups remain); one arrival counter per dX output tile (16 x 20);
     # the dX split partials: N cut into 3 ranges (the cost model's choice for 320 tiles of 432
-    # steps), each slot a 256 x 256 fp32 tile plus a rank-16 G panel.
+    # steps) and, for the first 64 tiles, into 4 (so that the 1024 units fill four rounds of the
+    # 256-CU grid): 4 slots per tile, each a 256 x 256 fp32 tile plus a rank-16 G panel.
     M, N, K, R = 4096, 27648, 5120, 16
     pad = lambda b: (b + 255) // 256 * 256
-    splits, tiles, n_split = 4, 16 * 20, 3
+    splits, tiles, n_split = 4, 16 * 20, 4
     slot = 4 * 64 * 64 * 16 + 4 * 1 * 4 * 64 * 16
     want = (pad(4 * M * R) + pad(4 * splits * R * K) + pad(4 * splits * R * N) + pad(4 * tiles)
             + pad(tiles * n_split * slot))
