@@ -185,11 +185,15 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     rWq = make_rsrc(static_cast<const uint8_t*>(Wp) + k0 / 2, (uint32_t)((size_t)N * (K / 2) - k0 / 2));
     rWs = make_rsrc(Wscale + k0 / 64, (uint32_t)((size_t)N * (K / 64) - k0 / 64) * 2u);
   }
-  // lanes 16 b .. 16 b + 15 of wave w: rows 16 w .. 16 w + 15 of 64-column block b.  (With the
-  // four blocks of a row on four consecutive lanes, which the blocks' 8 KB spacing puts on the
-  // same LDS banks, the unpacked stores conflicted 4-way.)  A load instruction still reads 16
-  // rows x 128 contiguous bytes.
-  const int qrow = (tid & 15) + 16 * (tid >> 6), qblk = (tid >> 4) & 3;
+  // lanes 16 b .. 16 b + 15 of wave w: rows 16 w .. 16 w + 15 of 64-column block b, lane l of
+  // the 16 on row 2 (l & 7) + (l >> 3): a 16-byte LDS store serves 8 lanes per cycle, and rows
+  // of one parity take 8 distinct wsw slots, so each 8 lanes fill the 8 distinct 16-byte bank
+  // groups.  (Rows in lane order paired equal slots, r and r + 1: 2-way conflicts on every
+  // store.  With the four blocks of a row on four consecutive lanes, 8 KB apart, the stores
+  // conflicted 4-way.)  A load instruction still reads 16 rows x 128 contiguous bytes.
+  // (rank 32 keeps rows in lane order: with the reordered rows its main loop spills)
+  const int qrow = RP == 32 ? (tid & 15) + 16 * (tid >> 6) : ((tid << 1) & 14) | ((tid >> 3) & 1) | ((tid >> 2) & 48);
+  const int qblk = (tid >> 4) & 3;
   auto load_w4 = [&](W4& v, int stn) {
     const uint32_t r = (uint32_t)(nbase + min(stn, nsteps - 1) * kStep + qrow);
     const uint32_t vo = r * (uint32_t)(K / 2) + (uint32_t)qblk * 32u;
