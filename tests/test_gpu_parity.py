@@ -370,6 +370,51 @@ def test_qlora_full_size(gpu_lib, b_dist):
     check_qlora(gpu_lib, workload_inputs("qlora_ffn", b_dist=b_dist), sampled=True)
 
 
+# The 4-bit paths unpack W into the same LDS tile the bf16 path copies, and run the same tiles,
+# MFMAs and sums: on the dequantised weight bf16_rne(q s) they give the bf16 layer's bits.  At the
+# full QLoRA FFN shape that covers the persistent forward with its staged int4 unpack and the
+# input gradient's mixed N splits (64 of its 320 tiles cut 4 ways, the rest 3).  (The MXFP4
+# input gradient of rank 16 keeps equal splits, so its partial sums, and the G panel dA uses,
+# group differently.)
+@pytest.mark.parametrize("group", [64, 32])
+def test_qlora_equals_bf16_layer_on_dequantised_weight(gpu_lib, group):
+    lora = gpu_lib
+    _say(f"case qlora vs bf16 on the dequantised weight, group {group}")
+    inp = workload_inputs("qlora_ffn")
+    Wq, Ws = lora.qlora_quantize(torch.from_numpy(inp.W).cuda(), group=group)
+    Wd = lora.qlora_dequant(Wq, Ws)
+    X, A, B, dY = (to_dev(inp, n) for n in ("X", "A", "B", "dY"))
+    Y4, XA4 = lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale)
+    Yb, XAb = lora.lora_fwd(X, Wd, A, B, inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(Y4, Yb) and torch.equal(XA4, XAb)
+    dX4, dA4, dB4 = lora.qlora_bwd(dY, X, Wq, Ws, A, B, XA4, inp.scale)
+    dXb, dAb, dBb = lora.lora_bwd(dY, X, Wd, A, B, XAb, inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dB4, dBb)  # dY^T XA: no input-gradient sums in it
+    if group == 64:
+        assert torch.equal(dX4, dXb) and torch.equal(dA4, dAb)
+    else:  # dX and the panel G that dA uses are summed over other split ranges
+        assert_close("dX", host(dX4), host(dXb).astype(np.float64))
+        assert_close("dA", host(dA4), host(dAb).astype(np.float64))
+
+
+def test_mixed_split_backward_is_bitwise_deterministic(gpu_lib):
+    # the QLoRA FFN input gradient: 1024 units on 256 CUs, partials added in split order
+    lora = gpu_lib
+    _say("case mixed-split determinism")
+    inp = workload_inputs("qlora_ffn")
+    Wq, Ws = lora.qlora_quantize(torch.from_numpy(inp.W).cuda())
+    X, A, B, dY = (to_dev(inp, n) for n in ("X", "A", "B", "dY"))
+    _, XA = lora.qlora_fwd(X, Wq, Ws, A, B, inp.scale)
+    ws = torch.empty(lora.qlora_bwd_workspace_bytes(inp.M, inp.N, inp.K, inp.R), dtype=torch.uint8, device=X.device)
+    d1 = lora.qlora_bwd_dx(dY, Wq, Ws, A, B, inp.scale, ws=ws).clone()
+    for _ in range(2):
+        d2 = lora.qlora_bwd_dx(dY, Wq, Ws, A, B, inp.scale, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(d1, d2)
+
+
 @pytest.mark.parametrize("name", ["decode_up", "decode_down"])
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_decode_full_size(gpu_lib, name, M):
