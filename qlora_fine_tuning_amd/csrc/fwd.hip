@@ -59,8 +59,10 @@ __device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stag
 }
 
 // PANEL: the panel X A^T is accumulated here from the X fragments of the main loop.  Without
-// it (rank 64, when the caller keeps XA) XA has been computed by a pass of its own and is read
-// in the epilogue: the rank-64 panel's accumulators and A fragments make the main loop spill.
+// it (when the caller keeps XA: rank 64, and the rank-32 SwiGLU pair) XA has been computed by a
+// pass of its own and is read in the epilogue: the rank-64 panel's accumulators and A fragments
+// make the main loop spill, and the SwiGLU pair's many column tiles per row of X would each
+// recompute the rank-32 panel.
 // EPI (bf16 W only when not kEpiLora): kEpiSwiglu, N = 2 Nh stacked rows, Y = [G | U] (M x 2 Nh)
 // and H (M x Nh) out; kEpiCeStats, the logits X W^T of an LM head (no adapter): per-row (max, sum
 // of exp) of each wave's 128 columns into `stats`, the label's logit, and the fp32 logits
@@ -68,7 +70,12 @@ __device__ __forceinline__ void store_half_bf16(const f32x4* acc, uint16_t* stag
 // reads them).
 // FP4 (with INT4): the 4-bit weight is MXFP4, E2M1 codes in the same nibble layout and one E8M0
 // exponent byte per 32 k (the two bytes of a 64-k step sit where the int4 fp16 scale would).
-constexpr bool fwd_persistent(int rp, int epi, bool int4) { return rp <= 16 && epi != kEpiSwiglu; }
+// Persistent (one resident workgroup per CU looping over tiles): the rank-16 instances with the
+// LoRA or LM-head epilogue, and the rank-32 SwiGLU pair without the panel.  The others keep one
+// tile per workgroup: with the tile loop around them the compiler fails or spills.
+constexpr bool fwd_persistent(int rp, int epi, bool int4, bool panel) {
+  return (rp <= 16 && epi != kEpiSwiglu) || (rp == 32 && epi == kEpiSwiglu && !panel);
+}
 
 template <int RP, bool INT4, bool PANEL, int EPI, bool FP4 = false>
 __global__ void __launch_bounds__(kThreads)
@@ -78,7 +85,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
                 float* __restrict__ XA, uint16_t* __restrict__ H, CeArgs ce, int M, int N, int K, int R,
                 float scale) {
   constexpr bool SWIGLU = EPI == kEpiSwiglu, CE = EPI >= kEpiCeStats, LORA = !CE;
-  constexpr bool PERSIST = fwd_persistent(RP, EPI, INT4);
+  constexpr bool PERSIST = fwd_persistent(RP, EPI, INT4, PANEL);
   static_assert(!(CE && INT4), "the LM head takes a bf16 weight");
   static_assert(!(CE && PANEL), "the LM head has no adapter");
   constexpr int TT = kTile * kStep;  // elements of one 256 x 64 operand tile
@@ -622,7 +629,7 @@ static hipError_t launch_fwd_rp(const FwdArgs& a, hipStream_t s) {
   const int tiles = (int)(((a.M + kTile - 1) / kTile) * ((a.N + kTile - 1) / kTile));
   // persistent instances: one resident workgroup per CU, each looping over its run of tiles
   const int cus = device_cus() & ~7;  // a multiple of the 8 XCDs
-  const int grid = (fwd_persistent(RP, EPI, INT4) && cus > 0 && tiles > cus) ? cus : tiles;
+  const int grid = (fwd_persistent(RP, EPI, INT4, PANEL) && cus > 0 && tiles > cus) ? cus : tiles;
   hipLaunchKernelGGL((fwd_mfma_kernel<RP, INT4, PANEL, EPI, FP4>), dim3(grid), dim3(kThreads), 0, s,
                      (const uint16_t*)a.X, a.W, (const uint16_t*)a.Ws, (const uint16_t*)a.A,
                      (const uint16_t*)a.B, (uint16_t*)a.Y, a.XA, (uint16_t*)a.H, a.ce, (int)a.M, (int)a.N,
@@ -637,14 +644,22 @@ hipError_t launch_ce_logits(const FwdArgs& a, hipStream_t s) { return launch_fwd
 hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
   const int rp = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
   const bool swiglu = a.H != nullptr;
-  if (swiglu && int4) {  // the SwiGLU pair over a stacked 4-bit weight
-    if (rp == 64 && a.XA != nullptr) {
-      const hipError_t e = launch_panel_xa(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A),
-                                           a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
-      if (e != hipSuccess) return e;
-      return a.fp4 ? launch_fwd_rp<64, true, false, kEpiSwiglu, true>(a, s)
-                   : launch_fwd_rp<64, true, false, kEpiSwiglu, false>(a, s);
+  if (swiglu && rp >= 32 && a.XA != nullptr) {
+    // the SwiGLU pair at ranks 32 and 64: the panel by its own pass into XA (partials in Y, which
+    // the kernel then overwrites), then the kernel without the panel (persistent at rank 32)
+    const hipError_t e = launch_panel_xa(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A),
+                                         a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
+    if (e != hipSuccess) return e;
+    if (rp == 32) {
+      if (!int4) return launch_fwd_rp<32, false, false, kEpiSwiglu>(a, s);
+      return a.fp4 ? launch_fwd_rp<32, true, false, kEpiSwiglu, true>(a, s)
+                   : launch_fwd_rp<32, true, false, kEpiSwiglu, false>(a, s);
     }
+    if (!int4) return launch_fwd_rp<64, false, false, kEpiSwiglu>(a, s);
+    return a.fp4 ? launch_fwd_rp<64, true, false, kEpiSwiglu, true>(a, s)
+                 : launch_fwd_rp<64, true, false, kEpiSwiglu, false>(a, s);
+  }
+  if (swiglu && int4) {  // the SwiGLU pair over a stacked 4-bit weight
     if (a.fp4) {
       if (rp == 16) return launch_fwd_rp<16, true, true, kEpiSwiglu, true>(a, s);
       if (rp == 32) return launch_fwd_rp<32, true, true, kEpiSwiglu, true>(a, s);
@@ -660,7 +675,6 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, bool int4, hipStream_t s) {
     const hipError_t e = launch_panel_xa(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A),
                                          a.XA, a.Y, (size_t)a.M * a.N * 2, a.M, a.K, a.R, s);
     if (e != hipSuccess) return e;
-    if (swiglu) return launch_fwd_rp<64, false, false, kEpiSwiglu>(a, s);
     if (int4 && a.fp4) return launch_fwd_rp<64, true, false, kEpiLora, true>(a, s);
     return int4 ? launch_fwd_rp<64, true, false>(a, s) : launch_fwd_rp<64, false, false>(a, s);
   }

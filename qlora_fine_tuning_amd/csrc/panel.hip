@@ -5,7 +5,9 @@
 // tutorial ch. 5 "加速原理：Triton kernel 与 fused LoRA", §5.3 (the LoRA backward; gradients
 // derived by hand).  Up to rank 32 the input-gradient kernel computes G from the dY tiles it
 // already holds; at rank 64 the panel's accumulators and operands no longer fit next to the
-// main tile's, so G comes from here and the main kernel reads it in its epilogue.
+// main tile's, so G comes from here and the main kernel reads it in its epilogue.  The same
+// kernels form the forward's XA = X A^T where the forward kernel goes without its panel (rank
+// 64, and the rank-32 SwiGLU pair, whose many column tiles per row would each recompute it).
 //
 //  * bt_transpose_kernel: B (N x R, rank-contiguous) -> Bt (R x N), so that both MFMA operands
 //    of the panel are contiguous along the contraction index n;
