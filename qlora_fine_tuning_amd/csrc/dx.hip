@@ -52,9 +52,10 @@ __device__ __forceinline__ f32x4 ld_part(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCpolSc1);
 }
 
-// The instances of rank 16 loop over units (one resident workgroup per CU); the others keep one
-// unit per workgroup: with the loop around them the compiler fails or spills in the main loop.
-constexpr bool dx_persistent(int rp, bool int4) { return rp <= 16; }
+// The instances of rank 16, and the bf16 ones of rank 32, loop over units (one resident workgroup
+// per CU); the others keep one unit per workgroup: with the loop around them the compiler fails
+// or spills in the main loop.
+constexpr bool dx_persistent(int rp, bool int4) { return rp <= 16 || (rp == 32 && !int4); }
 
 // FP4 (with INT4): the 4-bit weight is MXFP4 (E2M1 codes, one E8M0 byte per 32 k; a thread's 64
 // codes are two blocks, whose two bytes sit where the int4 fp16 scale would).
@@ -417,10 +418,12 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   }
   if (st < nsteps) step(st, w4odd, sD0, sW0, sB0, sD1, sW1, sB1);
   // the A tile of the low-rank epilogue, loaded now so its latency overlaps the panel work
-  // (ranks up to 32; the rank-64 instances load it later, prefetching there crashes the compiler)
-  constexpr int AQ = RP <= 32 ? (RP * 32 + kThreads - 1) / kThreads : 1;
+  // (rank 16, and the one-unit instances of rank 32; the others load it later: prefetching there
+  // crashes the compiler)
+  constexpr bool APRE = !NOADP && (RP <= 16 || (RP == 32 && !PERSIST));
+  constexpr int AQ = APRE ? (RP * 32 + kThreads - 1) / kThreads : 1;
   u32x4 av[AQ];
-  if constexpr (RP <= 32 && !NOADP) {
+  if constexpr (APRE) {
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
       const int c = q * kThreads + tid, rank = c >> 5, kc = c & 31;
@@ -528,7 +531,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
       *reinterpret_cast<f32x4*>(grow(ml) + rk) = v;
     }
   }
-  if constexpr (RP <= 32) {
+  if constexpr (APRE) {
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
       const int c = q * kThreads + tid, rank = c >> 5, kc = c & 31;

@@ -76,15 +76,16 @@ def test_bf16_shapes(gpu_lib, M, N, K, R):
     check_full(gpu_lib, make_inputs(M, N, K, R, seed=200 + M + R, dtype="bf16"))
 
 
-# Above 256 tiles the rank-16 GEMMs launch one workgroup per CU, each walking several tiles and
-# reusing the rank panel while its tiles stay in one row of tiles.  With 11 row tiles the last
-# group of rows is 3 high, so some workgroups' consecutive tiles lie in different rows and the
-# panel is computed again: 11 x 24 = 264 tiles in the forward (M x N) and in the input gradient
-# (M x K); whole outputs.
-def test_bf16_persistent_row_change(gpu_lib):
-    M, N, K, R = 2816, 6144, 6144, 16
+# Above 256 tiles the rank-16 GEMMs (and the bf16 input gradient of rank 32) launch one workgroup
+# per CU, each walking several tiles and reusing the rank panel while its tiles stay in one row of
+# tiles.  With 11 row tiles the last group of rows is 3 high, so some workgroups' consecutive
+# tiles lie in different rows and the panel is computed again: 11 x 24 = 264 tiles in the forward
+# (M x N) and in the input gradient (M x K); whole outputs.
+@pytest.mark.parametrize("R", [16, 32])
+def test_bf16_persistent_row_change(gpu_lib, R):
+    M, N, K = 2816, 6144, 6144
     _say(f"case bf16 persistent M={M} N={N} K={K} R={R}")
-    check_full(gpu_lib, make_inputs(M, N, K, R, seed=777, dtype="bf16"))
+    check_full(gpu_lib, make_inputs(M, N, K, R, seed=777 + R, dtype="bf16"))
 
 
 def _dadb_split_rows(M, N, K):
@@ -264,6 +265,13 @@ def check_sampled(lora, inp, seed=0):
 def test_full_size_workloads(gpu_lib, name):
     _say(f"case full-size {name}")
     check_sampled(gpu_lib, workload_inputs(name))
+
+
+def test_bf16_rank32_split_persistent_full_size(gpu_lib):
+    # the bf16 input gradient of rank 32 walks units with its rank panel, here at the QLoRA FFN
+    # shape, whose 320 dX tiles split N (with more units than CUs, mixed 3- and 4-way splits)
+    _say("case bf16 rank 32 at the qlora_ffn shape")
+    check_sampled(gpu_lib, make_inputs(4096, 27648, 5120, 32, seed=909, dtype="bf16"), seed=2)
 
 
 def test_full_size_attn_proj_std_reading_of_b(gpu_lib):
