@@ -11,9 +11,12 @@
 //
 //  * bt_transpose_kernel: B (N x R, rank-contiguous) -> Bt (R x N), so that both MFMA operands
 //    of the panel are contiguous along the contraction index n;
-//  * panel_kernel: one workgroup per (64 tokens, share of N); each wave owns 16 tokens and all
-//    64 ranks (4 MFMA blocks) and streams its dY rows and the Bt rows straight from memory
-//    (no LDS: dY is read once, Bt is small and stays in L2), writing an fp32 partial;
+//  * panel_kernel: one workgroup per (128 tokens, share of N); each wave owns 32 tokens and the
+//    ranks in 16-wide blocks (2 up to rank 32, else 4) and streams its dY rows and the Bt rows
+//    straight from memory (no LDS: dY is read once, Bt is small and stays in L2), writing an
+//    fp32 partial.  Two token blocks per wave halve the Bt loads per MFMA, and the next 128
+//    columns' loads are in flight while the current ones are multiplied: at rank 64 the pass
+//    takes ~10 us less at the attention shape than with 16 tokens per wave and no lookahead;
 //  * panel_reduce_kernel: adds the partials in share order into G.
 // The sums run in a fixed order: results are bitwise reproducible.
 #include <algorithm>
@@ -23,7 +26,8 @@
 
 namespace lora {
 
-constexpr int kPanelRows = 64;   // tokens per workgroup (16 per wave)
+constexpr int kPanelTB = 2;      // 16-token blocks per wave
+constexpr int kPanelRows = 64 * kPanelTB;  // tokens per workgroup
 constexpr int kPanelRanks = 64;  // ranks covered (R in 33..64; ranks >= R read as zero)
 
 // Bt[r][n] = B[n][r]: a 64 x R block of B per workgroup through LDS.
@@ -43,49 +47,87 @@ bt_transpose_kernel(const uint16_t* __restrict__ B, uint16_t* __restrict__ Bt, i
 }
 
 // out[s][m][r] = sum over c in share s of Q[m][c] * S[r][c]  (Q: M x C, S: R x C, bf16), rows
-// of ldo floats: 64 for partials, or R when one share writes the panel itself (ranks < R only)
+// of ldo floats: 64 for partials, or R when one share writes the panel itself (ranks < R only).
+// Each wave owns TB blocks of 16 tokens and RB blocks of 16 ranks (RB = 2 up to rank 32): one
+// 32-wide step loads TB token and RB rank fragments for TB x RB MFMAs, and the loads of the next
+// four steps are in flight while the current four are multiplied.
+template <int RB>
 __global__ void __launch_bounds__(256)
 panel_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ S, float* __restrict__ part,
              int M, int C, int R, int share, int ldo) {
+  constexpr int TB = kPanelTB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int m0 = blockIdx.x * kPanelRows + wave * 16;
+  const int m0 = blockIdx.x * kPanelRows + wave * 16 * TB;
   const int cs = blockIdx.y;
   const int c0 = cs * share, c1 = min(C, c0 + share);
-  const rsrc_t rQ = make_rsrc(Q + (size_t)m0 * C, (uint32_t)max(0, min(16, M - m0)) * (uint32_t)C * 2u);
+  const rsrc_t rQ = make_rsrc(Q + (size_t)m0 * C, (uint32_t)max(0, min(16 * TB, M - m0)) * (uint32_t)C * 2u);
   const rsrc_t rS = make_rsrc(S, (uint32_t)R * (uint32_t)C * 2u);
   const uint32_t qoff = ((uint32_t)l16 * (uint32_t)C + (uint32_t)(8 * g4)) * 2u;
-  f32x4 acc[4] = {fzero4(), fzero4(), fzero4(), fzero4()};
-  // four 32-wide steps per iteration: their 20 loads are issued before the first MFMA
-  int c = c0;
-  for (; c + 128 <= c1; c += 128) {
-    u32x4 a[4], s[4][4];
+  const uint32_t qrow16 = 16u * (uint32_t)C * 2u;  // 16 token rows
+  f32x4 acc[RB][TB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[rb][t] = fzero4();
+  struct Frags {
+    u32x4 a[4][TB], s[4][RB];
+  };
+  auto load = [&](Frags& f, int c) {  // four 32-wide steps from column c
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      a[u] = bload16(rQ, qoff + (uint32_t)(c + 32 * u) * 2u, 0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        s[u][rb] = bload16(rS, ((uint32_t)(rb * 16 + l16) * (uint32_t)C + (uint32_t)(c + 32 * u + 8 * g4)) * 2u, 0);
+      for (int t = 0; t < TB; ++t) f.a[u][t] = bload16(rQ, qoff + (uint32_t)t * qrow16 + (uint32_t)(c + 32 * u) * 2u, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        f.s[u][rb] = bload16(rS, ((uint32_t)(rb * 16 + l16) * (uint32_t)C + (uint32_t)(c + 32 * u + 8 * g4)) * 2u, 0);
     }
+  };
+  auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb] = mfma16(s[u][rb], a[u], acc[rb]);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) acc[rb][t] = mfma16(f.s[u][rb], f.a[u][t], acc[rb][t]);
+  };
+  int c = c0;
+  if (c + 128 <= c1) {
+    Frags f0, f1;
+    load(f0, c);
+    for (; c + 256 <= c1; c += 256) {  // two 128-wide blocks per iteration, one in flight
+      load(f1, c + 128);
+      mma(f0);
+      if (c + 384 <= c1) load(f0, c + 256);
+      mma(f1);
+    }
+    if (c + 128 <= c1) {  // one block left, already loaded into f0
+      mma(f0);
+      c += 128;
+    }
   }
   for (; c < c1; c += 32) {
-    const u32x4 a = bload16(rQ, qoff + (uint32_t)c * 2u, 0);
+    u32x4 a[TB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      acc[rb] = mfma16(bload16(rS, ((uint32_t)(rb * 16 + l16) * (uint32_t)C + (uint32_t)(c + 8 * g4)) * 2u, 0), a, acc[rb]);
+    for (int t = 0; t < TB; ++t) a[t] = bload16(rQ, qoff + (uint32_t)t * qrow16 + (uint32_t)c * 2u, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const u32x4 sv = bload16(rS, ((uint32_t)(rb * 16 + l16) * (uint32_t)C + (uint32_t)(c + 8 * g4)) * 2u, 0);
+#pragma unroll
+      for (int t = 0; t < TB; ++t) acc[rb][t] = mfma16(sv, a[t], acc[rb][t]);
+    }
   }
-  // acc[rb]: ranks rb*16 + 4 g4 .. +3 of token m0 + l16
-  const int m = m0 + l16;
-  if (m < M) {
-    float* dst = part + ((size_t)cs * M + m) * ldo;
+  // acc[rb][t]: ranks rb*16 + 4 g4 .. +3 of token m0 + 16 t + l16
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      if (rb * 16 + 4 * g4 < ldo) *reinterpret_cast<f32x4*>(dst + rb * 16 + 4 * g4) = acc[rb];
+  for (int t = 0; t < TB; ++t) {
+    const int m = m0 + 16 * t + l16;
+    if (m < M) {
+      float* dst = part + ((size_t)cs * M + m) * ldo;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb * 16 + 4 * g4 < ldo) *reinterpret_cast<f32x4*>(dst + rb * 16 + 4 * g4) = acc[rb][t];
+    }
   }
 }
 
@@ -134,8 +176,11 @@ hipError_t launch_panel_g(const uint16_t* dY, const uint16_t* B, float* G, void*
   hipLaunchKernelGGL(bt_transpose_kernel, dim3((unsigned)(N / 64)), dim3(256), 0, s, B, Bt, (int)N, R);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(panel_kernel, dim3((unsigned)((M + kPanelRows - 1) / kPanelRows), (unsigned)used), dim3(256), 0, s,
-                     dY, Bt, part, (int)M, (int)N, R, (int)len, kPanelRanks);
+  const dim3 grid((unsigned)((M + kPanelRows - 1) / kPanelRows), (unsigned)used);
+  if (R <= 32)
+    hipLaunchKernelGGL(panel_kernel<2>, grid, dim3(256), 0, s, dY, Bt, part, (int)M, (int)N, R, (int)len, kPanelRanks);
+  else
+    hipLaunchKernelGGL(panel_kernel<4>, grid, dim3(256), 0, s, dY, Bt, part, (int)M, (int)N, R, (int)len, kPanelRanks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = M * R;
@@ -155,12 +200,18 @@ hipError_t launch_panel_xa(const uint16_t* X, const uint16_t* A, float* XA, void
   const int64_t len = panel_share_len(K, shares);
   const int used = (int)((K + len - 1) / len);
   const dim3 grid((unsigned)((M + kPanelRows - 1) / kPanelRows), (unsigned)used);
+  auto run = [&](float* out, int ldo) {
+    if (R <= 32)
+      hipLaunchKernelGGL(panel_kernel<2>, grid, dim3(256), 0, s, X, A, out, (int)M, (int)K, R, (int)len, ldo);
+    else
+      hipLaunchKernelGGL(panel_kernel<4>, grid, dim3(256), 0, s, X, A, out, (int)M, (int)K, R, (int)len, ldo);
+  };
   if (used == 1) {
-    hipLaunchKernelGGL(panel_kernel, grid, dim3(256), 0, s, X, A, XA, (int)M, (int)K, R, (int)len, R);
+    run(XA, R);
     return hipGetLastError();
   }
   float* part = static_cast<float*>(scratch);
-  hipLaunchKernelGGL(panel_kernel, grid, dim3(256), 0, s, X, A, part, (int)M, (int)K, R, (int)len, kPanelRanks);
+  run(part, kPanelRanks);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = M * R;
