@@ -213,12 +213,20 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
 #pragma unroll
     for (int d = 0; d < 8; ++d) store_w4_part(v, w, d);
   };
-  // B: 64 rows x RP ranks, through registers (ranks >= R are zero); branch-free: chunks past
-  // the tile read a valid row and land in the padding
-  // (ranks >= R read past the end of the buffer, which returns zeros: no select after the
-  // load, so nothing waits for it before the LDS store)
+  // B: 64 rows x RP ranks (ranks >= R are zero: their chunks read past the end of the buffer,
+  // which returns zeros).  bf16 rank 16 copies it straight into LDS, 16-byte chunk c = 64 w + lane
+  // by waves w < 2: row c / 2, ranks 8 (c % 2) ..  The others go through registers, branch-free
+  // (chunks past the tile read a valid row and land in the padding; no select after the load, so
+  // nothing waits for it before the LDS store): with the direct copy the rank-32 instances spill
+  // in the main loop, and the MXFP4 one ran slower.
+  constexpr bool BDMA = RP == 16 && !INT4;
   u32x4 rb[BQ];
   const rsrc_t rB = make_rsrc(Bm, (uint32_t)N * (uint32_t)R * 2u);
+  auto dma_b = [&](uint16_t* b, int n0) {
+    const int c = wave * 64 + lane, row = (c >> 1) & 63, rk = (c & 1) * 8;
+    const uint32_t vo = rk < R ? ((uint32_t)row * (uint32_t)R + (uint32_t)rk) * 2u : 0x80000000u;
+    if (wave < 2) dma16(rB, b + wave * 512, vo, (uint32_t)n0 * (uint32_t)R * 2u);
+  };
   auto load_b = [&](int n0) {
 #pragma unroll
     for (int q = 0; q < BQ; ++q) {
@@ -335,17 +343,24 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const int n0 = nbase + min(st, nsteps - 1) * kStep;
     dma_d(dn, n0);
     if constexpr (!INT4) dma_w(wn, n0);
-    if constexpr (PANEL)
+    if constexpr (PANEL && BDMA) {
+      if (pan) dma_b(bn, n0);
+    } else if constexpr (PANEL) {
       if (pan) load_b(n0);
+    }
     (void)bn;
   };
   // the same copies in 16 parts for phase(): the B rows first (a register load, waited for
   // at the next barrier, so it gets the longest time), then dY rows 8q.. (q < 8), W rows (bf16)
   // or the int4 register loads
-  auto prefetch_part = [&](int q, int st, uint16_t* dn, uint16_t* wn) {
+  auto prefetch_part = [&](int q, int st, uint16_t* dn, uint16_t* wn, uint16_t* bn) {
     const int n0 = nbase + min(st, nsteps - 1) * kStep;
-    if constexpr (PANEL)
+    if constexpr (PANEL && BDMA) {
+      if (pan && q == 0) dma_b(bn, n0);
+    } else if constexpr (PANEL) {
       if (pan && q == 0) load_b(n0);
+    }
+    (void)bn;
     if (q < 8) {
       dma16(rD, dn + (4 * q + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)q * 32u * rowD);
     } else if constexpr (!INT4) {
@@ -357,14 +372,14 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
   const NoCopy nocopy;
   auto finish = [&](uint16_t* wn, uint16_t* bn) {  // register-staged parts of a prefetch (bf16)
     (void)wn;
-    if constexpr (PANEL) {
+    if constexpr (PANEL && !BDMA) {
       if (pan) store_b(bn);
     } else {
       (void)bn;
     }
   };
   auto finish_b = [&](uint16_t* bn) {
-    if constexpr (PANEL) {
+    if constexpr (PANEL && !BDMA) {
       if (pan) store_b(bn);
     } else {
       (void)bn;
@@ -400,7 +415,7 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     }
     wait_all();
     phase(f1, f0, dn, wn, bn, 0, [&](int q) {
-      prefetch_part(q, st + 2, dc, wc);
+      prefetch_part(q, st + 2, dc, wc, bc);
       if constexpr (INT4)
         if (q == 15) load_w4(w4n, st + 3);  // after every copy
     });
