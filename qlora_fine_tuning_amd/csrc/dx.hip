@@ -154,9 +154,15 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const int r = wave * 8 + (lane >> 3);
     return (uint32_t)r * rowD + (uint32_t)((lane & 7) ^ swzf(r)) * 16u;
   }();
+  // Offset of instruction i's rows: in the lane offset (one VGPR per i, kept across the loop) at
+  // bf16 rank 16, so a copy needs no scalar add before it; the others (short of VGPRs) add it to
+  // the scalar offset.
+  constexpr bool VROW = RP == 16 && !INT4;
+  auto voffd_i = [&](int i) { return VROW ? voffD + (uint32_t)i * 32u * rowD : voffD; };
+  auto soffd_i = [&](int n0, int i) { return (uint32_t)n0 * 2u + (VROW ? 0u : (uint32_t)i * 32u * rowD); };
   auto dma_d = [&](uint16_t* dst, int n0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(rD, dst + (4 * i + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)i * 32u * rowD);
+    for (int i = 0; i < 8; ++i) dma16(rD, dst + (4 * i + wave) * 512, voffd_i(i), soffd_i(n0, i));
   };
   // W (bf16): instruction i of wave w fills block i >> 1, rows ((i & 1) * 4 + w) * 8 .. +7
   rsrc_t rW;
@@ -166,11 +172,16 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const int r = wave * 8 + (lane >> 3);  // row within the 64-row tile, less (i & 1) * 32
     return (uint32_t)r * rowW + (uint32_t)((lane & 7) ^ wsw(r)) * 16u;
   }();
+  auto voffw_i = [&](int i) {
+    return voffW + (VROW ? (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u : 0u);
+  };
+  auto soffw_i = [&](int n0, int i) {
+    return (uint32_t)n0 * rowW + (VROW ? 0u : (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
+  };
   auto dma_w = [&](uint16_t* dst, int n0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      dma16(rW, dst + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffW,
-            (uint32_t)n0 * rowW + (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
+      dma16(rW, dst + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffw_i(i), soffw_i(n0, i));
   };
   // W (int4): each thread unpacks one row's 64 codes of one 64-column block (one scale group).
   // A step's codes and raw fp16 scale stay in registers from their load to their unpacking
@@ -362,11 +373,10 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     }
     (void)bn;
     if (q < 8) {
-      dma16(rD, dn + (4 * q + wave) * 512, voffD, (uint32_t)n0 * 2u + (uint32_t)q * 32u * rowD);
+      dma16(rD, dn + (4 * q + wave) * 512, voffd_i(q), soffd_i(n0, q));
     } else if constexpr (!INT4) {
       const int i = q - 8;
-      dma16(rW, wn + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffW,
-            (uint32_t)n0 * rowW + (uint32_t)(i & 1) * 32u * rowW + (uint32_t)(i >> 1) * 128u);
+      dma16(rW, wn + (i >> 1) * 4096 + ((i & 1) * 4 + wave) * 512, voffw_i(i), soffw_i(n0, i));
     }
   };
   const NoCopy nocopy;
