@@ -297,17 +297,25 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // every row of the next phase uses all eight dY fragments: they go out in rows 0-3
+      // every row of the next phase uses all eight dY fragments: they go out in rows 0-3.  In
+      // those rows the bf16 instances read the row's W fragment (two transposing reads) after
+      // the first MFMA, so no gap between MFMAs holds more than three other instructions (a
+      // fourth costs the matrix core four cycles); the 4-bit ones spill with that order.
       if (i < 4) {
         nx.d[2 * i] = ld16(d + lds_offf(wm * 128 + 2 * i * 16 + l16, ch));
         nx.d[2 * i + 1] = ld16(d + lds_offf(wm * 128 + (2 * i + 1) * 16 + l16, ch));
       }
-      nx.w[i] = wfrag(w, kk, i);
+      if (INT4 || i >= 4) nx.w[i] = wfrag(w, kk, i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if constexpr (ASM) mfma16_acc(acc[i * 8 + j], cu.w[i], cu.d[j]);
         else acc[i * 8 + j] = mfma16(cu.w[i], cu.d[j], acc[i * 8 + j]);
+        if (!INT4 && i < 4 && j == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          nx.w[i] = wfrag(w, kk, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (!std::is_same_v<std::decay_t<decltype(copy)>, NoCopy>) {
           if (j == 1 || j == 5) {
             __builtin_amdgcn_sched_barrier(0);
