@@ -151,10 +151,16 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     const int r = wave * 8 + (lane >> 3);
     return (uint32_t)r * rowb + (uint32_t)((lane & 7) ^ swzf(r)) * 16u;
   }();
+  // Offset of instruction i's rows: in the lane offset (one VGPR per i, kept across the loop) at
+  // bf16 rank 16, so a copy needs no scalar add before it; the others (short of VGPRs) add it to
+  // the scalar offset.
+  constexpr bool VROW = RP == 16 && !INT4;
+  auto voff_i = [&](int i) { return VROW ? tile_voff + (uint32_t)i * 32u * rowb : tile_voff; };
+  auto soff_i = [&](int k0, int i) { return (uint32_t)k0 * 2u + (VROW ? 0u : (uint32_t)i * 32u * rowb); };
   auto dma_tile = [&](const rsrc_t& rs, uint16_t* dst, int k0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      dma16(rs, dst + (4 * i + wave) * 512, tile_voff, (uint32_t)k0 * 2u + (uint32_t)i * 32u * rowb);
+      dma16(rs, dst + (4 * i + wave) * 512, voff_i(i), soff_i(k0, i));
   };
   // instruction i of the W tile (rows (4i + w) * 8 ..): SwiGLU takes i < 4 from the gate rows
   // and i >= 4 from the up rows
@@ -163,7 +169,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
       dma16(i < 4 ? rW : rWu, dst + (4 * i + wave) * 512, tile_voff,
             (uint32_t)k0 * 2u + (uint32_t)(i & 3) * 32u * rowb);
     else
-      dma16(rW, dst + (4 * i + wave) * 512, tile_voff, (uint32_t)k0 * 2u + (uint32_t)i * 32u * rowb);
+      dma16(rW, dst + (4 * i + wave) * 512, voff_i(i), soff_i(k0, i));
   };
   auto dma_a = [&](uint16_t* dst, int k0) {
 #pragma unroll
@@ -277,18 +283,26 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     const int ch = kk * 4 + g4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // every row of the next phase uses all eight X fragments: they go out in rows 0-3
+      // every row of the next phase uses all eight X fragments: they go out in rows 0-3.  In
+      // those rows the bf16 instances read the row's W fragment after the first MFMA, so no gap
+      // between MFMAs holds more than three other instructions (a fourth costs the matrix core
+      // four cycles).
       if (i < 4) {
         nx.x[2 * i] = ld16(x + lds_offf(wm * 128 + 2 * i * 16 + l16, ch));
         nx.x[2 * i + 1] = ld16(x + lds_offf(wm * 128 + (2 * i + 1) * 16 + l16, ch));
       }
-      nx.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
+      if (INT4 || i >= 4) nx.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
       __builtin_amdgcn_sched_barrier(0);
       using Hook = std::decay_t<decltype(copy)>;
       [[maybe_unused]] typename std::conditional_t<IsEveryMfma<Hook>::value, Hook, EveryMfma<int, NoCopy>>::State hs{};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         mfma16_acc(acc[i * 8 + j], cu.w[i], cu.x[j]);
+        if (!INT4 && i < 4 && j == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          nx.w[i] = ld16(w + lds_offf(wn * 128 + i * 16 + l16, ch));
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (IsEveryMfma<Hook>::value) {
           __builtin_amdgcn_sched_barrier(0);
           copy.f(i * 8 + j, hs);
@@ -352,7 +366,7 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     if constexpr (PANEL)
       if (pan && d == 0) dma_a(an, k1);
     if (d < 8) {
-      dma16(rX, xn + (4 * d + wave) * 512, tile_voff, (uint32_t)k1 * 2u + (uint32_t)d * 32u * rowb);
+      dma16(rX, xn + (4 * d + wave) * 512, voff_i(d), soff_i(k1, d));
     } else if constexpr (!INT4) {
       dma_w_part(wnx, k1, d - 8);
     }
