@@ -155,9 +155,9 @@ dx_mfma_kernel(const uint16_t* __restrict__ dY, const void* __restrict__ Wp,
     return (uint32_t)r * rowD + (uint32_t)((lane & 7) ^ swzf(r)) * 16u;
   }();
   // Offset of instruction i's rows: in the lane offset (one VGPR per i, kept across the loop) at
-  // rank 16, so a copy needs no scalar add before it; the others (short of VGPRs) add it to the
-  // scalar offset.
-  constexpr bool VROW = RP == 16;
+  // rank 16 and bf16 rank 32, so a copy needs no scalar add before it; the others (short of
+  // VGPRs) add it to the scalar offset.
+  constexpr bool VROW = RP == 16 || (RP == 32 && !INT4);
   auto voffd_i = [&](int i) { return VROW ? voffD + (uint32_t)i * 32u * rowD : voffD; };
   auto soffd_i = [&](int n0, int i) { return (uint32_t)n0 * 2u + (VROW ? 0u : (uint32_t)i * 32u * rowD); };
   auto dma_d = [&](uint16_t* dst, int n0) {
