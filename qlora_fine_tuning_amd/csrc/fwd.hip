@@ -152,9 +152,9 @@ fwd_mfma_kernel(const uint16_t* __restrict__ X, const void* __restrict__ Wp,
     return (uint32_t)r * rowb + (uint32_t)((lane & 7) ^ swzf(r)) * 16u;
   }();
   // Offset of instruction i's rows: in the lane offset (one VGPR per i, kept across the loop) at
-  // bf16 rank 16, so a copy needs no scalar add before it; the others (short of VGPRs) add it to
-  // the scalar offset.
-  constexpr bool VROW = RP == 16 && !INT4;
+  // bf16 ranks 16 and 32, so a copy needs no scalar add before it; the others (short of VGPRs, or
+  // measured slower: the 4-bit rank-16 forward) add it to the scalar offset.
+  constexpr bool VROW = RP <= 32 && !INT4;
   auto voff_i = [&](int i) { return VROW ? tile_voff + (uint32_t)i * 32u * rowb : tile_voff; };
   auto soff_i = [&](int k0, int i) { return (uint32_t)k0 * 2u + (VROW ? 0u : (uint32_t)i * 32u * rowb); };
   auto dma_tile = [&](const rsrc_t& rs, uint16_t* dst, int k0) {
